@@ -1,0 +1,96 @@
+"""Glue: run the oracle on a generated case (test infrastructure).
+
+A case is any object with the attributes of sga_inputs.SgaCase (torch
+tensors in storage form, possibly on a GPU). Only the slices a query needs
+are copied to the host and decoded, so sampled queries of multi-GB caches
+stay cheap. No SGA arithmetic lives here; it all happens in `sga`.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+from . import formats, sga
+
+
+def raw(t) -> np.ndarray:
+    """A torch tensor in storage form -> NumPy array of its raw storage."""
+    import torch
+
+    t = t.detach().to("cpu")
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _dec(t, dtype: str, scales=None) -> np.ndarray:
+    return formats.decode(raw(t), dtype, None if scales is None else raw(scales))
+
+
+def run_queries(case, queries: Optional[Iterable[int]] = None, *, keep_scores: bool = True,
+                topk: Optional[int] = None) -> Dict[str, object]:
+    """Oracle SGA forward on the listed queries of `case` (all by default)."""
+    T = case.num_q
+    qs = list(range(T)) if queries is None else [int(t) for t in queries]
+    k = case.topk if topk is None else int(topk)
+    q_seq = raw(case.q_seq).astype(np.int64)
+    q_pos = raw(case.q_pos).astype(np.int64)
+    kv_start = raw(case.kv_start).astype(np.int64)
+    kv_len = raw(case.kv_len).astype(np.int64)
+    idx_dt = "fp8" if case.idx_dtype == "fp8" else "f32"
+    H, Dc = case.heads, case.d_latent
+    out_idx = np.full((len(qs), k), -1, dtype=np.int64)
+    out_y = np.zeros((len(qs), H, Dc))
+    out_lse = np.full((len(qs), H), -np.inf)
+    scores, exact = [], []
+    for i, t in enumerate(qs):
+        b = int(q_seq[t])
+        start = int(kv_start[b])
+        n = sga.visible_count(q_pos[t], kv_len[b])
+        q_idx_t = _dec(case.q_idx[t], idx_dt)
+        w_t = raw(case.w[t]).astype(np.float64)
+        keys = _dec(case.k_idx[start:start + n], idx_dt)
+        s64 = sga.index_scores(q_idx_t, w_t, keys)
+        exact.append(sga.fp32_exact_bound(q_idx_t, w_t, keys))
+        s32 = sga.to_fp32(s64)
+        if keep_scores:
+            scores.append(s32)
+        sel = sga.select_topk(s32, k)
+        out_idx[i] = sel
+        chosen = sel[sel >= 0]
+        import torch
+
+        rows_idx = torch.as_tensor(start + chosen, dtype=torch.int64, device=case.kv.device)
+        kv_rows = case.kv.index_select(0, rows_idx)
+        if case.kv_dtype == "mxfp8":
+            rows = _dec(kv_rows, "mxfp8", case.kv_scale.index_select(0, rows_idx))
+        else:
+            rows = _dec(kv_rows, case.kv_dtype)
+        q_t = _dec(case.q[t], case.q_dtype)
+        o, lse, _ = sga.attend(q_t, rows, case.softmax_scale, Dc)
+        g = None if case.gate is None else _dec(case.gate[t], case.gate_dtype)
+        out_y[i] = sga.output_gate(o, g)
+        out_lse[i] = lse
+    return {"scores": scores, "scores_exact": exact, "topk_idx": out_idx, "y": out_y,
+            "lse": out_lse, "queries": np.array(qs, dtype=np.int64)}
+
+
+def decode_all(case) -> Dict[str, np.ndarray]:
+    """Every input of a (small) case decoded to float64, plus int64 metadata."""
+    idx_dt = "fp8" if case.idx_dtype == "fp8" else "f32"
+    kv = (_dec(case.kv, "mxfp8", case.kv_scale) if case.kv_dtype == "mxfp8"
+          else _dec(case.kv, case.kv_dtype))
+    return {
+        "q": _dec(case.q, case.q_dtype),
+        "kv": kv,
+        "q_idx": _dec(case.q_idx, idx_dt),
+        "k_idx": _dec(case.k_idx, idx_dt),
+        "w": raw(case.w).astype(np.float64),
+        "gate": None if case.gate is None else _dec(case.gate, case.gate_dtype),
+        "q_seq": raw(case.q_seq).astype(np.int64),
+        "q_pos": raw(case.q_pos).astype(np.int64),
+        "kv_start": raw(case.kv_start).astype(np.int64),
+        "kv_len": raw(case.kv_len).astype(np.int64),
+    }
