@@ -1,0 +1,246 @@
+"""SGA decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: decode at 128K context, 16 sequences x 131,072 cached tokens,
+one query each, k = 2048, 64 heads (sga_inputs "decode_b16_n128k"). A step is
+one sga_layer_fwd call over the whole batch: indexer scores -> top-k -> sparse
+MLA -> gate. Inputs are generated on the GPU before timing and stay resident;
+the latent and index caches are rotated over 3 copies so that a step never
+finds the previous step's caches in the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, published
+METRIC = "SGA decode queries/s at 128K ctx, k=2048; % of HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_scores_fp8_traffic.json")
+INDEX_SRC = os.path.join(ROOT, "sparse_top_latent_amd", "csrc", "index_scores.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(case):
+    """Per-query bytes the method must move (index-key scan, selected latent
+    rows, per-query inputs and output), summed over the batch; and the index
+    kernel's share (index keys + index query + weights)."""
+    H, Dc, D, HI, DI = case.heads, case.d_latent, case.d_qk, case.idx_heads, case.idx_dim
+    row = D * 2 if case.kv_dtype == "bf16" else D + D // 32
+    qbytes = H * D * 2 + HI * DI + HI * 4 + H * Dc * 2 + H * Dc * (2 if case.out_dtype == "bf16" else 4)
+    lens = case.kv_len.cpu().tolist()
+    seqs = case.q_seq.cpu().tolist()
+    pos = case.q_pos.cpu().tolist()
+    total = index = 0
+    for b, p in zip(seqs, pos):
+        n = max(0, min(p + 1, lens[b]))
+        total += n * DI + min(n, case.topk) * row + qbytes
+        index += n * DI + HI * DI + HI * 4
+    return total, index
+
+
+def traffic_record():
+    """Measured HBM bytes of the index kernel, if taken on the current source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    sha = hashlib.sha256(open(INDEX_SRC, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+def host_subcase(case, queries):
+    """The listed queries of a device case, with only their sequences, on the host."""
+    import torch
+    from sga_inputs.gen import SgaCase
+
+    seqs = sorted({int(case.q_seq[t]) for t in queries})
+    starts = case.kv_start.cpu().tolist()
+    lens = case.kv_len.cpu().tolist()
+    remap = {b: i for i, b in enumerate(seqs)}
+    rows = torch.cat([torch.arange(starts[b], starts[b] + lens[b]) for b in seqs]).to(case.kv.device)
+    new_lens = [lens[b] for b in seqs]
+    new_starts = [0]
+    for n in new_lens[:-1]:
+        new_starts.append(new_starts[-1] + n)
+    qi = torch.as_tensor(queries, device=case.q.device)
+
+    def pick(x, idx):
+        return None if x is None else x.index_select(0, idx).cpu()
+
+    return SgaCase(
+        name=case.name + "-sample", heads=case.heads, d_latent=case.d_latent, d_rope=case.d_rope,
+        idx_heads=case.idx_heads, idx_dim=case.idx_dim, topk=case.topk,
+        softmax_scale=case.softmax_scale, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+        idx_dtype=case.idx_dtype, gate_dtype=case.gate_dtype, out_dtype=case.out_dtype,
+        lens=new_lens,
+        q_seq=torch.tensor([remap[int(case.q_seq[t])] for t in queries], dtype=torch.int32),
+        q_pos=case.q_pos.index_select(0, qi).cpu(),
+        kv_start=torch.tensor(new_starts, dtype=torch.int64),
+        kv_len=torch.tensor(new_lens, dtype=torch.int32),
+        q=pick(case.q, qi), kv=pick(case.kv, rows), kv_scale=pick(case.kv_scale, rows),
+        q_idx=pick(case.q_idx, qi), k_idx=pick(case.k_idx, rows), w=pick(case.w, qi),
+        gate=pick(case.gate, qi))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(case, budget_s=15.0):
+    """The oracle, as it stands, on host-resident queries of the same workload.
+
+    Queries are taken in a fixed order until about `budget_s` seconds of oracle
+    time are spent; copying each query's sequence to the host is not timed."""
+    from oracle import case as ocase
+
+    T = case.num_q
+    order = list(range(0, T, 2)) + list(range(1, T, 2))
+    done, t_used = 0, 0.0
+    for t in order:
+        if t_used >= budget_s:
+            break
+        sub = host_subcase(case, [t])
+        t0 = time.perf_counter()
+        ocase.run_queries(sub, keep_scores=False)
+        t_used += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": round(done / t_used, 3),
+        "unit": "queries/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{done} of the {T} queries of {case.name} through the whole path "
+                   f"(exact scores, full-sort top-k, two-pass softmax MLA, gate) in float64, "
+                   f"host-resident inputs, {t_used:.1f} s of oracle time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_b16_n128k")
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+            "(the SGA decode path shards whole sequences per GPU with no exchange; "
+            "see the design notes)")
+        sys.exit(2)
+
+    import torch
+
+    import sparse_top_latent_amd as sga
+    from sga_inputs import make_case
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    case = make_case(args.workload, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {args.workload} on the GPU in {time.time() - t0:.1f} s "
+        f"({case.num_kv_rows} cached rows, {case.num_q} queries)")
+    prob = sga.Problem.from_case(case)
+    T, H, Dc = case.num_q, case.heads, case.d_latent
+    out = torch.empty((T, H, Dc), dtype=sga.out_torch_dtype(prob.c.out_dtype), device=dev)
+    ws = sga.workspace(prob, sga.SGA_OP_LAYER, device=dev)
+    # independent cache copies, rotated per step (defeats the 256 MB MALL)
+    kvs = [case.kv] + [case.kv.clone() for _ in range(args.copies - 1)]
+    kis = [case.k_idx] + [case.k_idx.clone() for _ in range(args.copies - 1)]
+    scs = [case.kv_scale] + ([case.kv_scale.clone() for _ in range(args.copies - 1)]
+                             if case.kv_scale is not None else [None] * (args.copies - 1))
+
+    def step(i):
+        c = i % args.copies
+        sga.sga_layer_fwd(prob, case.q_idx, case.w, kis[c], case.q, kvs[c], scs[c], case.gate,
+                          out, None, None, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sga.sga_profile_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phase_ms, calls = sga.sga_profile_collect(4)
+    sga.sga_profile_enable(0)
+    ms_step = elapsed * 1e3 / args.steps
+    qps = T * args.steps / elapsed
+    total_bytes, index_bytes = algorithmic_bytes(case)
+    idx_ms = phase_ms[0] / max(calls, 1)
+    achieved = index_bytes / (idx_ms * 1e-3) / 1e9
+    step_gbs = total_bytes / (ms_step * 1e-3) / 1e9
+    phases = {n: round(v / max(calls, 1) * 1e3, 2) for n, v in
+              zip(("index_us", "topk_us", "mla_us", "combine_us"), phase_ms)}
+    log(f"[bench] {ms_step * 1e3:.1f} us/step, {qps:,.0f} queries/s, step {step_gbs:,.0f} GB/s "
+        f"({step_gbs / HBM_PEAK_GBS:.1%} of HBM), phases {phases}")
+    rec = traffic_record()
+    roofline = {
+        "bound": "hbm", "kernel": "k_index_fp8 (indexer score pass)",
+        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "bytes_per_launch": index_bytes,
+        "traffic": None if rec is None else rec["hbm_bytes_per_launch"],
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "seqs": case.num_seqs, "queries": T,
+                   "ctx": case.max_kv_len, "topk": case.topk, "heads": H, "d_latent": Dc,
+                   "d_rope": case.d_rope, "idx_heads": case.idx_heads, "idx_dim": case.idx_dim,
+                   "kv": case.kv_dtype, "index": case.idx_dtype, "out": case.out_dtype,
+                   "cache_copies": args.copies},
+        "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": total_bytes},
+        "phases_us": phases,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

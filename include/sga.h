@@ -1,0 +1,205 @@
+/*
+ * sga.h -- C ABI of the Sparse Gated Attention (SGA) forward hot path on AMD
+ * MI355X (gfx950).
+ *
+ * SGA is the attention sublayer described on the A.X K2 pages:
+ *   - "A.X-K2: a sparse-attention upgrade that costs nothing, trained natively
+ *     in FP8", section "Sparse Gated Attention": a lightweight indexer scores
+ *     every cached key, the top 2,048 tokens per query are kept at token
+ *     granularity, MLA runs over exactly the selected rows KV[I_topk], and a
+ *     learned head-specific gate scales the attention output before Wo;
+ *   - "SK Telecom Opens A.X K2: 688B Parameters and One Telling Benchmark",
+ *     section "Sparse Gated Attention" and its block-diagram caption (indexer
+ *     and top-k selector feed MLA; a sigmoid output gate);
+ *   - "A.X K2 Technical Report", section 2 (MLA backbone with a head-specific
+ *     output gate) and section 3.4 (Stage 3C: the indexer selects the top 2,048
+ *     tokens per query).
+ * The pages print no formula. The operations below implement these readings:
+ *   scores  I[t,s] = sum_h w[t,h] * max(0, qI[t,h,:] . kI[s,:])   for s <= p_t
+ *   select  S_t    = the k positions of largest I[t,.], ties to the lowest
+ *                    position; every position when p_t + 1 <= k
+ *   attend  o[t,h] = sum_{s in S_t} softmax_s(tau * q[t,h,:] . kv[s,:]) * kv[s,:Dc]
+ *   gate    y[t,h,c] = sigmoid(g[t,h,c]) * o[t,h,c]
+ * (absorbed MLA: every head reads the same cached row kv[s] = [c_s | kR_s] of
+ * Dc + Dr values; the value is its first Dc = d_latent entries).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *     16-byte aligned. Pointers in sga_problem are device pointers too.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns without synchronising. Device faults, if
+ *     any, surface at the caller's next synchronisation.
+ *   - The caller owns all memory, including the workspace `ws` (size from
+ *     sga_workspace_size). The library allocates no device memory and keeps
+ *     no pointer after a call returns. Calls that share a workspace must not
+ *     overlap in time.
+ *   - Argument errors are returned synchronously as an sga_status before any
+ *     work is enqueued; sga_last_error() gives this thread's detail message.
+ *     No C++ exception crosses this boundary.
+ *   - Sequence metadata lives on the device and is not checked on the host.
+ *     Kernels stay inside every buffer whatever it holds: a query's candidate
+ *     count is n_t = clamp(q_pos[t] + 1, 0, min(kv_len[b], max_kv_len,
+ *     num_kv_rows - kv_start[b])), and a query with an out-of-range q_seq has
+ *     n_t = 0. A query with n_t = 0 selects nothing and outputs y = 0 and
+ *     lse = -inf.
+ *
+ * Supported shapes (anything else returns SGA_ERR_UNSUPPORTED)
+ *   - fp32 path: q, kv, index q/k all SGA_F32; 1 <= heads <= 64,
+ *     d_latent + d_rope <= 1024 (d_latent a multiple of 4), idx_heads * idx_dim
+ *     <= 8192, topk <= 4096.
+ *   - MI355X path: heads = 64, d_latent = 512, d_rope = 64 with q SGA_BF16 and
+ *     kv SGA_BF16 or SGA_MXFP8_E4M3FN; index heads 64 x dim 128 in
+ *     SGA_FP8_E4M3FN; 1 <= topk <= 2048.
+ *   Gate and output may be SGA_F32 or SGA_BF16 on either path.
+ */
+#ifndef SGA_H
+#define SGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGA_ABI_VERSION 1
+
+typedef enum sga_status {
+  SGA_OK = 0,
+  SGA_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, bad size, bad dtype code          */
+  SGA_ERR_UNSUPPORTED = 2,      /* valid, but no kernel for this shape/dtype mix   */
+  SGA_ERR_WORKSPACE = 3,        /* ws NULL or smaller than sga_workspace_size()    */
+  SGA_ERR_DEVICE = 4,           /* HIP runtime error before launching              */
+  SGA_ERR_LAUNCH = 5            /* a kernel launch failed                          */
+} sga_status;
+
+typedef enum sga_dtype {
+  SGA_F32 = 0,          /* IEEE binary32                                              */
+  SGA_BF16 = 1,         /* bfloat16                                                   */
+  SGA_FP8_E4M3FN = 2,   /* OCP FP8 E4M3FN bytes (bias 7, max 448, no inf)             */
+  SGA_MXFP8_E4M3FN = 3  /* E4M3FN bytes + one E8M0 scale byte per 32 consecutive values */
+} sga_dtype;
+
+typedef enum sga_op {
+  SGA_OP_INDEX = 0, /* sga_index_scores   */
+  SGA_OP_TOPK = 1,  /* sga_topk_select    */
+  SGA_OP_MLA = 2,   /* sga_sparse_mla_fwd */
+  SGA_OP_LAYER = 3  /* sga_layer_fwd      */
+} sga_op;
+
+/* Shapes, dtypes and sequence metadata of one call. */
+typedef struct sga_problem {
+  int32_t num_seqs;      /* B: sequences in the caches                                   */
+  int32_t num_q;         /* T: query rows                                                */
+  int32_t max_kv_len;    /* host bound on every kv_len[b]; row stride of the score buffer */
+  int32_t reserved0;     /* must be 0                                                    */
+  int64_t num_kv_rows;   /* rows in kv, kv_scale and k_idx                               */
+  int32_t heads;         /* H: attention heads (64)                                      */
+  int32_t d_latent;      /* Dc: latent width = value width (512)                          */
+  int32_t d_rope;        /* Dr: rotary key width (64)                                     */
+  int32_t idx_heads;     /* HI: indexer heads (64)                                        */
+  int32_t idx_dim;       /* DI: indexer head width (128)                                  */
+  int32_t topk;          /* k: positions kept per query (2048)                            */
+  float softmax_scale;   /* tau, applied to q . kv                                         */
+  int32_t q_dtype;       /* sga_dtype of q                                                 */
+  int32_t kv_dtype;      /* sga_dtype of kv                                                */
+  int32_t idx_dtype;     /* sga_dtype of q_idx and k_idx                                   */
+  int32_t gate_dtype;    /* sga_dtype of gate logits (ignored when gate is NULL)           */
+  int32_t out_dtype;     /* sga_dtype of out                                               */
+  const int32_t *q_seq;  /* [T] sequence of each query row                                 */
+  const int32_t *q_pos;  /* [T] position of each query row within its sequence             */
+  const int64_t *kv_start; /* [B] cache row holding position 0 of each sequence           */
+  const int32_t *kv_len;   /* [B] cached tokens of each sequence                           */
+} sga_problem;
+
+/* ABI version of the loaded library (SGA_ABI_VERSION). */
+int sga_abi_version(void);
+
+/* Static text for a status code. */
+const char *sga_status_string(int status);
+
+/* Detail message of this thread's last non-OK return ("" if none). */
+const char *sga_last_error(void);
+
+/* Workspace bytes `op` needs for problem `p`, written to *bytes (0 when none is
+ * needed). Pure host computation; validates `p` like the op itself. */
+sga_status sga_workspace_size(const sga_problem *p, int op, size_t *bytes);
+
+/*
+ * Indexer score pass (the pages' "lightweight indexer scores every cached
+ * key"; see the header comment for sources).
+ *   q_idx  [T, HI, DI]   idx_dtype (SGA_F32 or SGA_FP8_E4M3FN)
+ *   w      [T, HI]       fp32 per-(query, head) weights
+ *   k_idx  [num_kv_rows, DI] idx_dtype, one key per cached token, shared by all
+ *                        index heads; sequence b owns rows kv_start[b] + s
+ *   scores [T, max_kv_len] fp32 output: scores[t, s] for s < n_t; entries with
+ *                        s >= n_t are left untouched.
+ * Arithmetic: fp32 accumulation (FP8 MFMA on the MI355X path). With integer
+ * q/k and a dyadic w that keeps every partial sum below 2^24 units of its
+ * finest bit, the result is the exact score in any evaluation order.
+ * A -0.0 result is stored as +0.0. Needs no workspace.
+ */
+sga_status sga_index_scores(const sga_problem *p, const void *q_idx, const float *w,
+                            const void *k_idx, float *scores, void *stream);
+
+/*
+ * Per-query top-k selection (the pages' selector: "keeps only the top 2,048
+ * tokens per query, selected at individual-token granularity").
+ *   scores   [T, max_kv_len] fp32, only s < n_t is read
+ *   topk_idx [T, topk] int32 output: the selected positions within the
+ *            sequence in ascending order; -1 fills the tail when n_t < topk.
+ * Order: larger score first, ties to the lower position; -0.0 equals +0.0;
+ * NaN orders above +inf. Exact (radix select on the fp32 bit pattern), so the
+ * result is deterministic.
+ */
+sga_status sga_topk_select(const sga_problem *p, const float *scores, int32_t *topk_idx,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Sparse MLA over the selected latent rows plus the sigmoid output gate (the
+ * pages' "MLA then runs exactly over the selected set"; "head-specific output
+ * gate ... before the Wo projection").
+ *   q        [T, H, Dc + Dr]  q_dtype (absorbed query: latent part then rope part)
+ *   kv       [num_kv_rows, Dc + Dr] kv_dtype, row = [c_s | kR_s]
+ *   kv_scale [num_kv_rows, (Dc + Dr) / 32] E8M0 bytes for SGA_MXFP8_E4M3FN, else NULL
+ *   topk_idx [T, topk] int32 positions within the query's sequence; entries
+ *            < 0 or >= n_t-clipped cache length are skipped (any order)
+ *   gate     [T, H, Dc] gate_dtype logits, or NULL for no gate
+ *   out      [T, H, Dc] out_dtype: sigmoid(gate) * softmax-weighted latent sum
+ *   lse      [T, H] fp32 log-sum-exp of the scaled logits, or NULL
+ * Arithmetic on the MI355X path: bf16 MFMA for q.kv and p.v with fp32
+ * accumulation, fp32 online softmax, p rounded to bf16 for p.v; MXFP8 rows
+ * are expanded exactly to bf16.
+ */
+sga_status sga_sparse_mla_fwd(const sga_problem *p, const void *q, const void *kv,
+                              const uint8_t *kv_scale, const int32_t *topk_idx,
+                              const void *gate, void *out, float *lse, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/*
+ * The whole path in one call: index scores -> top-k -> sparse MLA -> gate.
+ * Arguments as in the three calls above. topk_idx_out [T, topk] and lse [T, H]
+ * are optional outputs (NULL to skip). The scores live in the workspace.
+ */
+sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w,
+                         const void *k_idx, const void *q, const void *kv,
+                         const uint8_t *kv_scale, const void *gate, void *out,
+                         int32_t *topk_idx_out, float *lse, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/*
+ * Phase timing of sga_layer_fwd, for measurement. While enabled, each
+ * sga_layer_fwd call on this thread records HIP events on its stream around
+ * each phase (0 index scores, 1 top-k, 2 sparse MLA, 3 combine + gate), for up
+ * to `max_calls` calls. sga_profile_collect waits for those events, writes the
+ * summed milliseconds per phase into ms[0..nphase) and the number of timed
+ * calls into *calls, then resets the record. Disable with max_calls = 0.
+ */
+sga_status sga_profile_enable(int max_calls);
+sga_status sga_profile_collect(double *ms, int nphase, int *calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGA_H */

@@ -1,0 +1,166 @@
+// Device helpers shared by the SGA kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sga.h"
+
+namespace sga {
+
+// ---------------------------------------------------------------------------
+// vector types used as MFMA operands
+// ---------------------------------------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// radix-select digits of the order-preserving score key
+//   level 0: key bits 31..20 (4096 bins), level 1: 19..10, level 2: 9..0
+// ---------------------------------------------------------------------------
+constexpr int kHist0Bins = 4096;
+constexpr int kHist0Shift = 20;
+constexpr int kHist12Bins = 1024;
+constexpr int kTopkChunk = 4096;  // scores per top-k scan workgroup
+
+// fp32 score -> uint32 key whose unsigned order is the numeric order of the
+// scores; -0.0 maps to the key of +0.0 and NaN above +inf.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// sequence metadata
+// ---------------------------------------------------------------------------
+struct SeqMeta {
+  const int32_t *q_seq;
+  const int32_t *q_pos;
+  const int64_t *kv_start;
+  const int32_t *kv_len;
+  int32_t num_seqs;
+  int32_t max_kv_len;
+  int64_t num_kv_rows;
+};
+
+// Cached length of sequence b clipped to the buffers (0 for a bad b).
+__device__ __forceinline__ int32_t seq_len_clipped(const SeqMeta &m, int32_t b, int64_t *start) {
+  if (b < 0 || b >= m.num_seqs) {
+    *start = 0;
+    return 0;
+  }
+  int64_t s = m.kv_start[b];
+  int64_t len = m.kv_len[b];
+  if (s < 0 || s > m.num_kv_rows) {
+    *start = 0;
+    return 0;
+  }
+  if (len > m.num_kv_rows - s) len = m.num_kv_rows - s;
+  if (len > m.max_kv_len) len = m.max_kv_len;
+  if (len < 0) len = 0;
+  *start = s;
+  return (int32_t)len;
+}
+
+// Candidate count n_t of query t (positions 0..q_pos that are cached).
+__device__ __forceinline__ int32_t query_candidates(const SeqMeta &m, int32_t t, int64_t *start) {
+  int32_t L = seq_len_clipped(m, m.q_seq[t], start);
+  int64_t n = (int64_t)m.q_pos[t] + 1;
+  if (n > L) n = L;
+  if (n < 0) n = 0;
+  return (int32_t)n;
+}
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                // round to nearest even
+  return u >> 16;
+}
+
+// OCP E4M3FN byte -> fp32 (exact).
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t code) {
+  uint32_t e = (code >> 3) & 0xFu;
+  uint32_t m = code & 0x7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  if ((code & 0x7fu) == 0x7fu) v = __builtin_nanf("");
+  return (code & 0x80u) ? -v : v;
+}
+
+// E8M0 scale byte -> fp32 2^(e-127) (NaN for 0xFF).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  if (e == 255u) return __builtin_nanf("");
+  if (e == 0u) return 0x1p-127f;
+  return __uint_as_float(e << 23);
+}
+
+__device__ __forceinline__ float load_as_f32(const void *p, int dtype, size_t i) {
+  if (dtype == SGA_BF16) return bf16_bits_to_f32(((const uint16_t *)p)[i]);
+  return ((const float *)p)[i];
+}
+
+__device__ __forceinline__ void store_from_f32(void *p, int dtype, size_t i, float v) {
+  if (dtype == SGA_BF16)
+    ((uint16_t *)p)[i] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    ((float *)p)[i] = v;
+}
+
+__device__ __forceinline__ float sigmoidf_exact_ends(float g) {
+  // 1 / (1 + e^-g): +inf -> 1 exactly, -inf -> 0 exactly
+  return 1.0f / (1.0f + __expf(-g));
+}
+
+// ---------------------------------------------------------------------------
+// block-wide exclusive scan of one uint32 per thread (blockDim a multiple of 64)
+// `scratch` needs blockDim/64 + 1 words of LDS.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
+                                                         uint32_t *total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  uint32_t inc = wave_inclusive_scan(v);
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int i = 0; i < nw; ++i) {
+      uint32_t x = scratch[i];
+      scratch[i] = acc;
+      acc += x;
+    }
+    scratch[nw] = acc;
+  }
+  __syncthreads();
+  uint32_t res = scratch[wave] + inc - v;
+  *total = scratch[nw];
+  __syncthreads();
+  return res;
+}
+
+}  // namespace sga

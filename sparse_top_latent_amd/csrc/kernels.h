@@ -1,0 +1,61 @@
+// Host-side launchers of the SGA kernels (one translation unit per kernel family).
+#pragma once
+
+#include "common.h"
+
+namespace sga {
+
+// --- workspace utility -----------------------------------------------------
+hipError_t launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
+
+// --- indexer score pass ----------------------------------------------------
+// scores[t * stride + s] for s < n_t; hist0 (T x 4096, zeroed) optional.
+hipError_t launch_index_f32(const SeqMeta &m, int T, int HI, int DI, const float *q_idx,
+                            const float *w, const float *k_idx, float *scores, int64_t stride,
+                            uint32_t *hist0, hipStream_t s);
+hipError_t launch_index_fp8(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
+                            const uint8_t *k_idx, float *scores, int64_t stride, uint32_t *hist0,
+                            hipStream_t s);
+
+// --- top-k select -----------------------------------------------------------
+struct TopkWs {
+  uint32_t *hist0;    // [T, 4096]
+  uint32_t *counts;   // [T, nchunk]
+  uint2 *entries;     // [T, nchunk * kTopkChunk] (position, key)
+  int32_t nchunk;     // ceil(max_kv_len / kTopkChunk)
+};
+size_t topk_ws_bytes(int T, int max_kv_len);
+TopkWs topk_ws_carve(void *ws, int T, int max_kv_len);
+hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
+                             uint32_t *hist0, hipStream_t s);
+hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
+                            const TopkWs &w, int32_t *topk_idx, hipStream_t s);
+hipError_t launch_topk_final(const SeqMeta &m, int T, int k, const TopkWs &w, int32_t *topk_idx,
+                             hipStream_t s);
+
+// --- sparse MLA + gate ---------------------------------------------------------
+struct MlaArgs {
+  SeqMeta meta;
+  int T, H, Dc, Dr, k;
+  float tau;
+  const void *q;
+  int q_dtype;
+  const void *kv;
+  int kv_dtype;
+  const uint8_t *kv_scale;
+  const int32_t *topk_idx;
+  const void *gate;
+  int gate_dtype;
+  void *out;
+  int out_dtype;
+  float *lse;
+};
+// generic fp32 path (one workgroup per (query, head))
+hipError_t launch_mla_f32(const MlaArgs &a, hipStream_t s);
+// MI355X path: H=64, Dc=512, Dr=64, bf16 or MXFP8 rows
+constexpr int kMlaRowsPerSplit = 128;
+size_t mla_split_ws_bytes(int T, int k);
+hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s);
+hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s);
+
+}  // namespace sga

@@ -1,0 +1,305 @@
+// Per-query top-k select: the k positions of largest score, ties to the lowest
+// position, returned in ascending position order (-1 padding when n_t < k).
+//
+// Source: "A.X-K2: a sparse-attention upgrade that costs nothing, trained
+// natively in FP8", section "Sparse Gated Attention" (keep the top 2,048 tokens
+// per query, at individual-token granularity rather than in blocks); "A.X K2
+// Technical Report", section 3.4 (the indexer selects the top 2,048 tokens).
+//
+// Exact radix select on the order-preserving 32-bit key of each fp32 score,
+// most significant digit first (12 + 10 + 10 bits):
+//  1. level-0 histogram of key bits 31..20 (built by the indexer in the fused
+//     layer, or by k_topk_hist0);
+//  2. k_topk_scan, many workgroups per query: every workgroup finds the level-0
+//     threshold bin b0 from the histogram, then compacts, in position order,
+//     the (position, key) pairs of its chunk whose digit is >= b0 (everything
+//     above b0 is certainly selected; bin b0 holds the threshold);
+//  3. k_topk_final, one workgroup per query: refines the threshold inside bin b0
+//     with two more 1024-bin histograms over the compacted pairs, giving the
+//     exact k-th key K* and how many ties at K* to take; a final ordered pass
+//     emits key > K* plus the first `take` ties, which are the lowest
+//     positions because chunks and their pairs are visited in position order.
+// No atomics decide the output, so it is deterministic.
+
+#include "kernels.h"
+
+namespace sga {
+
+namespace {
+
+constexpr int kScanBlock = 256;
+constexpr int kPerThread = kTopkChunk / kScanBlock;  // 16 consecutive scores per thread
+constexpr int kFinalBlock = 512;
+constexpr int kFinalCap = 14336;                     // pairs staged in LDS (112 KiB)
+constexpr int kMaxChunks = 1024;                     // max_kv_len <= 4M
+
+__global__ void k_zero_u32(uint32_t *p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__restrict__ scores,
+                                                    int64_t stride, uint32_t *hist0) {
+  __shared__ uint32_t hist[kHist0Bins];
+  const int t = blockIdx.y;
+  int64_t start;
+  const int n = query_candidates(m, t, &start);
+  const int c0 = blockIdx.x * kTopkChunk;
+  if (c0 >= n) return;
+  for (int i = threadIdx.x; i < kHist0Bins; i += 256) hist[i] = 0u;
+  __syncthreads();
+  const float *row = scores + t * stride;
+  for (int j = 0; j < kPerThread; ++j) {
+    int s = c0 + j * 256 + threadIdx.x;
+    if (s < n) atomicAdd(&hist[score_key(row[s]) >> kHist0Shift], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHist0Bins; i += 256) {
+    uint32_t c = hist[i];
+    if (c) atomicAdd(hist0 + (size_t)t * kHist0Bins + i, c);
+  }
+}
+
+// Finds the bin b holding the `want`-th largest element of a histogram: the
+// count of elements in bins above b (returned in *above) is < want and adding
+// bin b reaches want. Each of blockDim threads owns nbins/blockDim consecutive bins.
+template <int NB>
+__device__ __forceinline__ int find_threshold_bin(const uint32_t *hist, uint32_t want,
+                                                  uint32_t *above, uint32_t *scratch,
+                                                  int *res) {
+  const int per = NB / (int)blockDim.x;
+  const int tid = threadIdx.x;
+  // thread tid owns bins [(nthreads-1-tid)*per, ...) so that an exclusive scan in
+  // thread order is a suffix scan over bins (largest bins first)
+  const int hi_bin = NB - 1 - tid * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += hist[hi_bin - i];
+  uint32_t total;
+  uint32_t excl = block_exclusive_scan(local, scratch, &total);
+  if (tid == 0) {
+    res[0] = -1;
+    res[1] = 0;
+  }
+  __syncthreads();
+  if (excl < want && excl + local >= want) {
+    uint32_t acc = excl;
+    for (int i = 0; i < per; ++i) {
+      uint32_t c = hist[hi_bin - i];
+      if (acc + c >= want) {
+        res[0] = hi_bin - i;
+        res[1] = (int)acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  int b = res[0];
+  *above = (uint32_t)res[1];
+  __syncthreads();
+  return b;
+}
+
+__global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
+                                                          const float *__restrict__ scores,
+                                                          int64_t stride, TopkWs ws,
+                                                          int32_t *__restrict__ topk_idx) {
+  __shared__ uint32_t hist[kHist0Bins];
+  __shared__ uint32_t scratch[kScanBlock / 64 + 1];
+  __shared__ int res[2];
+  const int t = blockIdx.y;
+  int64_t start;
+  const int n = query_candidates(m, t, &start);
+  if (n <= k) {
+    // every candidate is kept: positions 0..n-1, then -1
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < k; i += kScanBlock)
+        topk_idx[(size_t)t * k + i] = i < n ? i : -1;
+    return;
+  }
+  const int c0 = blockIdx.x * kTopkChunk;
+  if (c0 >= n) return;
+  const uint32_t *h = ws.hist0 + (size_t)t * kHist0Bins;
+  for (int i = threadIdx.x; i < kHist0Bins; i += kScanBlock) hist[i] = h[i];
+  __syncthreads();
+  uint32_t above;
+  const int b0 = find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &above, scratch, res);
+
+  // 16 consecutive scores per thread, kept in position order
+  const float *row = scores + t * stride;
+  const int p0 = c0 + threadIdx.x * kPerThread;
+  uint32_t keys[kPerThread];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    int s = p0 + j;
+    uint32_t key = s < n ? score_key(row[s]) : 0u;
+    keys[j] = key;
+    cnt += (s < n && (int)(key >> kHist0Shift) >= b0) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t off = block_exclusive_scan(cnt, scratch, &total);
+  uint2 *dst = ws.entries + ((size_t)t * ws.nchunk + blockIdx.x) * kTopkChunk;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    int s = p0 + j;
+    if (s < n && (int)(keys[j] >> kHist0Shift) >= b0) dst[off++] = make_uint2((uint32_t)s, keys[j]);
+  }
+  if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunk + blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, TopkWs ws,
+                                                            int32_t *__restrict__ topk_idx) {
+  extern __shared__ uint2 pairs[];  // kFinalCap entries
+  __shared__ uint32_t hist[kHist0Bins];
+  __shared__ uint32_t offs[kMaxChunks + 1];
+  __shared__ uint32_t scratch[kFinalBlock / 64 + 1];
+  __shared__ int res[2];
+  const int t = blockIdx.x;
+  int64_t start;
+  const int n = query_candidates(m, t, &start);
+  if (n <= k) return;
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  const uint32_t *h0 = ws.hist0 + (size_t)t * kHist0Bins;
+  for (int i = threadIdx.x; i < kHist0Bins; i += kFinalBlock) hist[i] = h0[i];
+  __syncthreads();
+  uint32_t above0;
+  const int b0 = find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &above0, scratch, res);
+  uint32_t want = (uint32_t)k - above0;
+
+  // chunk offsets in position order
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int c = 0; c < nch; ++c) {
+      offs[c] = acc;
+      acc += ws.counts[(size_t)t * ws.nchunk + c];
+    }
+    offs[nch] = acc;
+  }
+  __syncthreads();
+  const uint32_t total = offs[nch];
+  const uint2 *src = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
+  const bool staged = total <= (uint32_t)kFinalCap;
+  if (staged) {
+    for (int c = 0; c < nch; ++c) {
+      uint32_t cnt = offs[c + 1] - offs[c];
+      for (uint32_t i = threadIdx.x; i < cnt; i += kFinalBlock)
+        pairs[offs[c] + i] = src[(size_t)c * kTopkChunk + i];
+    }
+  }
+  __syncthreads();
+  // pair number i (in position order) -> its (position, key)
+  auto pair_at = [&](uint32_t i, int &c_hint) -> uint2 {
+    if (staged) return pairs[i];
+    while (offs[c_hint + 1] <= i) ++c_hint;
+    return src[(size_t)c_hint * kTopkChunk + (i - offs[c_hint])];
+  };
+
+  // level 1 and 2: refine inside bin b0
+  uint32_t prefix = (uint32_t)b0;  // known high bits of K*
+  int shift = kHist0Shift;
+#pragma unroll 1
+  for (int level = 1; level <= 2; ++level) {
+    for (int i = threadIdx.x; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
+    __syncthreads();
+    const int nshift = shift - 10;
+    int ch = 0;
+    for (uint32_t i = threadIdx.x; i < total; i += kFinalBlock) {
+      uint2 pk = pair_at(i, ch);
+      if ((pk.y >> shift) == prefix) atomicAdd(&hist[(pk.y >> nshift) & 1023u], 1u);
+    }
+    __syncthreads();
+    uint32_t above;
+    int b = find_threshold_bin<kHist12Bins>(hist, want, &above, scratch, res);
+    want -= above;
+    prefix = (prefix << 10) | (uint32_t)b;
+    shift = nshift;
+  }
+  const uint32_t kstar = prefix;  // the exact k-th largest key
+  const uint32_t take = want;     // ties at kstar to keep (lowest positions)
+
+  // ordered emission
+  uint32_t out_base = 0, tie_base = 0;
+  int ch = 0;
+  for (uint32_t i0 = 0; i0 < total; i0 += kFinalBlock) {
+    uint32_t i = i0 + threadIdx.x;
+    uint2 pk = make_uint2(0u, 0u);
+    bool valid = i < total;
+    if (valid) pk = pair_at(i, ch);
+    uint32_t is_tie = (valid && pk.y == kstar) ? 1u : 0u;
+    uint32_t tie_tot;
+    uint32_t tie_rank = tie_base + block_exclusive_scan(is_tie, scratch, &tie_tot);
+    uint32_t sel = (valid && (pk.y > kstar || (is_tie && tie_rank < take))) ? 1u : 0u;
+    uint32_t sel_tot;
+    uint32_t pos = out_base + block_exclusive_scan(sel, scratch, &sel_tot);
+    if (sel && pos < (uint32_t)k) topk_idx[(size_t)t * k + pos] = (int32_t)pk.x;
+    out_base += sel_tot;
+    tie_base += tie_tot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero_u32(uint32_t *p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t topk_ws_bytes(int T, int max_kv_len) {
+  size_t nch = ((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk;
+  return align256((size_t)T * kHist0Bins * 4) + align256((size_t)T * nch * 4) +
+         align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
+}
+
+TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
+  TopkWs w;
+  w.nchunk = (int32_t)(((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk);
+  char *p = (char *)ws;
+  w.hist0 = (uint32_t *)p;
+  p += align256((size_t)T * kHist0Bins * 4);
+  w.counts = (uint32_t *)p;
+  p += align256((size_t)T * w.nchunk * 4);
+  w.entries = (uint2 *)p;
+  return w;
+}
+
+hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
+                             uint32_t *hist0, hipStream_t s) {
+  if (T == 0 || m.max_kv_len == 0) return hipSuccess;
+  dim3 grid((m.max_kv_len + kTopkChunk - 1) / kTopkChunk, T);
+  hipLaunchKernelGGL(k_topk_hist0, grid, dim3(256), 0, s, m, scores, stride, hist0);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
+                            const TopkWs &w, int32_t *topk_idx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int nch = m.max_kv_len > 0 ? (m.max_kv_len + kTopkChunk - 1) / kTopkChunk : 1;
+  dim3 grid(nch, T);
+  hipLaunchKernelGGL(k_topk_scan, grid, dim3(kScanBlock), 0, s, m, k, scores, stride, w,
+                     topk_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_final(const SeqMeta &m, int T, int k, const TopkWs &w, int32_t *topk_idx,
+                             hipStream_t s) {
+  if (T == 0 || m.max_kv_len <= k) return hipSuccess;
+  static bool attr_set = false;
+  const size_t dyn = (size_t)kFinalCap * sizeof(uint2);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)k_topk_final,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_topk_final, dim3(T), dim3(kFinalBlock), dyn, s, m, k, w, topk_idx);
+  return hipGetLastError();
+}
+
+}  // namespace sga

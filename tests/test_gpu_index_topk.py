@@ -1,0 +1,113 @@
+"""GPU parity of the indexer score pass and the top-k select (bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_top_latent_amd as sga
+from gpu_util import run_scores, say
+from oracle import case as ocase
+from oracle import sga as osga
+from sga_inputs import make_case, make_custom
+from sga_inputs.gen import FULL_DIMS
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_scores(case, queries=None):
+    got = run_scores(case).cpu().numpy()
+    ref = ocase.run_queries(case, queries)
+    assert all(ref["scores_exact"])
+    for i, t in enumerate(ref["queries"]):
+        r = ref["scores"][i]
+        g = got[t, : r.size]
+        assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), \
+            f"query {t}: {np.count_nonzero(g != r)} scores differ"
+
+
+def test_index_scores_tiny_fp32_all_queries():
+    say("case tiny_fp32_L512 index scores")
+    _check_scores(make_case("tiny_fp32_L512", device="cuda"))
+
+
+def test_index_scores_fp8_ragged():
+    # several 2048-key workgroups, ragged tails, one-key and empty sequences
+    lens = [5000, 2049, 2048, 63, 1, 0, 4100]
+    qs = [(0, 4999), (0, 1234), (1, 2048), (2, 2047), (3, 62), (4, 0), (5, 0), (6, 4099), (6, 64)]
+    case = make_custom(lens, qs, dims=FULL_DIMS, precision="bf16", seed=11, device="cuda")
+    say("case fp8 ragged index scores")
+    _check_scores(case)
+
+
+def test_index_scores_fp8_full_decode_b32_n32k():
+    case = make_case("decode_b32_n32k", device="cuda")
+    say("case decode_b32_n32k index scores, 4 sampled queries")
+    _check_scores(case, [0, 7, 20, 31])
+
+
+# --------------------------------------------------------------------------
+# top-k select on adversarial score rows
+# --------------------------------------------------------------------------
+def _topk_case(rows, k):
+    """Problem whose query t owns sequence t with n_t = len(rows[t])."""
+    T = len(rows)
+    lens = [len(r) for r in rows]
+    L = max(max(lens), 1)
+    scores = torch.full((T, L), float("nan"))
+    for t, r in enumerate(rows):
+        scores[t, : len(r)] = torch.as_tensor(r, dtype=torch.float32)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    prob = sga.Problem(
+        q_seq=torch.arange(T, dtype=torch.int32, device="cuda"),
+        q_pos=torch.as_tensor([max(n - 1, 0) if n else -1 for n in lens], dtype=torch.int32,
+                              device="cuda"),
+        kv_start=torch.as_tensor(starts, device="cuda"),
+        kv_len=torch.as_tensor(lens, dtype=torch.int32, device="cuda"),
+        max_kv_len=L, num_kv_rows=int(sum(lens)), heads=64, d_latent=512, d_rope=64,
+        idx_heads=64, idx_dim=128, topk=k, softmax_scale=1.0)
+    return prob, scores.cuda()
+
+
+def _check_topk(rows, k, label):
+    prob, scores = _topk_case(rows, k)
+    out = torch.full((len(rows), k), -7, dtype=torch.int32, device="cuda")
+    ws = sga.workspace(prob, sga.SGA_OP_TOPK)
+    say(f"case topk {label}: T={len(rows)} k={k} max_n={scores.shape[1]}")
+    sga.sga_topk_select(prob, scores, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t, r in enumerate(rows):
+        ref = osga.select_topk(np.asarray(r, dtype=np.float32), k)
+        assert np.array_equal(got[t], ref), f"{label}: query {t} (n={len(r)}) differs"
+
+
+def test_topk_ties_and_short_rows():
+    g = torch.Generator().manual_seed(0)
+    rows = []
+    for n in (0, 1, 5, 2047, 2048, 2049, 4096, 4097, 9000, 30000):
+        rows.append((torch.randint(-3, 4, (n,), generator=g).float() * 0.5).tolist())
+    _check_topk(rows, 2048, "integer ties")
+
+
+def test_topk_all_equal_signed_zero_and_negative():
+    n = 20000
+    zeros = [0.0] * n
+    signed = [(-0.0 if i % 3 else 0.0) for i in range(n)]
+    neg = (-torch.arange(n, dtype=torch.float32) / 7).tolist()
+    _check_topk([zeros, signed, neg], 2048, "equal / signed zero / negative")
+
+
+def test_topk_one_dense_bin_beyond_lds_staging():
+    # 100k distinct scores that share their top 12 key bits: the refinement walks
+    # more pairs than fit in LDS
+    g = torch.Generator().manual_seed(1)
+    n = 100_000
+    vals = (1.0 + torch.rand(n, generator=g) * 0.12).tolist()
+    _check_topk([vals, vals[: n // 2]], 2048, "dense level-0 bin")
+
+
+def test_topk_small_k_and_continuous_scores():
+    g = torch.Generator().manual_seed(2)
+    rows = [torch.randn(n, generator=g).tolist() for n in (3, 100, 5000, 70000)]
+    for k in (1, 7, 64):
+        _check_topk(rows, k, f"k={k}")
