@@ -120,21 +120,27 @@ def cpu_baseline(case, budget_s=15.0):
 
     T = case.num_q
     order = list(range(0, T, 2)) + list(range(1, T, 2))
-    done, t_used = 0, 0.0
-    for t in order:
-        if t_used >= budget_s:
-            break
-        sub = host_subcase(case, [t])
-        t0 = time.perf_counter()
-        ocase.run_queries(sub, keep_scores=False)
-        t_used += time.perf_counter() - t0
-        done += 1
+    done, t_used, passes = 0, 0.0, 0
+    subs = {}
+    while t_used < budget_s and passes < 50:
+        for t in order:
+            if t_used >= budget_s:
+                break
+            if t not in subs:
+                subs[t] = host_subcase(case, [t])
+            t0 = time.perf_counter()
+            ocase.run_queries(subs[t], keep_scores=False)
+            t_used += time.perf_counter() - t0
+            done += 1
+        passes += 1
+        if len(subs) * 200e6 > 8e9:  # keep at most ~8 GB of host copies around
+            subs.clear()
     return {
         "value": round(done / t_used, 3),
         "unit": "queries/s",
         "cores": blas_threads(),
         "kind": "oracle",
-        "sample": (f"{done} of the {T} queries of {case.name} through the whole path "
+        "sample": (f"{done} query evaluations over the {T} queries of {case.name} through the whole path "
                    f"(exact scores, full-sort top-k, two-pass softmax MLA, gate) in float64, "
                    f"host-resident inputs, {t_used:.1f} s of oracle time"),
     }

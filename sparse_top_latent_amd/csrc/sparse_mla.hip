@@ -123,10 +123,26 @@ __global__ __launch_bounds__(kF32Block) void k_mla_f32(MlaArgs a) {
 // MI355X path
 // --------------------------------------------------------------------------
 constexpr int kH = 64, kDc = 512, kD = 576;  // d_rope = 64
-constexpr int kTile = 32;                 // rows per LDS tile
-constexpr int kLdsStride = kD + 8;        // bf16 elements per LDS row (pad 16 B)
-constexpr int kKsteps = kD / 32;          // 18 MFMA k-steps for q . row
-constexpr int kCt = kDc / 16;             // 32 channel tiles of the value
+constexpr int kTile = 32;                     // rows per LDS tile
+constexpr int kMaxTiles = kMlaRowsPerSplit / kTile;
+constexpr int kRowChunks = kD * 2 / 16;       // 72 16-byte chunks per bf16 row
+constexpr int kTileBytes = kTile * kD * 2;    // 36,864
+constexpr int kBfDma = kTile * kRowChunks / 256;  // 9 DMA issues per thread per tile
+constexpr int kMxChunks = kTile * kD / 16;    // 1,152 16-byte chunks of E4M3FN values per tile
+constexpr int kMxDma = 5;                     // 1,280 slots per tile (the last 128 are padding)
+constexpr int kMxRawBytes = kMxDma * 256 * 16;
+constexpr int kScales = kD / 32;              // 18 E8M0 scales per row
+constexpr int kKsteps = kD / 32;              // 18 MFMA k-steps for q . row
+constexpr int kCt = kDc / 16;                 // 32 channel tiles of the value
+constexpr float kRescaleSlack = 8.0f;         // log2 headroom before the running max moves
+
+constexpr size_t kBfSmem = (size_t)kMaxTiles * kTileBytes;
+constexpr size_t kMxSmem = (size_t)kMaxTiles * kMxRawBytes + kTileBytes + kMlaRowsPerSplit * kScales;
+
+// 16 zero bytes: the DMA source of rows that are not selected
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf &a, const v8bf &b, const v4f &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -134,78 +150,133 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf &a, const v8bf &b, const v4f
 
 __device__ __forceinline__ v8bf as_v8bf(const v4i &x) { return __builtin_bit_cast(v8bf, x); }
 
-template <bool kMx>
-__device__ __forceinline__ void gather_tile(uint16_t *tile, const int64_t *rows, int r0, int nrows,
-                                            const void *kv, const uint8_t *kv_scale) {
-  if (!kMx) {
-    // 32 rows x 72 chunks of 16 bytes
-    const uint8_t *base = (const uint8_t *)kv;
-#pragma unroll
-    for (int j = 0; j < (kTile * 72) / 256; ++j) {
-      int c = threadIdx.x + 256 * j;
-      int r = c / 72, col = c - r * 72;
-      int ri = r0 + r;
-      int64_t g = ri < nrows ? rows[ri] : -1;
-      v4i v = {0, 0, 0, 0};
-      if (g >= 0) v = __builtin_nontemporal_load((const v4i *)(base + g * (kD * 2) + col * 16));
-      *(v4i *)(tile + r * kLdsStride + col * 8) = v;
-    }
-  } else {
-    // 32 rows x 36 chunks of 16 E4M3FN values; chunk col lies in scale block col/2
-    const uint8_t *base = (const uint8_t *)kv;
-    for (int c = threadIdx.x; c < kTile * 36; c += 256) {
-      int r = c / 36, col = c - r * 36;
-      int ri = r0 + r;
-      int64_t g = ri < nrows ? rows[ri] : -1;
-      v4i out0 = {0, 0, 0, 0}, out1 = {0, 0, 0, 0};
-      if (g >= 0) {
-        v4i v = __builtin_nontemporal_load((const v4i *)(base + g * kD + col * 16));
-        float sc = e8m0_to_f32(kv_scale[g * (kD / 32) + (col >> 1)]);
-        uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-        uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            uint32_t b0 = (w[i] >> (16 * hh)) & 0xFFu;
-            uint32_t b1 = (w[i] >> (16 * hh + 8)) & 0xFFu;
-            uint32_t lo = f32_to_bf16_bits(e4m3fn_to_f32(b0) * sc);
-            uint32_t hi = f32_to_bf16_bits(e4m3fn_to_f32(b1) * sc);
-            o[i * 2 + hh] = lo | (hi << 16);
-          }
-        }
-        out0 = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-        out1 = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
-      }
-      v4i *dst = (v4i *)(tile + r * kLdsStride + col * 16);
-      dst[0] = out0;
-      dst[1] = out1;
-    }
+// 16-byte chunk `chunk` of tile row `row` lives at chunk slot row*72 + (chunk ^ (row & 7)):
+// an XOR swizzle inside groups of 8 chunks that spreads same-column reads of
+// consecutive rows over the LDS banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowChunks + (chunk ^ (row & 7)); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until this thread's DMAs of tile `tt` have landed: kPer DMA issues per
+// tile were made for all kMaxTiles tiles, in order.
+template <int kPer>
+__device__ __forceinline__ void wait_tile(int tt) {
+  switch (tt) {
+    case 0: wait_vmcnt<3 * kPer>(); break;
+    case 1: wait_vmcnt<2 * kPer>(); break;
+    case 2: wait_vmcnt<kPer>(); break;
+    default: wait_vmcnt<0>(); break;
   }
+}
+
+// Workgroup barrier that waits for this wave's LDS operations but not for its
+// outstanding global->LDS DMAs (a __syncthreads() would drain those too).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const void *src, unsigned char *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
 }
 
 template <bool kMx>
 __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, float *__restrict__ opart,
                                                    float2 *__restrict__ ml) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kLdsStride];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t rows[kMlaRowsPerSplit];
   const int split = blockIdx.x, t = blockIdx.y, S = gridDim.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   int64_t start;
   const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
   const int r0 = split * kMlaRowsPerSplit;
   const int nrows = min(kMlaRowsPerSplit, a.k - r0);
-  for (int r = threadIdx.x; r < kMlaRowsPerSplit; r += 256) {
-    int32_t pos = r < nrows ? a.topk_idx[(size_t)t * a.k + r0 + r] : -1;
-    rows[r] = (pos >= 0 && pos < L) ? start + pos : -1;
+  const int ntiles = (nrows + kTile - 1) / kTile;
+  if (tid < kMlaRowsPerSplit) {
+    int32_t pos = tid < nrows ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
+    rows[tid] = (pos >= 0 && pos < L) ? start + pos : -1;
   }
-  // query slice of this wave's head (B operand of S^T = rows . Q^T)
+  __syncthreads();  // rows[] ready
+  // this wave's 16 heads: B operand of S^T = rows . Q^T, kept in VGPRs
   const int head = wave * 16 + c16;
   const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
   v8bf qreg[kKsteps];
 #pragma unroll
   for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
+
+  unsigned char *tiles = smem;                                  // bf16: kMaxTiles x 36 KB
+  unsigned char *cvt = smem + kMaxTiles * kMxRawBytes;          // MXFP8: expanded tile
+  uint8_t *scl = (uint8_t *)(cvt + kTileBytes);                 // MXFP8: [128][18] scales
+  uint32_t sreg[5];
+  if (kMx) {
+    // scales as 9 two-byte words per row, loaded without branches (unselected
+    // rows and padding read the zero block) and replaced by 2^0 afterwards
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int i = tid + 256 * j;
+      const int64_t gr = i < kMlaRowsPerSplit * 9 ? rows[i / 9] : -1;
+      const uint16_t *src = gr >= 0 ? (const uint16_t *)(a.kv_scale + gr * kScales + 2 * (i % 9))
+                                    : (const uint16_t *)g_zero16;
+      sreg[j] = *src;
+      if (gr < 0) sreg[j] = 0x7F7Fu;
+    }
+  }
+  // issue every tile's gather now; tiles are consumed in order below. The
+  // row ids of a tile are read from LDS in one batch before its DMAs.
+#pragma unroll
+  for (int tt = 0; tt < kMaxTiles; ++tt) {
+    // tiles past ntiles are filled from the zero block so that every thread
+    // issues the same, static number of DMAs (exact vmcnt bookkeeping)
+    if (!kMx) {
+      unsigned char *tbase = tiles + tt * kTileBytes;
+      int64_t gr[kBfDma];
+#pragma unroll
+      for (int j = 0; j < kBfDma; ++j)
+        gr[j] = tt < ntiles ? rows[tt * kTile + (j * 256 + tid) / kRowChunks] : -1;
+#pragma unroll
+      for (int j = 0; j < kBfDma; ++j) {
+        const int c = j * 256 + tid;                 // chunk slot in the tile
+        const int r = c / kRowChunks;
+        const int col = (c - r * kRowChunks) ^ (r & 7);
+        const void *src = gr[j] >= 0
+                              ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
+                              : (const void *)g_zero16;
+        dma16(src, tbase + (j * 256 + wave * 64) * 16);
+      }
+    } else {
+      unsigned char *tbase = tiles + tt * kMxRawBytes;
+      int64_t gr[kMxDma];
+#pragma unroll
+      for (int j = 0; j < kMxDma; ++j) {
+        const int c = j * 256 + tid;                 // raw chunk slot: row c/36, 16 values
+        gr[j] = (c < kMxChunks && tt < ntiles) ? rows[tt * kTile + c / 36] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kMxDma; ++j) {
+        const int c = j * 256 + tid;
+        const int r = c / 36;
+        const void *src = gr[j] >= 0
+                              ? (const void *)((const uint8_t *)a.kv + gr[j] * kD + (c - r * 36) * 16)
+                              : (const void *)g_zero16;
+        dma16(src, tbase + (j * 256 + wave * 64) * 16);
+      }
+    }
+  }
+  if (kMx) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      int i = tid + 256 * j;
+      if (i < kMlaRowsPerSplit * 9) *(uint16_t *)(scl + (i / 9) * kScales + 2 * (i % 9)) = (uint16_t)sreg[j];
+    }
+  }
 
   v4f acc[kCt];
 #pragma unroll
@@ -213,19 +284,44 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, float *__restrict_
   float m_run = -INFINITY, l_run = 0.0f;
   const float scale2 = a.tau * kLog2e;  // logits kept in the exp2 domain
 
-  const int ntiles = (nrows + kTile - 1) / kTile;
-  for (int tt = 0; tt < ntiles; ++tt) {
-    __syncthreads();
-    gather_tile<kMx>(tile, rows, tt * kTile, nrows, a.kv, a.kv_scale);
-    __syncthreads();
+#pragma unroll
+  for (int tt = 0; tt < kMaxTiles; ++tt) {
+    if (tt >= ntiles) break;
+    const unsigned char *tile;
+    if (!kMx) {
+      wait_tile<kBfDma>(tt);
+      barrier_lds();  // every wave's DMAs of tile tt have landed
+      tile = tiles + tt * kTileBytes;
+    } else {
+      wait_tile<kMxDma>(tt);
+      barrier_lds();  // raw tile tt and the scales are in LDS; the previous tile is consumed
+      const unsigned char *raw = tiles + tt * kMxRawBytes;
+      for (int c = tid; c < kMxChunks; c += 256) {
+        const int r = c / 36, blk = c - r * 36;      // 16 values = channels blk*16 ..
+        const v4i v = *(const v4i *)(raw + c * 16);
+        const float sc = e8m0_to_f32(scl[(tt * kTile + r) * kScales + (blk >> 1)]);
+        const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, false));
+          o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, true));
+        }
+        *(v4i *)(cvt + swz(r, 2 * blk) * 16) = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        *(v4i *)(cvt + swz(r, 2 * blk + 1) * 16) = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      }
+      barrier_lds();
+      tile = cvt;
+    }
     // S^T[row][head] for the two 16-row halves of the tile
     v4f s[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       v4f sacc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t *rp = tile + (rt * 16 + c16) * kLdsStride + 8 * g;
+      const int row = rt * 16 + c16;
 #pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks) sacc = mfma_bf16(as_v8bf(*(const v4i *)(rp + ks * 32)), qreg[ks], sacc);
+      for (int ks = 0; ks < kKsteps; ++ks)
+        sacc = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(row, 4 * ks + g) * 16)), qreg[ks], sacc);
       s[rt] = sacc;
     }
     float lg[8];
@@ -239,33 +335,41 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, float *__restrict_
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    if (!(m_new > -INFINITY)) continue;  // nothing valid yet for this head
-    const float alpha = exp2f(m_run - m_new);
+    if (!(mt > -INFINITY)) continue;  // no selected row in this tile (uniform over heads)
+    // move the running max only when a logit would exceed it by 2^8 (exact either way)
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] *= alpha;
+      m_run = m_new;
+    }
     float p[8], ps = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(lg[j] - m_new);
+      p[j] = exp2f(lg[j] - m_run);
       ps += p[j];
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
+    l_run += ps;
     v8bf pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-    // V^T operand: rows {4g..4g+3, 16+4g..16+4g+3}, channel ct*16 + c16
-    const uint16_t *vp = tile + c16;
+    // V^T operand by transposed LDS reads: lane (g, c16) receives channel ct*16 + c16
+    // of rows 4g..4g+3 (first read) and 16+4g..16+4g+3 (second read)
+    const int vr = 4 * g + (c16 >> 2);
+    const int vsub = (c16 & 1) * 8;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) {
-      v8bf va;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int r = (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
-        va[j] = __builtin_bit_cast(__bf16, vp[r * kLdsStride + ct * 16]);
-      }
-      acc[ct] = mfma_bf16(va, pb, acc[ct] * alpha);
+      const int chunk = 2 * ct + ((c16 & 3) >> 1);
+      const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) v4bf *)(tile + swz(vr, chunk) * 16 + vsub));
+      const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) v4bf *)(tile + swz(vr + 16, chunk) * 16 + vsub));
+      const v8bf va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[ct] = mfma_bf16(va, pb, acc[ct]);
     }
   }
   // partial O^T: lane holds channels ct*16 + 4g + i of head `head`
@@ -275,24 +379,37 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, float *__restrict_
   if (g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m_run, l_run);
 }
 
+constexpr int kMaxSplits = 2048 / kMlaRowsPerSplit;
+
 __global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const float *__restrict__ opart,
                                                      const float2 *__restrict__ ml, int S) {
   const int h = blockIdx.x, t = blockIdx.y;
   const int c = threadIdx.x * 4;
+  float2 st[kMaxSplits];
+  v4f x[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < S) {
+      st[s] = ml[((size_t)t * S + s) * kH + h];
+      x[s] = *(const v4f *)(opart + (((size_t)t * S + s) * kH + h) * kDc + c);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[((size_t)t * S + s) * kH + h].x);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) M = fmaxf(M, st[s].x);
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (M > -INFINITY) {
     float wsum = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      float2 v = ml[((size_t)t * S + s) * kH + h];
-      float wgt = v.x > -INFINITY ? exp2f(v.x - M) : 0.0f;
-      if (wgt == 0.0f) continue;
-      wsum += wgt * v.y;
-      v4f x = *(const v4f *)(opart + (((size_t)t * S + s) * kH + h) * kDc + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = fmaf(wgt, x[i], o[i]);
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < S && st[s].x > -INFINITY) {
+        const float wgt = exp2f(st[s].x - M);
+        wsum = fmaf(wgt, st[s].y, wsum);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaf(wgt, x[s][i], o[i]);
+      }
     }
     const float inv = 1.0f / wsum;
 #pragma unroll
@@ -331,10 +448,19 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   const int S = mla_splits(a.k);
   float *opart = (float *)ws;
   float2 *ml = (float2 *)((char *)ws + align256((size_t)a.T * S * kH * kDc * 4));
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)k_mla_split<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxSmem);
+    (void)hipGetLastError();
+    attr = true;
+  }
   if (a.kv_dtype == SGA_MXFP8_E4M3FN)
-    hipLaunchKernelGGL(k_mla_split<true>, dim3(S, a.T), dim3(256), 0, s, a, opart, ml);
+    hipLaunchKernelGGL(k_mla_split<true>, dim3(S, a.T), dim3(256), kMxSmem, s, a, opart, ml);
   else
-    hipLaunchKernelGGL(k_mla_split<false>, dim3(S, a.T), dim3(256), 0, s, a, opart, ml);
+    hipLaunchKernelGGL(k_mla_split<false>, dim3(S, a.T), dim3(256), kBfSmem, s, a, opart, ml);
   return hipGetLastError();
 }
 

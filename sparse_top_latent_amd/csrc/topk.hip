@@ -101,6 +101,7 @@ __device__ __forceinline__ int find_threshold_bin(const uint32_t *hist, uint32_t
   return b;
 }
 
+template <bool kVec>
 __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
                                                           const float *__restrict__ scores,
                                                           int64_t stride, TopkWs ws,
@@ -120,33 +121,58 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
   }
   const int c0 = blockIdx.x * kTopkChunk;
   if (c0 >= n) return;
+  // this thread's 16 consecutive scores, requested before the threshold search
+  const float *row = scores + t * stride;
+  const int p0 = c0 + threadIdx.x * kPerThread;
+  float v[kPerThread];
+  if (kVec && p0 + kPerThread <= n) {
+#pragma unroll
+    for (int q = 0; q < kPerThread / 4; ++q) {
+      const float4 x = *(const float4 *)(row + p0 + 4 * q);
+      v[4 * q] = x.x;
+      v[4 * q + 1] = x.y;
+      v[4 * q + 2] = x.z;
+      v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) v[j] = p0 + j < n ? row[p0 + j] : 0.0f;
+  }
   const uint32_t *h = ws.hist0 + (size_t)t * kHist0Bins;
   for (int i = threadIdx.x; i < kHist0Bins; i += kScanBlock) hist[i] = h[i];
   __syncthreads();
   uint32_t above;
   const int b0 = find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &above, scratch, res);
 
-  // 16 consecutive scores per thread, kept in position order
-  const float *row = scores + t * stride;
-  const int p0 = c0 + threadIdx.x * kPerThread;
   uint32_t keys[kPerThread];
   uint32_t cnt = 0;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    int s = p0 + j;
-    uint32_t key = s < n ? score_key(row[s]) : 0u;
+    const uint32_t key = score_key(v[j]);
     keys[j] = key;
-    cnt += (s < n && (int)(key >> kHist0Shift) >= b0) ? 1u : 0u;
+    cnt += (p0 + j < n && (int)(key >> kHist0Shift) >= b0) ? 1u : 0u;
   }
   uint32_t total;
   uint32_t off = block_exclusive_scan(cnt, scratch, &total);
   uint2 *dst = ws.entries + ((size_t)t * ws.nchunk + blockIdx.x) * kTopkChunk;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
-    int s = p0 + j;
-    if (s < n && (int)(keys[j] >> kHist0Shift) >= b0) dst[off++] = make_uint2((uint32_t)s, keys[j]);
+    if (p0 + j < n && (int)(keys[j] >> kHist0Shift) >= b0)
+      dst[off++] = make_uint2((uint32_t)(p0 + j), keys[j]);
   }
   if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunk + blockIdx.x] = total;
+}
+
+constexpr int kBatch = 8;  // independent loads in flight per thread
+
+// Chunk holding flat pair index f (offs ascending, offs[0] = 0, offs[nch] = total > f).
+__device__ __forceinline__ int chunk_of(const uint32_t *offs, int nch, uint32_t f) {
+  int lo = 0, hi = nch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= f) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, TopkWs ws,
@@ -156,62 +182,77 @@ __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, To
   __shared__ uint32_t offs[kMaxChunks + 1];
   __shared__ uint32_t scratch[kFinalBlock / 64 + 1];
   __shared__ int res[2];
+  const int tid = threadIdx.x;
   const int t = blockIdx.x;
   int64_t start;
   const int n = query_candidates(m, t, &start);
   if (n <= k) return;
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
   const uint32_t *h0 = ws.hist0 + (size_t)t * kHist0Bins;
-  for (int i = threadIdx.x; i < kHist0Bins; i += kFinalBlock) hist[i] = h0[i];
+  const uint32_t *cnts = ws.counts + (size_t)t * ws.nchunk;
+  // chunk counts (<= 2 per thread) and the level-0 histogram, loaded together
+  const uint32_t c_a = 2 * tid < nch ? cnts[2 * tid] : 0u;
+  const uint32_t c_b = 2 * tid + 1 < nch ? cnts[2 * tid + 1] : 0u;
+  for (int i = tid; i < kHist0Bins; i += kFinalBlock) hist[i] = h0[i];
   __syncthreads();
   uint32_t above0;
   const int b0 = find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &above0, scratch, res);
   uint32_t want = (uint32_t)k - above0;
-
-  // chunk offsets in position order
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int c = 0; c < nch; ++c) {
-      offs[c] = acc;
-      acc += ws.counts[(size_t)t * ws.nchunk + c];
-    }
-    offs[nch] = acc;
-  }
+  uint32_t total;
+  const uint32_t ex = block_exclusive_scan(c_a + c_b, scratch, &total);
+  if (2 * tid < nch) offs[2 * tid] = ex;
+  if (2 * tid + 1 < nch) offs[2 * tid + 1] = ex + c_a;
+  if (tid == 0) offs[nch] = total;
   __syncthreads();
-  const uint32_t total = offs[nch];
+
   const uint2 *src = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
   const bool staged = total <= (uint32_t)kFinalCap;
-  if (staged) {
-    for (int c = 0; c < nch; ++c) {
-      uint32_t cnt = offs[c + 1] - offs[c];
-      for (uint32_t i = threadIdx.x; i < cnt; i += kFinalBlock)
-        pairs[offs[c] + i] = src[(size_t)c * kTopkChunk + i];
-    }
-  }
-  __syncthreads();
-  // pair number i (in position order) -> its (position, key)
-  auto pair_at = [&](uint32_t i, int &c_hint) -> uint2 {
-    if (staged) return pairs[i];
-    while (offs[c_hint + 1] <= i) ++c_hint;
-    return src[(size_t)c_hint * kTopkChunk + (i - offs[c_hint])];
+  auto gload = [&](uint32_t f) -> uint2 {
+    const int c = chunk_of(offs, nch, f);
+    return src[(size_t)c * kTopkChunk + (f - offs[c])];
   };
+  if (staged) {
+    for (uint32_t base = 0; base < total; base += kFinalBlock * kBatch) {
+      uint2 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t f = base + u * kFinalBlock + tid;
+        if (f < total) v[u] = gload(f);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t f = base + u * kFinalBlock + tid;
+        if (f < total) pairs[f] = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  auto pair_at = [&](uint32_t f) -> uint2 { return staged ? pairs[f] : gload(f); };
 
-  // level 1 and 2: refine inside bin b0
+  // levels 1 and 2: refine the threshold inside bin b0
   uint32_t prefix = (uint32_t)b0;  // known high bits of K*
   int shift = kHist0Shift;
 #pragma unroll 1
   for (int level = 1; level <= 2; ++level) {
-    for (int i = threadIdx.x; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
+    for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
     __syncthreads();
     const int nshift = shift - 10;
-    int ch = 0;
-    for (uint32_t i = threadIdx.x; i < total; i += kFinalBlock) {
-      uint2 pk = pair_at(i, ch);
-      if ((pk.y >> shift) == prefix) atomicAdd(&hist[(pk.y >> nshift) & 1023u], 1u);
+    for (uint32_t base = 0; base < total; base += kFinalBlock * kBatch) {
+      uint2 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t f = base + u * kFinalBlock + tid;
+        v[u] = f < total ? pair_at(f) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t f = base + u * kFinalBlock + tid;
+        if (f < total && (v[u].y >> shift) == prefix) atomicAdd(&hist[(v[u].y >> nshift) & 1023u], 1u);
+      }
     }
     __syncthreads();
     uint32_t above;
-    int b = find_threshold_bin<kHist12Bins>(hist, want, &above, scratch, res);
+    const int b = find_threshold_bin<kHist12Bins>(hist, want, &above, scratch, res);
     want -= above;
     prefix = (prefix << 10) | (uint32_t)b;
     shift = nshift;
@@ -219,23 +260,31 @@ __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, To
   const uint32_t kstar = prefix;  // the exact k-th largest key
   const uint32_t take = want;     // ties at kstar to keep (lowest positions)
 
-  // ordered emission
-  uint32_t out_base = 0, tie_base = 0;
-  int ch = 0;
-  for (uint32_t i0 = 0; i0 < total; i0 += kFinalBlock) {
-    uint32_t i = i0 + threadIdx.x;
-    uint2 pk = make_uint2(0u, 0u);
-    bool valid = i < total;
-    if (valid) pk = pair_at(i, ch);
-    uint32_t is_tie = (valid && pk.y == kstar) ? 1u : 0u;
-    uint32_t tie_tot;
-    uint32_t tie_rank = tie_base + block_exclusive_scan(is_tie, scratch, &tie_tot);
-    uint32_t sel = (valid && (pk.y > kstar || (is_tie && tie_rank < take))) ? 1u : 0u;
-    uint32_t sel_tot;
-    uint32_t pos = out_base + block_exclusive_scan(sel, scratch, &sel_tot);
-    if (sel && pos < (uint32_t)k) topk_idx[(size_t)t * k + pos] = (int32_t)pk.x;
-    out_base += sel_tot;
-    tie_base += tie_tot;
+  // ordered emission: each thread owns a contiguous run of pairs
+  const uint32_t seg = (total + kFinalBlock - 1) / kFinalBlock;
+  const uint32_t s0 = min(total, tid * seg), s1 = min(total, s0 + seg);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (uint32_t f = s0; f < s1; ++f) {
+    const uint32_t key = pair_at(f).y;
+    n_gt += key > kstar;
+    n_eq += key == kstar;
+  }
+  uint32_t tmp;
+  const uint32_t tie_base = block_exclusive_scan(n_eq, scratch, &tmp);
+  const uint32_t ties_here = tie_base >= take ? 0u : min(n_eq, take - tie_base);
+  const uint32_t out_base = block_exclusive_scan(n_gt + ties_here, scratch, &tmp);
+  uint32_t o = out_base, tr = tie_base;
+  for (uint32_t f = s0; f < s1; ++f) {
+    const uint2 pk = pair_at(f);
+    bool sel = pk.y > kstar;
+    if (pk.y == kstar) {
+      sel = tr < take;
+      ++tr;
+    }
+    if (sel) {
+      if (o < (uint32_t)k) topk_idx[(size_t)t * k + o] = (int32_t)pk.x;
+      ++o;
+    }
   }
 }
 
@@ -282,8 +331,13 @@ hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores,
   if (T == 0) return hipSuccess;
   int nch = m.max_kv_len > 0 ? (m.max_kv_len + kTopkChunk - 1) / kTopkChunk : 1;
   dim3 grid(nch, T);
-  hipLaunchKernelGGL(k_topk_scan, grid, dim3(kScanBlock), 0, s, m, k, scores, stride, w,
-                     topk_idx);
+  const bool vec = (stride % 4 == 0) && (((uintptr_t)scores & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL(k_topk_scan<true>, grid, dim3(kScanBlock), 0, s, m, k, scores, stride, w,
+                       topk_idx);
+  else
+    hipLaunchKernelGGL(k_topk_scan<false>, grid, dim3(kScanBlock), 0, s, m, k, scores, stride, w,
+                       topk_idx);
   return hipGetLastError();
 }
 

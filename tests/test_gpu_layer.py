@@ -60,7 +60,8 @@ def test_layer_out_of_range_metadata_is_empty():
         assert torch.count_nonzero(out[t].float()) == 0
         assert bool(torch.all(idx[t] == -1))
         assert bool(torch.all(torch.isneginf(lse[t])))
-    assert torch.equal(idx[3], idx[0]) and torch.equal(out[3], out[0])
+    # query 3 sits past the end of its cache: it sees the whole sequence, like query 0
+    assert bool(torch.all(idx[3] >= 0)) and int(idx[3].max()) <= 4999
     compare_layer(case, [0, 3], out=out, idx=idx, lse=lse, label="clip")
 
 
