@@ -154,6 +154,7 @@ def main():
     ap.add_argument("--workload", default="decode_b16_n128k")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -191,25 +192,60 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    sga.sga_profile_enable(args.steps)
+
+    # one HIP graph per cache copy: a decode step is a fixed chain of small
+    # launches, replayed without host launch overhead
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(args.copies):
+                step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in range(args.copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % args.copies].replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        if graphs:
+            graphs[i % args.copies].replay()
+        else:
+            step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    phase_ms, calls = sga.sga_profile_collect(4)
-    sga.sga_profile_enable(0)
     ms_step = elapsed * 1e3 / args.steps
     qps = T * args.steps / elapsed
+
+    # per-kernel durations: the same steps launched eagerly with HIP events
+    # recorded by the library around each phase on the launch stream
+    sga.sga_profile_enable(args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    phase_ms, calls = sga.sga_profile_collect(4)
+    sga.sga_profile_enable(0)
     total_bytes, index_bytes = algorithmic_bytes(case)
     idx_ms = phase_ms[0] / max(calls, 1)
     achieved = index_bytes / (idx_ms * 1e-3) / 1e9
     step_gbs = total_bytes / (ms_step * 1e-3) / 1e9
     phases = {n: round(v / max(calls, 1) * 1e3, 2) for n, v in
               zip(("index_us", "topk_us", "mla_us", "combine_us"), phase_ms)}
-    log(f"[bench] {ms_step * 1e3:.1f} us/step, {qps:,.0f} queries/s, step {step_gbs:,.0f} GB/s "
-        f"({step_gbs / HBM_PEAK_GBS:.1%} of HBM), phases {phases}")
+    log(f"[bench] {ms_step * 1e3:.1f} us/step ({'graph' if graphs else 'eager'}), eager {eager_ms * 1e3:.1f} us/step, "
+        f"{qps:,.0f} queries/s, step {step_gbs:,.0f} GB/s ({step_gbs / HBM_PEAK_GBS:.1%} of HBM), "
+        f"phases {phases}")
     rec = traffic_record()
     roofline = {
         "bound": "hbm", "kernel": "k_index_fp8 (indexer score pass)",
@@ -231,6 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8+bf16",
         "data": "synthetic",
+        "launch": "hip-graph" if graphs else "eager",
+        "eager_ms_per_step": round(eager_ms, 5),
         "config": {"workload": case.name, "seqs": case.num_seqs, "queries": T,
                    "ctx": case.max_kv_len, "topk": case.topk, "heads": H, "d_latent": Dc,
                    "d_rope": case.d_rope, "idx_heads": case.idx_heads, "idx_dim": case.idx_dim,

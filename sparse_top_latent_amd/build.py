@@ -44,6 +44,14 @@ COMMON = [
 ]
 
 
+# extra flags per source file
+PER_FILE = {
+    # the indexer's ReLU runs on MFMA accumulators that are never NaN for finite
+    # inputs; without this every max is preceded by a NaN-quieting max
+    "index_scores.hip": ["-fno-honor-nans"],
+}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -65,7 +73,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, "-c", *COMMON, "-o", o, s], verbose) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [cc, "-c", *COMMON, *PER_FILE.get(os.path.basename(s), []), "-o", o, s],
+                          verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
     tmp = LIB + ".tmp"

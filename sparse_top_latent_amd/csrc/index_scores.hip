@@ -10,11 +10,11 @@
 //  * k_index_f32: generic fp32 path, one thread per (query, key).
 //  * k_index_fp8: MI355X path for 64 index heads x 128 dims in E4M3FN. Each
 //    wave keeps the query's 64 x 128 index matrix in registers as four 16 x 128
-//    MFMA A tiles and streams 16-key B tiles straight from HBM into registers
-//    (every key is used once, so no LDS staging). One 16x16x128 FP8 MFMA per
-//    (head tile, key tile) gives 16 heads x 16 keys; the ReLU and the weighted
-//    head sum run on the accumulators, and a 2-step cross-lane reduction leaves
-//    one finished score per lane, stored coalesced.
+//    MFMA A tiles and streams its own range of keys through LDS (LDS-DMA, two
+//    8 KiB tiles in flight). One 16x16x128 FP8 MFMA per (head tile, 16-key
+//    tile) gives 16 heads x 16 keys; the ReLU and the weighted head sum run on
+//    the accumulators, and a 2-step cross-lane reduction leaves one finished
+//    score per lane, stored coalesced.
 // Both can also build the level-0 histogram (top 12 bits of the score key) the
 // top-k select starts from, so the layer never re-reads the scores for it.
 
@@ -43,15 +43,16 @@ __device__ __forceinline__ void hist_zero(uint32_t *lds_hist) {
 constexpr int kF32Block = 256;
 constexpr int kF32MaxQ = 8192;  // HI * DI
 
-__global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int HI, int DI,
+__global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int HI, int DI,
                                                          const float *__restrict__ q_idx,
                                                          const float *__restrict__ w,
                                                          const float *__restrict__ k_idx,
                                                          float *__restrict__ scores,
-                                                         int64_t stride, uint32_t *hist0) {
+                                                         int64_t stride, TopkWs sel) {
   __shared__ float qs[kF32MaxQ];
   __shared__ float ws[64];
   __shared__ uint32_t hist[kHist0Bins];
+  const bool want_hist = sel.hist0 != nullptr;
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int HI, int 
   if (base >= n) return;
   for (int i = threadIdx.x; i < HI * DI; i += kF32Block) qs[i] = q_idx[(size_t)t * HI * DI + i];
   for (int i = threadIdx.x; i < HI; i += kF32Block) ws[i] = w[(size_t)t * HI + i];
-  if (hist0) hist_zero(hist);
+  if (want_hist) hist_zero(hist);
   __syncthreads();
   const int s = base + threadIdx.x;
   if (s < n) {
@@ -72,85 +73,158 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int HI, int 
     }
     acc += 0.0f;  // -0 -> +0
     scores[t * stride + s] = acc;
-    if (hist0) atomicAdd(&hist[score_key(acc) >> kHist0Shift], 1u);
+    if (want_hist) atomicAdd(&hist[score_key(acc) >> kHist0Shift], 1u);
   }
-  if (hist0) hist_flush(hist, hist0 + (size_t)t * kHist0Bins);
+  if (want_hist) hist_flush(hist, sel.hist0 + (size_t)t * kHist0Bins);
 }
 
 // --------------------------------------------------------------------------
 // FP8 MFMA path (HI = 64, DI = 128)
+//
+// Each wave streams its own contiguous range of keys. 64-key tiles (8 KiB)
+// are copied global -> LDS with LDS-DMA (global_load_lds_dwordx4): every DMA
+// instruction moves 1 KiB of consecutive bytes, and two tiles per wave are in
+// flight. The MFMA B operand is then read from LDS in the layout the
+// 16x16x128 FP8 MFMA wants. Within a 128-byte key row the 32-byte segments are
+// XOR-swizzled by key so that the 16 keys read by one instruction spread over
+// the LDS banks; the swizzle is applied on the DMA source side.
 // --------------------------------------------------------------------------
-constexpr int kFp8Waves = 4;
-constexpr int kFp8Iters = 8;                                   // 64-key steps per wave
-constexpr int kFp8Chunk = kFp8Waves * kFp8Iters * 64;          // keys per workgroup
+constexpr int kIdxWaves = 4;                 // waves per workgroup
+constexpr int kIdxTileKeys = 64;             // keys per DMA tile
+constexpr int kIdxTileBytes = kIdxTileKeys * 128;
+constexpr int kIdxDmaPerTile = kIdxTileBytes / (64 * 16);  // 8 DMA issues per lane
+constexpr int kIdxBufs = 2;                  // tiles in flight per wave
+constexpr size_t kIdxSmem = (size_t)kIdxWaves * kIdxBufs * kIdxTileBytes;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i &a, const v8i &b, const v4f &c) {
   // E4M3 x E4M3 (format code 0), unit E8M0 scales (127 = 2^0)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__device__ __forceinline__ void load_key_tiles(v8i (&b)[4], const uint8_t *__restrict__ k_idx,
-                                               int64_t start, int n, int base, int lane) {
-  const int kg = lane >> 4;  // which 32-byte quarter of the 128-byte key
+// LDS atomic add without a return value, issued as inline asm so that the
+// compiler does not make it wait for the wave's in-flight LDS-DMA copies
+// (it cannot tell that the histogram and the DMA buffers do not overlap).
+// It has no result register; later lgkmcnt waits cover its completion.
+__device__ __forceinline__ void lds_add_u32(uint32_t *p, uint32_t v) {
+  const uint32_t addr =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)p;
+  asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// segment swizzle of key row r: 16-byte piece q lives at piece q ^ swz(r)
+__device__ __forceinline__ int key_swz(int r) { return ((r >> 1) & 3) << 1; }
+
+// Byte offset, inside a 64-key tile, of the global 16-byte piece that lane
+// `lane` copies with DMA issue i (add i * 1024): piece p = 64 i + lane of the
+// LDS tile holds key row p / 8, global piece (p % 8) ^ key_swz(row); the
+// swizzle only depends on the lane because rows advance by 8 per issue.
+__device__ __forceinline__ int key_dma_offset(int lane) {
+  const int r = lane >> 3;
+  return r * 128 + (((lane & 7) ^ key_swz(r)) << 4);
+}
+
+// Issue the DMA of one 64-key tile (keys base.., clamped to n-1) into `buf`.
+__device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t *__restrict__ k_idx,
+                                               int64_t start, int n, int base, int lane,
+                                               int lane_off) {
+  if (base + kIdxTileKeys <= n) {
+    const uint8_t *src = k_idx + (start + base) * 128 + lane_off;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    int key = base + kt * 16 + (lane & 15);
-    key = key < n ? key : n - 1;
-    const v4i *src = (const v4i *)(k_idx + (start + key) * 128 + kg * 32);
-    v4i lo = __builtin_nontemporal_load(src);
-    v4i hi = __builtin_nontemporal_load(src + 1);
-    b[kt] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    for (int i = 0; i < kIdxDmaPerTile; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 1024, (lds_void *)(buf + i * 1024), 16, 0, 0);
+  } else {
+    // sequence tail: rows past the end repeat the last key (their scores are dropped)
+#pragma unroll
+    for (int i = 0; i < kIdxDmaPerTile; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      int key = base + r;
+      key = key < n ? key : n - 1;
+      const uint8_t *src = k_idx + (start + key) * 128 + (lane_off & 127);
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, 0);
+    }
   }
 }
 
 template <bool kHist>
-__global__ __launch_bounds__(256) void k_index_fp8(SeqMeta m, const uint8_t *__restrict__ q_idx,
-                                                   const float *__restrict__ w,
-                                                   const uint8_t *__restrict__ k_idx,
-                                                   float *__restrict__ scores, int64_t stride,
-                                                   uint32_t *hist0) {
-  __shared__ uint32_t hist[kHist ? kHist0Bins : 1];
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int k, int iters,
+                                                              const uint8_t *__restrict__ q_idx,
+                                                              const float *__restrict__ w,
+                                                              const uint8_t *__restrict__ k_idx,
+                                                              float *__restrict__ scores,
+                                                              int64_t stride, TopkWs sel) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // level-0 histogram with two 16-bit bins per word (a workgroup scores at most
+  // 4 x 32 x 64 = 8192 keys, so a bin cannot overflow)
+  __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
-  const int chunk0 = blockIdx.x * kFp8Chunk;
+  const int wave_keys = iters * kIdxTileKeys;
+  const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
   if (chunk0 >= n) return;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int kg = lane >> 4;
+  const int kg = lane >> 4, c16 = lane & 15;
 
-  // A tiles: head (ht*16 + lane%16), bytes [32*kg, 32*kg+32) of its 128-byte row
+  // A tiles: head (ht*16 + c16), bytes [32*kg, 32*kg+32) of its 128-byte row
   v8i a[4];
   float wv[16];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + (lane & 15)) * 128 + kg * 32);
-    v4i lo = src[0], hi = src[1];
+    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
+    const v4i lo = src[0], hi = src[1];
     a[ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     // accumulator row r of this lane is head ht*16 + 4*kg + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
   }
-  if (kHist) hist_zero(hist);
+  if (kHist) {
+    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
+    __syncthreads();
+  }
 
-  v8i bcur[4], bnext[4];
-  int base = chunk0 + wave * 64;
-  if (base < n) load_key_tiles(bcur, k_idx, start, n, base, lane);
-  for (int it = 0; it < kFp8Iters; ++it) {
-    if (base >= n) break;
-    const int nbase = base + kFp8Waves * 64;
-    const bool more = (it + 1 < kFp8Iters) && (nbase < n);
-    if (more) load_key_tiles(bnext, k_idx, start, n, nbase, lane);
-
+  const int wbase = chunk0 + wave * wave_keys;
+  const int nit = wbase < n ? min(iters, (n - wbase + kIdxTileKeys - 1) / kIdxTileKeys) : 0;
+  unsigned char *mybuf = smem + (size_t)wave * kIdxBufs * kIdxTileBytes;
+  const int lane_off = key_dma_offset(lane);
+  // the q/w loads above must have landed before the DMA counting starts
+  wait_vmcnt<0>();
+  if (nit > 0) issue_key_tile(mybuf, k_idx, start, n, wbase, lane, lane_off);
+  if (nit > 1) issue_key_tile(mybuf + kIdxTileBytes, k_idx, start, n, wbase + kIdxTileKeys, lane, lane_off);
+  float *srow = scores + t * stride;
+  for (int it = 0; it < nit; ++it) {
+    // Outstanding vector-memory ops issued after tile `it`: the score store of
+    // iteration it-1 (if any) and the DMA of tile it+1 (if any). They retire in
+    // order, so waiting down to that many guarantees tile `it` has landed.
+    const int later = (it > 0 ? 1 : 0) + (it + 1 < nit ? kIdxDmaPerTile : 0);
+    if (later == kIdxDmaPerTile + 1) wait_vmcnt<kIdxDmaPerTile + 1>();
+    else if (later == kIdxDmaPerTile) wait_vmcnt<kIdxDmaPerTile>();
+    else if (later == 1) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    const unsigned char *tb = mybuf + (it & 1) * kIdxTileBytes;
     float part[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+      const int r = kt * 16 + c16;
+      const unsigned char *rp = tb + r * 128 + ((2 * kg) ^ key_swz(r)) * 16;
+      const v4i lo = *(const v4i *)rp;
+      const v4i hi = *(const v4i *)(rp + 16);
+      const v8i b = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       float acc = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
-        v4f d = mfma_fp8(a[ht], bcur[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+        const v4f d = mfma_fp8(a[ht], b, (v4f){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc = fmaf(fmaxf(d[r], 0.0f), wv[ht * 4 + r], acc);
+        for (int rr = 0; rr < 4; ++rr) acc = fmaf(fmaxf(d[rr], 0.0f), wv[ht * 4 + rr], acc);
       }
       part[kt] = acc;
     }
@@ -160,51 +234,87 @@ __global__ __launch_bounds__(256) void k_index_fp8(SeqMeta m, const uint8_t *__r
     const bool b4 = (lane & 16) != 0;
     float k0 = b5 ? part[2] : part[0];
     float k1 = b5 ? part[3] : part[1];
-    float s0 = b5 ? part[0] : part[2];
-    float s1 = b5 ? part[1] : part[3];
+    const float s0 = b5 ? part[0] : part[2];
+    const float s1 = b5 ? part[1] : part[3];
     k0 += __shfl_xor(s0, 32, 64);
     k1 += __shfl_xor(s1, 32, 64);
     float keep = b4 ? k1 : k0;
-    float send = b4 ? k0 : k1;
+    const float send = b4 ? k0 : k1;
     keep += __shfl_xor(send, 16, 64);
     keep += 0.0f;  // -0 -> +0
-    const int s = base + lane;
-    if (s < n) {
-      scores[t * stride + s] = keep;
-      if (kHist) atomicAdd(&hist[score_key(keep) >> kHist0Shift], 1u);
+    const int s = wbase + it * kIdxTileKeys + lane;
+    // the tile buffer is free once this iteration's LDS reads completed
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    if (s < n) srow[s] = keep;
+    if (it + 2 < nit)
+      issue_key_tile(mybuf + (it & 1) * kIdxTileBytes, k_idx, start, n,
+                     wbase + (it + 2) * kIdxTileKeys, lane, lane_off);
+    if (kHist && s < n) {
+      const uint32_t bin = score_key(keep) >> kHist0Shift;
+      lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
     }
-    if (more) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) bcur[kt] = bnext[kt];
-    }
-    base = nbase;
   }
-  if (kHist) hist_flush(hist, hist0 + (size_t)t * kHist0Bins);
+  if (kHist) {
+    __syncthreads();
+    uint32_t *g = sel.hist0 + (size_t)t * kHist0Bins;
+    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) {
+      const uint32_t c = hist[i];
+      if (c & 0xFFFFu) atomicAdd(g + 2 * i, c & 0xFFFFu);
+      if (c >> 16) atomicAdd(g + 2 * i + 1, c >> 16);
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_index_f32(const SeqMeta &m, int T, int HI, int DI, const float *q_idx,
+int index_fp8_iters(int T, int max_kv_len) {
+  // aim for about eight 4-wave workgroups per CU over the whole batch
+  const int64_t keys = (int64_t)T * max_kv_len;
+  const int64_t per_iter = 2048LL * kIdxWaves * kIdxTileKeys;
+  int64_t it = (keys + per_iter - 1) / per_iter;
+  if (it < 2) it = 2;
+  if (it > 32) it = 32;
+  return (int)it;
+}
+
+namespace {
+}  // namespace
+
+hipError_t launch_index_f32(const SeqMeta &m, int T, int k, int HI, int DI, const float *q_idx,
                             const float *w, const float *k_idx, float *scores, int64_t stride,
-                            uint32_t *hist0, hipStream_t s) {
+                            const TopkWs *sel, hipStream_t s) {
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
+  TopkWs none{};
   dim3 grid((m.max_kv_len + kF32Block - 1) / kF32Block, T);
-  hipLaunchKernelGGL(k_index_f32, grid, dim3(kF32Block), 0, s, m, HI, DI, q_idx, w, k_idx,
-                     scores, stride, hist0);
+  hipLaunchKernelGGL(k_index_f32, grid, dim3(kF32Block), 0, s, m, k, HI, DI, q_idx, w, k_idx,
+                     scores, stride, sel ? *sel : none);
   return hipGetLastError();
 }
 
-hipError_t launch_index_fp8(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
-                            const uint8_t *k_idx, float *scores, int64_t stride, uint32_t *hist0,
+hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx, const float *w,
+                            const uint8_t *k_idx, float *scores, int64_t stride, const TopkWs *sel,
                             hipStream_t s) {
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
-  dim3 grid((m.max_kv_len + kFp8Chunk - 1) / kFp8Chunk, T);
-  if (hist0)
-    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(256), 0, s, m, q_idx, w, k_idx, scores,
-                       stride, hist0);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIdxSmem);
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIdxSmem);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  const int iters = index_fp8_iters(T, m.max_kv_len);
+  const int per_wg = kIdxWaves * iters * kIdxTileKeys;
+  dim3 grid((m.max_kv_len + per_wg - 1) / per_wg, T);
+  TopkWs none{};
+  if (sel)
+    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, k, iters,
+                       q_idx, w, k_idx, scores, stride, *sel);
   else
-    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(256), 0, s, m, q_idx, w, k_idx, scores,
-                       stride, hist0);
+    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, k, iters,
+                       q_idx, w, k_idx, scores, stride, none);
   return hipGetLastError();
 }
 

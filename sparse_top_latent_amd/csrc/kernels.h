@@ -10,24 +10,30 @@ hipError_t launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
 
 // --- indexer score pass ----------------------------------------------------
 // scores[t * stride + s] for s < n_t; hist0 (T x 4096, zeroed) optional.
-hipError_t launch_index_f32(const SeqMeta &m, int T, int HI, int DI, const float *q_idx,
+struct TopkWs;
+// With `sel` set, the indexer also builds the level-0 histogram (sel->hist0).
+hipError_t launch_index_f32(const SeqMeta &m, int T, int k, int HI, int DI, const float *q_idx,
                             const float *w, const float *k_idx, float *scores, int64_t stride,
-                            uint32_t *hist0, hipStream_t s);
-hipError_t launch_index_fp8(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
-                            const uint8_t *k_idx, float *scores, int64_t stride, uint32_t *hist0,
+                            const TopkWs *sel, hipStream_t s);
+hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx, const float *w,
+                            const uint8_t *k_idx, float *scores, int64_t stride, const TopkWs *sel,
                             hipStream_t s);
 
 // --- top-k select -----------------------------------------------------------
 struct TopkWs {
-  uint32_t *hist0;    // [T, 4096]
+  uint32_t *hist0;    // [T, 4096]  level-0 histogram (zeroed before the indexer)
+  uint32_t *hist1;    // [T, 1024]  level-1 histogram of bin b0 (zeroed with hist0)
+  uint2 *thr;         // [T]        (b0, count above bin b0)
   uint32_t *counts;   // [T, nchunk]
   uint2 *entries;     // [T, nchunk * kTopkChunk] (position, key)
   int32_t nchunk;     // ceil(max_kv_len / kTopkChunk)
+  size_t zero_words;  // hist0 + hist1 words to clear before each selection
 };
 size_t topk_ws_bytes(int T, int max_kv_len);
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len);
 hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
-                             uint32_t *hist0, hipStream_t s);
+                             const TopkWs &w, hipStream_t s);
+hipError_t launch_topk_thr0(const SeqMeta &m, int T, int k, const TopkWs &w, hipStream_t s);
 hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
                             const TopkWs &w, int32_t *topk_idx, hipStream_t s);
 hipError_t launch_topk_final(const SeqMeta &m, int T, int k, const TopkWs &w, int32_t *topk_idx,

@@ -22,7 +22,7 @@
 //      online softmax per head in fp32 (exp2 domain),
 //      O^T += V^T . P^T  with bf16 MFMA; P^T comes straight from the S^T
 //      accumulator layout, V^T is read column-wise from the LDS tile.
-//    It writes an fp32 partial (max, sum, O) per (query, split, head).
+//    It writes a partial (max, sum in fp32; O in bf16) per (query, split, head).
 //  * k_mla_combine: merges the splits of each (query, head) with the usual
 //    log-sum-exp rescaling and applies the gate in the epilogue.
 
@@ -188,7 +188,7 @@ __device__ __forceinline__ void dma16(const void *src, unsigned char *lds_wave_b
 }
 
 template <bool kMx>
-__global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, float *__restrict__ opart,
+__global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, uint16_t *__restrict__ opart,
                                                    float2 *__restrict__ ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int64_t rows[kMlaRowsPerSplit];
@@ -372,26 +372,40 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, float *__restrict_
       acc[ct] = mfma_bf16(va, pb, acc[ct]);
     }
   }
-  // partial O^T: lane holds channels ct*16 + 4g + i of head `head`
+  // partial O^T in bf16 (the softmax weights are still unnormalised, so only
+  // relative precision matters): lane holds channels ct*16 + 4g + i of `head`
   const size_t pbase = (((size_t)t * S + split) * kH + head) * kDc;
 #pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) *(v4f *)(opart + pbase + ct * 16 + 4 * g) = acc[ct];
+  for (int ct = 0; ct < kCt; ++ct) {
+    const uint32_t lo = f32_to_bf16_bits(acc[ct][0]) | (f32_to_bf16_bits(acc[ct][1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(acc[ct][2]) | (f32_to_bf16_bits(acc[ct][3]) << 16);
+    *(uint2 *)(opart + pbase + ct * 16 + 4 * g) = make_uint2(lo, hi);
+  }
   if (g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m_run, l_run);
 }
 
 constexpr int kMaxSplits = 2048 / kMlaRowsPerSplit;
 
-__global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const float *__restrict__ opart,
+__global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const uint16_t *__restrict__ opart,
                                                      const float2 *__restrict__ ml, int S) {
   const int h = blockIdx.x, t = blockIdx.y;
   const int c = threadIdx.x * 4;
+  // gate logits first: their loads overlap the partial loads below
+  float gv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.gate) {
+    const size_t gi = ((size_t)t * kH + h) * kDc + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gv[i] = load_as_f32(a.gate, a.gate_dtype, gi + i);
+  }
   float2 st[kMaxSplits];
   v4f x[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < S) {
       st[s] = ml[((size_t)t * S + s) * kH + h];
-      x[s] = *(const v4f *)(opart + (((size_t)t * S + s) * kH + h) * kDc + c);
+      const uint2 b = *(const uint2 *)(opart + (((size_t)t * S + s) * kH + h) * kDc + c);
+      x[s] = (v4f){bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
+                   bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16)};
     }
   }
   float M = -INFINITY;
@@ -417,11 +431,17 @@ __global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const float *__r
     lse = M / kLog2e + __logf(wsum);
   }
   const size_t oi = ((size_t)t * kH + h) * kDc + c;
+  float y[4] = {o[0], o[1], o[2], o[3]};
+  if (a.gate) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float y = o[i];
-    if (a.gate) y *= sigmoidf_exact_ends(load_as_f32(a.gate, a.gate_dtype, oi + i));
-    store_from_f32(a.out, a.out_dtype, oi + i, y);
+    for (int i = 0; i < 4; ++i) y[i] *= sigmoidf_exact_ends(gv[i]);
+  }
+  if (a.out_dtype == SGA_BF16) {
+    const uint32_t lo = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+    *(uint2 *)((uint16_t *)a.out + oi) = make_uint2(lo, hi);
+  } else {
+    *(v4f *)((float *)a.out + oi) = (v4f){y[0], y[1], y[2], y[3]};
   }
   if (a.lse && threadIdx.x == 0) a.lse[(size_t)t * kH + h] = lse;
 }
@@ -440,14 +460,14 @@ static int mla_splits(int k) { return (k + kMlaRowsPerSplit - 1) / kMlaRowsPerSp
 
 size_t mla_split_ws_bytes(int T, int k) {
   size_t S = (size_t)mla_splits(k);
-  return align256((size_t)T * S * kH * kDc * 4) + align256((size_t)T * S * kH * sizeof(float2));
+  return align256((size_t)T * S * kH * kDc * 2) + align256((size_t)T * S * kH * sizeof(float2));
 }
 
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int S = mla_splits(a.k);
-  float *opart = (float *)ws;
-  float2 *ml = (float2 *)((char *)ws + align256((size_t)a.T * S * kH * kDc * 4));
+  uint16_t *opart = (uint16_t *)ws;
+  float2 *ml = (float2 *)((char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void *)k_mla_split<false>,
@@ -467,8 +487,8 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
 hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int S = mla_splits(a.k);
-  const float *opart = (const float *)ws;
-  const float2 *ml = (const float2 *)((const char *)ws + align256((size_t)a.T * S * kH * kDc * 4));
+  const uint16_t *opart = (const uint16_t *)ws;
+  const float2 *ml = (const float2 *)((const char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
   hipLaunchKernelGGL(k_mla_combine, dim3(kH, a.T), dim3(128), 0, s, a, opart, ml, S);
   return hipGetLastError();
 }

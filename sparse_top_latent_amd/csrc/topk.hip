@@ -10,18 +10,23 @@
 // most significant digit first (12 + 10 + 10 bits):
 //  1. level-0 histogram of key bits 31..20 (built by the indexer in the fused
 //     layer, or by k_topk_hist0);
-//  2. k_topk_scan, many workgroups per query: every workgroup finds the level-0
-//     threshold bin b0 from the histogram, then compacts, in position order,
-//     the (position, key) pairs of its chunk whose digit is >= b0 (everything
-//     above b0 is certainly selected; bin b0 holds the threshold);
-//  3. k_topk_final, one workgroup per query: refines the threshold inside bin b0
-//     with two more 1024-bin histograms over the compacted pairs, giving the
-//     exact k-th key K* and how many ties at K* to take; a final ordered pass
-//     emits key > K* plus the first `take` ties, which are the lowest
-//     positions because chunks and their pairs are visited in position order.
+//  2. k_topk_thr0, one workgroup per query: the level-0 threshold bin b0 (the
+//     bin holding the k-th largest key) and the count of keys above it;
+//  3. k_topk_scan, many workgroups per query: compacts, in position order, the
+//     (position, key) pairs of its chunk whose digit is >= b0 (everything above
+//     b0 is certainly selected; bin b0 holds the threshold) and adds the
+//     level-1 histogram (key bits 19..10) of the bin-b0 keys;
+//  4. k_topk_final, one workgroup per query: takes the level-1 bin from that
+//     histogram, lists the pairs that share the top 22 bits of the threshold
+//     while staging all pairs in LDS, resolves the last 10 bits with a third
+//     histogram, giving the exact k-th key K* and how many ties at K* to take;
+//     an ordered pass then emits key > K* plus the first `take` ties, which are
+//     the lowest positions because chunks and their pairs are visited in
+//     position order.
 // No atomics decide the output, so it is deterministic.
 
 #include "kernels.h"
+#include "select_common.h"
 
 namespace sga {
 
@@ -40,7 +45,7 @@ __global__ void k_zero_u32(uint32_t *p, size_t n) {
 }
 
 __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__restrict__ scores,
-                                                    int64_t stride, uint32_t *hist0) {
+                                                    int64_t stride, TopkWs ws) {
   __shared__ uint32_t hist[kHist0Bins];
   const int t = blockIdx.y;
   int64_t start;
@@ -57,48 +62,18 @@ __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__re
   __syncthreads();
   for (int i = threadIdx.x; i < kHist0Bins; i += 256) {
     uint32_t c = hist[i];
-    if (c) atomicAdd(hist0 + (size_t)t * kHist0Bins + i, c);
+    if (c) atomicAdd(ws.hist0 + (size_t)t * kHist0Bins + i, c);
   }
 }
 
-// Finds the bin b holding the `want`-th largest element of a histogram: the
-// count of elements in bins above b (returned in *above) is < want and adding
-// bin b reaches want. Each of blockDim threads owns nbins/blockDim consecutive bins.
-template <int NB>
-__device__ __forceinline__ int find_threshold_bin(const uint32_t *hist, uint32_t want,
-                                                  uint32_t *above, uint32_t *scratch,
-                                                  int *res) {
-  const int per = NB / (int)blockDim.x;
-  const int tid = threadIdx.x;
-  // thread tid owns bins [(nthreads-1-tid)*per, ...) so that an exclusive scan in
-  // thread order is a suffix scan over bins (largest bins first)
-  const int hi_bin = NB - 1 - tid * per;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[hi_bin - i];
-  uint32_t total;
-  uint32_t excl = block_exclusive_scan(local, scratch, &total);
-  if (tid == 0) {
-    res[0] = -1;
-    res[1] = 0;
-  }
-  __syncthreads();
-  if (excl < want && excl + local >= want) {
-    uint32_t acc = excl;
-    for (int i = 0; i < per; ++i) {
-      uint32_t c = hist[hi_bin - i];
-      if (acc + c >= want) {
-        res[0] = hi_bin - i;
-        res[1] = (int)acc;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
-  int b = res[0];
-  *above = (uint32_t)res[1];
-  __syncthreads();
-  return b;
+// One workgroup per query: level-0 threshold bin from the finished histogram.
+__global__ __launch_bounds__(256) void k_topk_thr0(SeqMeta m, int k, TopkWs ws) {
+  __shared__ uint32_t scratch[256 / 64 + 1];
+  const int t = blockIdx.x;
+  int64_t start;
+  const int n = query_candidates(m, t, &start);
+  if (n <= k) return;
+  publish_threshold0(ws, t, k, scratch, nullptr);
 }
 
 template <bool kVec>
@@ -106,9 +81,8 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
                                                           const float *__restrict__ scores,
                                                           int64_t stride, TopkWs ws,
                                                           int32_t *__restrict__ topk_idx) {
-  __shared__ uint32_t hist[kHist0Bins];
+  __shared__ uint32_t h1[kHist12Bins];
   __shared__ uint32_t scratch[kScanBlock / 64 + 1];
-  __shared__ int res[2];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
@@ -138,11 +112,8 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) v[j] = p0 + j < n ? row[p0 + j] : 0.0f;
   }
-  const uint32_t *h = ws.hist0 + (size_t)t * kHist0Bins;
-  for (int i = threadIdx.x; i < kHist0Bins; i += kScanBlock) hist[i] = h[i];
-  __syncthreads();
-  uint32_t above;
-  const int b0 = find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &above, scratch, res);
+  const uint2 thr = ws.thr[t];
+  const int b0 = (int)thr.x;
 
   uint32_t keys[kPerThread];
   uint32_t cnt = 0;
@@ -152,18 +123,28 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
     keys[j] = key;
     cnt += (p0 + j < n && (int)(key >> kHist0Shift) >= b0) ? 1u : 0u;
   }
+  // level-1 histogram (key bits 19..10) of this chunk's keys in bin b0
+  for (int i = threadIdx.x; i < kHist12Bins; i += kScanBlock) h1[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j)
+    if (p0 + j < n && (int)(keys[j] >> kHist0Shift) == b0)
+      atomicAdd(&h1[(keys[j] >> (kHist0Shift - 10)) & 1023u], 1u);
   uint32_t total;
-  uint32_t off = block_exclusive_scan(cnt, scratch, &total);
+  uint32_t off = block_exclusive_scan(cnt, scratch, &total);  // includes barriers
   uint2 *dst = ws.entries + ((size_t)t * ws.nchunk + blockIdx.x) * kTopkChunk;
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     if (p0 + j < n && (int)(keys[j] >> kHist0Shift) >= b0)
       dst[off++] = make_uint2((uint32_t)(p0 + j), keys[j]);
   }
+  uint32_t *g1 = ws.hist1 + (size_t)t * kHist12Bins;
+  for (int i = threadIdx.x; i < kHist12Bins; i += kScanBlock) {
+    const uint32_t c = h1[i];
+    if (c) atomicAdd(g1 + i, c);
+  }
   if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunk + blockIdx.x] = total;
 }
-
-constexpr int kBatch = 8;  // independent loads in flight per thread
 
 // Chunk holding flat pair index f (offs ascending, offs[0] = 0, offs[nch] = total > f).
 __device__ __forceinline__ int chunk_of(const uint32_t *offs, int nch, uint32_t f) {
@@ -175,91 +156,107 @@ __device__ __forceinline__ int chunk_of(const uint32_t *offs, int nch, uint32_t 
   return lo;
 }
 
+constexpr int kBatch = 8;    // independent loads in flight per thread
+constexpr int kL2Cap = 2048;  // pairs sharing the top 22 key bits of the threshold
+
 __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, TopkWs ws,
                                                             int32_t *__restrict__ topk_idx) {
   extern __shared__ uint2 pairs[];  // kFinalCap entries
-  __shared__ uint32_t hist[kHist0Bins];
+  __shared__ uint32_t hist[kHist12Bins];
   __shared__ uint32_t offs[kMaxChunks + 1];
+  __shared__ uint32_t l2keys[kL2Cap];
   __shared__ uint32_t scratch[kFinalBlock / 64 + 1];
   __shared__ int res[2];
+  __shared__ uint32_t l2n;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   int64_t start;
   const int n = query_candidates(m, t, &start);
   if (n <= k) return;
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
-  const uint32_t *h0 = ws.hist0 + (size_t)t * kHist0Bins;
   const uint32_t *cnts = ws.counts + (size_t)t * ws.nchunk;
-  // chunk counts (<= 2 per thread) and the level-0 histogram, loaded together
+  // chunk counts (<= 2 per thread), the level-1 histogram and the level-0 result
   const uint32_t c_a = 2 * tid < nch ? cnts[2 * tid] : 0u;
   const uint32_t c_b = 2 * tid + 1 < nch ? cnts[2 * tid + 1] : 0u;
-  for (int i = tid; i < kHist0Bins; i += kFinalBlock) hist[i] = h0[i];
+  const uint32_t *h1 = ws.hist1 + (size_t)t * kHist12Bins;
+  for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = h1[i];
+  const uint2 thr = ws.thr[t];
+  const uint32_t b0 = thr.x;
+  uint32_t want = (uint32_t)k - thr.y;
+  if (tid == 0) l2n = 0u;
   __syncthreads();
-  uint32_t above0;
-  const int b0 = find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &above0, scratch, res);
-  uint32_t want = (uint32_t)k - above0;
   uint32_t total;
   const uint32_t ex = block_exclusive_scan(c_a + c_b, scratch, &total);
   if (2 * tid < nch) offs[2 * tid] = ex;
   if (2 * tid + 1 < nch) offs[2 * tid + 1] = ex + c_a;
   if (tid == 0) offs[nch] = total;
-  __syncthreads();
+  uint32_t above1;
+  const int b1 = find_threshold_bin<kHist12Bins>(hist, want, &above1, scratch, res);
+  want -= above1;
+  const uint32_t prefix22 = (b0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
 
+  // stage the pairs in position order: a group of threads per chunk, no search;
+  // pairs that share the top 22 bits of K* are also listed for level 2
   const uint2 *src = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
   const bool staged = total <= (uint32_t)kFinalCap;
-  auto gload = [&](uint32_t f) -> uint2 {
+  int gsz = kFinalBlock;
+  while (gsz > 1 && gsz > kFinalBlock / nch) gsz >>= 1;  // threads per chunk (power of 2)
+  if (gsz * nch > kFinalBlock) gsz = 1;
+  const int groups = kFinalBlock / gsz;
+  const int gid = tid / gsz, gl = tid % gsz;
+  for (int c0 = 0; c0 < nch; c0 += groups) {
+    const int c = c0 + gid;
+    if (c < nch) {
+      const uint32_t cnt = offs[c + 1] - offs[c];
+      const uint2 *cs = src + (size_t)c * kTopkChunk;
+      for (uint32_t i0 = gl; i0 < cnt; i0 += gsz * kBatch) {
+        uint2 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = i0 + u * gsz;
+          if (i < cnt) v[u] = cs[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = i0 + u * gsz;
+          if (i < cnt) {
+            if (staged) pairs[offs[c] + i] = v[u];
+            if ((v[u].y >> 10) == prefix22) {
+              const uint32_t slot = atomicAdd(&l2n, 1u);
+              if (slot < (uint32_t)kL2Cap) l2keys[slot] = v[u].y;
+            }
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // level 2: the last 10 bits among the listed pairs
+  for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t nl2 = l2n;
+  if (nl2 <= (uint32_t)kL2Cap) {
+    for (uint32_t i = tid; i < nl2; i += kFinalBlock) atomicAdd(&hist[l2keys[i] & 1023u], 1u);
+  } else {
+    // more than kL2Cap pairs share 22 bits: histogram them from the pair list
+    for (uint32_t f = tid; f < total; f += kFinalBlock) {
+      const int c = chunk_of(offs, nch, f);
+      const uint32_t key = src[(size_t)c * kTopkChunk + (f - offs[c])].y;
+      if ((key >> 10) == prefix22) atomicAdd(&hist[key & 1023u], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t above2;
+  const int b2 = find_threshold_bin<kHist12Bins>(hist, want, &above2, scratch, res);
+  want -= above2;
+  const uint32_t kstar = (prefix22 << 10) | (uint32_t)b2;  // the exact k-th largest key
+  const uint32_t take = want;                                 // ties at kstar to keep
+
+  auto pair_at = [&](uint32_t f) -> uint2 {
+    if (staged) return pairs[f];
     const int c = chunk_of(offs, nch, f);
     return src[(size_t)c * kTopkChunk + (f - offs[c])];
   };
-  if (staged) {
-    for (uint32_t base = 0; base < total; base += kFinalBlock * kBatch) {
-      uint2 v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t f = base + u * kFinalBlock + tid;
-        if (f < total) v[u] = gload(f);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t f = base + u * kFinalBlock + tid;
-        if (f < total) pairs[f] = v[u];
-      }
-    }
-    __syncthreads();
-  }
-  auto pair_at = [&](uint32_t f) -> uint2 { return staged ? pairs[f] : gload(f); };
-
-  // levels 1 and 2: refine the threshold inside bin b0
-  uint32_t prefix = (uint32_t)b0;  // known high bits of K*
-  int shift = kHist0Shift;
-#pragma unroll 1
-  for (int level = 1; level <= 2; ++level) {
-    for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
-    __syncthreads();
-    const int nshift = shift - 10;
-    for (uint32_t base = 0; base < total; base += kFinalBlock * kBatch) {
-      uint2 v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t f = base + u * kFinalBlock + tid;
-        v[u] = f < total ? pair_at(f) : make_uint2(0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t f = base + u * kFinalBlock + tid;
-        if (f < total && (v[u].y >> shift) == prefix) atomicAdd(&hist[(v[u].y >> nshift) & 1023u], 1u);
-      }
-    }
-    __syncthreads();
-    uint32_t above;
-    const int b = find_threshold_bin<kHist12Bins>(hist, want, &above, scratch, res);
-    want -= above;
-    prefix = (prefix << 10) | (uint32_t)b;
-    shift = nshift;
-  }
-  const uint32_t kstar = prefix;  // the exact k-th largest key
-  const uint32_t take = want;     // ties at kstar to keep (lowest positions)
-
   // ordered emission: each thread owns a contiguous run of pairs
   const uint32_t seg = (total + kFinalBlock - 1) / kFinalBlock;
   const uint32_t s0 = min(total, tid * seg), s1 = min(total, s0 + seg);
@@ -302,8 +299,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t topk_ws_bytes(int T, int max_kv_len) {
   size_t nch = ((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk;
-  return align256((size_t)T * kHist0Bins * 4) + align256((size_t)T * nch * 4) +
-         align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
+  return align256((size_t)T * (kHist0Bins + kHist12Bins) * 4) + align256((size_t)T * sizeof(uint2)) +
+         align256((size_t)T * nch * 4) + align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
 }
 
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
@@ -311,7 +308,11 @@ TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
   w.nchunk = (int32_t)(((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk);
   char *p = (char *)ws;
   w.hist0 = (uint32_t *)p;
-  p += align256((size_t)T * kHist0Bins * 4);
+  w.hist1 = w.hist0 + (size_t)T * kHist0Bins;
+  w.zero_words = (size_t)T * (kHist0Bins + kHist12Bins);
+  p += align256((size_t)T * (kHist0Bins + kHist12Bins) * 4);
+  w.thr = (uint2 *)p;
+  p += align256((size_t)T * sizeof(uint2));
   w.counts = (uint32_t *)p;
   p += align256((size_t)T * w.nchunk * 4);
   w.entries = (uint2 *)p;
@@ -319,10 +320,16 @@ TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
 }
 
 hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
-                             uint32_t *hist0, hipStream_t s) {
+                             const TopkWs &w, hipStream_t s) {
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   dim3 grid((m.max_kv_len + kTopkChunk - 1) / kTopkChunk, T);
-  hipLaunchKernelGGL(k_topk_hist0, grid, dim3(256), 0, s, m, scores, stride, hist0);
+  hipLaunchKernelGGL(k_topk_hist0, grid, dim3(256), 0, s, m, scores, stride, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_thr0(const SeqMeta &m, int T, int k, const TopkWs &w, hipStream_t s) {
+  if (T == 0 || m.max_kv_len <= k) return hipSuccess;
+  hipLaunchKernelGGL(k_topk_thr0, dim3(T), dim3(256), 0, s, m, k, w);
   return hipGetLastError();
 }
 
