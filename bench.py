@@ -146,6 +146,54 @@ def cpu_baseline(case, budget_s=15.0):
     }
 
 
+def indexer_flops(case):
+    lens = case.kv_len.cpu().tolist()
+    seqs = case.q_seq.cpu().tolist()
+    pos = case.q_pos.cpu().tolist()
+    pairs = sum(max(0, min(p + 1, lens[b])) for b, p in zip(seqs, pos))
+    return 2.0 * case.idx_heads * case.idx_dim * pairs, pairs
+
+
+def indexer_only(args, case, prob, sga, torch):
+    """The indexer score pass alone (the unit of the prefill target)."""
+    scores = torch.empty((case.num_q, case.max_kv_len), dtype=torch.float32, device="cuda")
+    kis = [case.k_idx] + [case.k_idx.clone() for _ in range(args.copies - 1)]
+
+    def step(i):
+        sga.sga_index_scores(prob, case.q_idx, case.w, kis[i % args.copies], scores)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops, pairs = indexer_flops(case)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] indexer {case.name}: {ms * 1e3:.1f} us per pass, {tflops:.0f} TFLOP/s "
+        f"({tflops / FP8_PEAK_TFLOPS:.1%} of FP8 MFMA peak), {pairs} (query, key) pairs")
+    print(json.dumps({
+        "metric": "SGA prefill indexer score pass TFLOP/s; % of FP8 MFMA peak",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": case.name, "queries": case.num_q, "ctx": case.max_kv_len,
+                   "idx_heads": case.idx_heads, "idx_dim": case.idx_dim},
+        "roofline": {"bound": "mfma", "kernel": "indexer score pass", "achieved": round(tflops, 1),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP8_PEAK_TFLOPS, 4), "flops_per_launch": flops,
+                     "traffic": None},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +203,8 @@ def main():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--indexer-only", action="store_true",
+                    help="time only sga_index_scores (reported in TFLOP/s against the FP8 MFMA peak)")
     args = ap.parse_args()
     if args.gpus != 1:
         log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -176,6 +226,8 @@ def main():
         f"({case.num_kv_rows} cached rows, {case.num_q} queries)")
     prob = sga.Problem.from_case(case)
     T, H, Dc = case.num_q, case.heads, case.d_latent
+    if args.indexer_only:
+        return indexer_only(args, case, prob, sga, torch)
     out = torch.empty((T, H, Dc), dtype=sga.out_torch_dtype(prob.c.out_dtype), device=dev)
     ws = sga.workspace(prob, sga.SGA_OP_LAYER, device=dev)
     # independent cache copies, rotated per step (defeats the 256 MB MALL)

@@ -37,6 +37,20 @@ __device__ __forceinline__ void hist_zero(uint32_t *lds_hist) {
   __syncthreads();
 }
 
+// Query rows are grouped in runs of kPfGroup for the prefill kernel. A group is
+// "shared" when all of its rows name the same sequence; the prefill kernel
+// scores exactly those groups and the per-query kernel skips them.
+constexpr int kPfGroup = 16;
+
+__device__ __forceinline__ bool group_is_shared(const SeqMeta &m, int T, int g) {
+  const int t0 = g * kPfGroup;
+  const int t1 = min(T, t0 + kPfGroup);
+  const int32_t b = m.q_seq[t0];
+  bool same = true;
+  for (int t = t0 + 1; t < t1; ++t) same = same && (m.q_seq[t] == b);
+  return same;
+}
+
 // --------------------------------------------------------------------------
 // fp32 path
 // --------------------------------------------------------------------------
@@ -154,7 +168,8 @@ __device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t
 }
 
 template <bool kHist>
-__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int k, int iters,
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int k, int iters,
+                                                              int skip_shared,
                                                               const uint8_t *__restrict__ q_idx,
                                                               const float *__restrict__ w,
                                                               const uint8_t *__restrict__ k_idx,
@@ -170,6 +185,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int k, 
   const int wave_keys = iters * kIdxTileKeys;
   const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
   if (chunk0 >= n) return;
+  if (skip_shared && group_is_shared(m, T, t / kPfGroup)) return;  // scored by k_index_fp8_pf
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kg = lane >> 4, c16 = lane & 15;
@@ -266,6 +282,133 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int k, 
   }
 }
 
+// --------------------------------------------------------------------------
+// Prefill: many queries of one sequence share every key tile.
+//
+// A workgroup owns a group of 16 query rows of one sequence (8 waves x 2
+// queries; each wave keeps its two 64 x 128 index matrices in VGPRs) and a
+// range of 8192 keys. Key tiles of 64 keys are copied once into LDS with
+// LDS-DMA (one 16-byte piece per thread, double-buffered) and reused by all 16
+// queries, so the pass is bound by MFMA and the ReLU/weight epilogue instead of
+// by HBM. Keys past a query's own position are neither scored nor stored.
+// --------------------------------------------------------------------------
+constexpr int kPfWaves = kPfGroup / 2;
+constexpr int kPfChunk = 8192;  // keys per workgroup
+
+__global__ __launch_bounds__(kPfWaves * 64) void k_index_fp8_pf(SeqMeta m, int T,
+                                                                const uint8_t *__restrict__ q_idx,
+                                                                const float *__restrict__ w,
+                                                                const uint8_t *__restrict__ k_idx,
+                                                                float *__restrict__ scores,
+                                                                int64_t stride) {
+  // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
+  // explicit waits below instead of draining every DMA before each read
+  extern __shared__ __attribute__((aligned(16))) unsigned char tiles[];
+  __shared__ int s_nmax;
+  const int g = blockIdx.y;
+  if (!group_is_shared(m, T, g)) return;  // left to the per-query kernel
+  const int t0 = g * kPfGroup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, c16 = lane & 15;
+  int64_t start;
+  if (tid == 0) {
+    int mx = 0;
+    for (int t = t0; t < min(T, t0 + kPfGroup); ++t) mx = max(mx, query_candidates(m, t, &start));
+    s_nmax = mx;
+  }
+  __syncthreads();
+  const int nmax = s_nmax;
+  const int c0 = blockIdx.x * kPfChunk;
+  if (c0 >= nmax) return;
+  const int ntiles = (min(nmax, c0 + kPfChunk) - c0 + kIdxTileKeys - 1) / kIdxTileKeys;
+
+  // the wave's two queries (rows past T get n = 0)
+  int nq[2];
+  v8i a[2][4];
+  float wv[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = t0 + 2 * wave + j;
+    nq[j] = t < T ? query_candidates(m, t, &start) : 0;
+    const int tt = t < T ? t : t0;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const v4i *src = (const v4i *)(q_idx + ((size_t)tt * 64 + ht * 16 + c16) * 128 + kg * 32);
+      const v4i lo = src[0], hi = src[1];
+      a[j][ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[j][ht * 4 + r] = w[(size_t)tt * 64 + ht * 16 + 4 * kg + r];
+    }
+  }
+  query_candidates(m, t0, &start);  // the group's sequence start
+  // DMA piece of this thread: tile row r = tid / 8, swizzled 16-byte piece
+  const int r_dma = tid >> 3;
+  const int off_dma = r_dma * 128 + (((tid & 7) ^ key_swz(r_dma)) << 4);
+  auto issue = [&](int i) {
+    int key = c0 + i * kIdxTileKeys + r_dma;
+    key = key < nmax ? key : nmax - 1;
+    const uint8_t *src = k_idx + (start + key) * 128 + (off_dma & 127);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(tiles + (i & 1) * kIdxTileBytes + wave * 1024),
+                                     16, 0, 0);
+  };
+  wait_vmcnt<0>();
+  issue(0);
+  if (ntiles > 1) issue(1);
+  for (int i = 0; i < ntiles; ++i) {
+    // only DMA(i+1) may still be in flight; older score stores drain as well
+    if (i + 1 < ntiles) wait_vmcnt<1>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const unsigned char *tb = tiles + (i & 1) * kIdxTileBytes;
+    const int kbase = c0 + i * kIdxTileKeys;
+    v8i b[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int r = kt * 16 + c16;
+      const unsigned char *rp = tb + r * 128 + ((2 * kg) ^ key_swz(r)) * 16;
+      const v4i lo = *(const v4i *)rp, hi = *(const v4i *)(rp + 16);
+      b[kt] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (kbase >= nq[j]) continue;  // the whole tile is past this query (wave-uniform)
+      float part[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const v4f d = mfma_fp8(a[j][ht], b[kt], (v4f){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) acc = fmaf(fmaxf(d[rr], 0.0f), wv[j][ht * 4 + rr], acc);
+        }
+        part[kt] = acc;
+      }
+      const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0;
+      float k0 = b5 ? part[2] : part[0];
+      float k1 = b5 ? part[3] : part[1];
+      const float s0 = b5 ? part[0] : part[2];
+      const float s1 = b5 ? part[1] : part[3];
+      k0 += __shfl_xor(s0, 32, 64);
+      k1 += __shfl_xor(s1, 32, 64);
+      float keep = b4 ? k1 : k0;
+      const float send = b4 ? k0 : k1;
+      keep += __shfl_xor(send, 16, 64);
+      keep += 0.0f;  // -0 -> +0
+      const int s = kbase + lane;
+      if (s < nq[j]) scores[(size_t)(t0 + 2 * wave + j) * stride + s] = keep;
+    }
+    // every wave is done with this buffer before it is refilled
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (i + 2 < ntiles) issue(i + 2);
+  }
+}
+
 }  // namespace
 
 int index_fp8_iters(int T, int max_kv_len) {
@@ -305,15 +448,30 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     (void)hipGetLastError();
     attr = true;
   }
+  // many query rows per sequence: score shared 16-row groups with the
+  // query-tiled kernel, the rest with the per-query kernel
+  const bool prefill = T >= 4 * kPfGroup && T >= 4 * m.num_seqs;
   const int iters = index_fp8_iters(T, m.max_kv_len);
   const int per_wg = kIdxWaves * iters * kIdxTileKeys;
   dim3 grid((m.max_kv_len + per_wg - 1) / per_wg, T);
   TopkWs none{};
+  if (prefill) {
+    dim3 pgrid((m.max_kv_len + kPfChunk - 1) / kPfChunk, (T + kPfGroup - 1) / kPfGroup);
+    hipLaunchKernelGGL(k_index_fp8_pf, pgrid, dim3(kPfWaves * 64), 2 * kIdxTileBytes, s, m, T,
+                       q_idx, w, k_idx, scores, stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
+                       1, q_idx, w, k_idx, scores, stride, none);
+    e = hipGetLastError();
+    if (e != hipSuccess || !sel) return e;
+    return launch_topk_hist0(m, T, scores, stride, *sel, s);
+  }
   if (sel)
-    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, k, iters,
+    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters, 0,
                        q_idx, w, k_idx, scores, stride, *sel);
   else
-    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, k, iters,
+    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters, 0,
                        q_idx, w, k_idx, scores, stride, none);
   return hipGetLastError();
 }

@@ -111,3 +111,25 @@ def test_topk_small_k_and_continuous_scores():
     rows = [torch.randn(n, generator=g).tolist() for n in (3, 100, 5000, 70000)]
     for k in (1, 7, 64):
         _check_topk(rows, k, f"k={k}")
+
+
+def test_index_scores_prefill_groups_mixed():
+    # 96 query rows over three sequences: 16-row groups that lie inside one
+    # sequence go through the query-tiled prefill kernel, the two groups that
+    # straddle a sequence boundary through the per-query kernel
+    lens = [9000, 20000, 3000]
+    qs = [(0, 8999 - i) for i in range(40)] + [(1, 19999 - 7 * i) for i in range(40)] + \
+         [(2, 2999 - i) for i in range(16)]
+    case = make_custom(lens, qs, dims=FULL_DIMS, precision="bf16", seed=41, device="cuda")
+    say("case prefill index scores, mixed groups")
+    _check_scores(case)
+
+
+def test_index_scores_prefill_single_sequence_chunk():
+    # a prefill chunk: 200 consecutive positions at the end of a 40,000-token
+    # sequence (a ragged last group and a ragged causal edge)
+    n = 40000
+    case = make_custom([n], [(0, n - 200 + i) for i in range(200)], dims=FULL_DIMS,
+                       precision="bf16", seed=42, device="cuda")
+    say("case prefill index scores, one sequence")
+    _check_scores(case, [0, 1, 17, 100, 150, 199])
