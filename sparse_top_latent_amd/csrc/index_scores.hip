@@ -6,17 +6,21 @@
 // "Sparse Gated Attention (SGA)" (the indexer scores and ranks key-value
 // candidates). The weighted-ReLU form is the reading this library implements.
 //
-// Two kernels:
+// Three kernels:
 //  * k_index_f32: generic fp32 path, one thread per (query, key).
-//  * k_index_fp8: MI355X path for 64 index heads x 128 dims in E4M3FN. Each
-//    wave keeps the query's 64 x 128 index matrix in registers as four 16 x 128
-//    MFMA A tiles and streams its own range of keys through LDS (LDS-DMA, two
-//    8 KiB tiles in flight). One 16x16x128 FP8 MFMA per (head tile, 16-key
-//    tile) gives 16 heads x 16 keys; the ReLU and the weighted head sum run on
-//    the accumulators, and a 2-step cross-lane reduction leaves one finished
-//    score per lane, stored coalesced.
-// Both can also build the level-0 histogram (top 12 bits of the score key) the
-// top-k select starts from, so the layer never re-reads the scores for it.
+//  * k_index_fp8: MI355X path for 64 index heads x 128 dims in E4M3FN, one
+//    query per workgroup row of the grid (decode). Each wave keeps the
+//    query's 64 x 128 index matrix in registers as four 16 x 128 MFMA A tiles
+//    and streams its own range of keys through LDS (LDS-DMA, two 8 KiB tiles
+//    in flight). One 16x16x128 FP8 MFMA per (head tile, 16-key tile) gives 16
+//    heads x 16 keys; the ReLU and the weighted head sum run on the
+//    accumulators, and lane-swap additions leave one finished score per lane,
+//    stored coalesced.
+//  * k_index_fp8_pf: the same arithmetic for runs of query rows of one
+//    sequence (prefill): the workgroup's waves share each LDS key tile.
+// k_index_f32 and k_index_fp8 can also build the level-0 histogram (top 12
+// bits of the score key) the top-k select starts from, so the layer never
+// re-reads the scores for it.
 
 #include "kernels.h"
 
@@ -40,7 +44,7 @@ __device__ __forceinline__ void hist_zero(uint32_t *lds_hist) {
 // Query rows are grouped in runs of kPfGroup for the prefill kernel. A group is
 // "shared" when all of its rows name the same sequence; the prefill kernel
 // scores exactly those groups and the per-query kernel skips them.
-constexpr int kPfGroup = 16;
+constexpr int kPfGroup = 8;
 
 __device__ __forceinline__ bool group_is_shared(const SeqMeta &m, int T, int g) {
   const int t0 = g * kPfGroup;
@@ -133,27 +137,97 @@ __device__ __forceinline__ void lds_add_u32(uint32_t *p, uint32_t v) {
   asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-// segment swizzle of key row r: 16-byte piece q lives at piece q ^ swz(r)
-__device__ __forceinline__ int key_swz(int r) { return ((r >> 1) & 3) << 1; }
+// Piece swizzle of key row r in LDS: the 16-byte piece q of the row is
+// stored at piece q ^ key_swz(r). A ds_read_b128 of the B operand serves 16
+// lanes at a time, 16 consecutive rows with one piece each; rows r and r + 1
+// sit half the banks apart, and (r >> 1) & 7 spreads each row pair over all
+// eight piece positions, so every 16-lane group hits 64 distinct banks.
+__device__ __forceinline__ int key_swz(int r) { return (r >> 1) & 7; }
 
-// Byte offset, inside a 64-key tile, of the global 16-byte piece that lane
-// `lane` copies with DMA issue i (add i * 1024): piece p = 64 i + lane of the
-// LDS tile holds key row p / 8, global piece (p % 8) ^ key_swz(row); the
-// swizzle only depends on the lane because rows advance by 8 per issue.
-__device__ __forceinline__ int key_dma_offset(int lane) {
-  const int r = lane >> 3;
-  return r * 128 + (((lane & 7) ^ key_swz(r)) << 4);
+// B operand of key tile kt (keys 16 kt .. 16 kt + 15 of a 64-key LDS tile):
+// key 16 kt + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row.
+__device__ __forceinline__ v8i load_key_operand(const unsigned char *tb, int kt, int kg, int c16) {
+  const int r = kt * 16 + c16;
+  const unsigned char *row = tb + r * 128;
+  const v4i lo = *(const v4i *)(row + (((2 * kg) ^ key_swz(r)) << 4));
+  const v4i hi = *(const v4i *)(row + (((2 * kg + 1) ^ key_swz(r)) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// Weighted-ReLU head sums of kQ queries over one 64-key LDS tile: part[j][kt]
+// (lane l) is the sum, over the 16 heads this lane's accumulator rows cover,
+// of w[h] * max(0, qI[h] . k) for query j and key 16 kt + l % 16.
+//
+// On gfx950 MFMA and VALU time add up on a SIMD (measured: they do not
+// overlap), so the epilogue (a max and an FMA per accumulator element) is
+// kept as short as it can be; each sum is split over two accumulators so
+// that consecutive FMAs do not wait on each other. The B operand is read
+// per key tile, which also bounds how many MFMA results are live at once.
+template <int kQ>
+__device__ __forceinline__ void score_tiles(const v8i (&a)[kQ][4], const unsigned char *tb, int kg,
+                                            int c16, const float (&wv)[kQ][16],
+                                            float (&part)[kQ][4]) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const v8i b = load_key_operand(tb, kt, kg, c16);
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      float ev = 0.0f, od = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const v4f x = mfma_fp8(a[j][ht], b, zero);
+        const float *wr = &wv[j][ht * 4];
+        ev = fmaf(fmaxf(x[0], 0.0f), wr[0], ev);
+        od = fmaf(fmaxf(x[1], 0.0f), wr[1], od);
+        ev = fmaf(fmaxf(x[2], 0.0f), wr[2], ev);
+        od = fmaf(fmaxf(x[3], 0.0f), wr[3], od);
+      }
+      part[j][kt] = ev + od;
+    }
+  }
+}
+
+__device__ __forceinline__ float add_swapped(float x, float y, bool wide) {
+  // lanes of x and y exchanged across the two 32-lane halves (wide) or across
+  // neighbouring 16-lane rows; the two results summed
+  const auto r = wide ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                      : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reduce-scatter of part[0..3] over the lanes l, l^16, l^32, l^48 that hold
+// partial sums of the same keys: lane l returns the score of key l of the
+// tile (-0 becomes +0). Lane-swap instructions of gfx950 do the exchange:
+// across the halves, lane l < 32 gets part[0] (part[1]) of lanes l and l + 32
+// and lane l >= 32 part[2] (part[3]) of lanes l - 32 and l; then across
+// 16-lane rows, even rows keep the first sum and odd rows the second.
+__device__ __forceinline__ float tile_scores(const float (&part)[4]) {
+  const float k0 = add_swapped(part[0], part[2], true);
+  const float k1 = add_swapped(part[1], part[3], true);
+  return add_swapped(k0, k1, false) + 0.0f;
+}
+
+
+// Global byte offset of the 16-byte piece that lane `lane` copies with DMA
+// issue i, relative to row 8 i of the tile: piece 64 i + lane of the LDS tile
+// holds key row r = 8 i + lane / 8 and global piece (lane % 8) ^ key_swz(r);
+// key_swz(r) only depends on the lane and on the parity of i.
+__device__ __forceinline__ int key_dma_offset(int lane, int i) {
+  const int r = 8 * i + (lane >> 3);
+  return (lane >> 3) * 128 + (((lane & 7) ^ key_swz(r)) << 4);
 }
 
 // Issue the DMA of one 64-key tile (keys base.., clamped to n-1) into `buf`.
 __device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t *__restrict__ k_idx,
                                                int64_t start, int n, int base, int lane,
-                                               int lane_off) {
+                                               const int (&lane_off)[2]) {
   if (base + kIdxTileKeys <= n) {
-    const uint8_t *src = k_idx + (start + base) * 128 + lane_off;
+    const uint8_t *src = k_idx + (start + base) * 128;
 #pragma unroll
     for (int i = 0; i < kIdxDmaPerTile; ++i)
-      __builtin_amdgcn_global_load_lds(src + i * 1024, (lds_void *)(buf + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane_off[i & 1], (lds_void *)(buf + i * 1024),
+                                       16, 0, 0);
   } else {
     // sequence tail: rows past the end repeat the last key (their scores are dropped)
 #pragma unroll
@@ -161,7 +235,7 @@ __device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t
       const int r = i * 8 + (lane >> 3);
       int key = base + r;
       key = key < n ? key : n - 1;
-      const uint8_t *src = k_idx + (start + key) * 128 + (lane_off & 127);
+      const uint8_t *src = k_idx + (start + key) * 128 + (lane_off[i & 1] & 127);
       __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, 0);
     }
   }
@@ -191,16 +265,16 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int kg = lane >> 4, c16 = lane & 15;
 
   // A tiles: head (ht*16 + c16), bytes [32*kg, 32*kg+32) of its 128-byte row
-  v8i a[4];
-  float wv[16];
+  v8i a[1][4];
+  float wv[1][16];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
     const v4i lo = src[0], hi = src[1];
-    a[ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    a[0][ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     // accumulator row r of this lane is head ht*16 + 4*kg + r
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
+    for (int r = 0; r < 4; ++r) wv[0][ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
   }
   if (kHist) {
     for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
@@ -210,7 +284,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int wbase = chunk0 + wave * wave_keys;
   const int nit = wbase < n ? min(iters, (n - wbase + kIdxTileKeys - 1) / kIdxTileKeys) : 0;
   unsigned char *mybuf = smem + (size_t)wave * kIdxBufs * kIdxTileBytes;
-  const int lane_off = key_dma_offset(lane);
+  const int lane_off[2] = {key_dma_offset(lane, 0), key_dma_offset(lane, 1)};
   // the q/w loads above must have landed before the DMA counting starts
   wait_vmcnt<0>();
   if (nit > 0) issue_key_tile(mybuf, k_idx, start, n, wbase, lane, lane_off);
@@ -227,37 +301,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
     else wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     const unsigned char *tb = mybuf + (it & 1) * kIdxTileBytes;
-    float part[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int r = kt * 16 + c16;
-      const unsigned char *rp = tb + r * 128 + ((2 * kg) ^ key_swz(r)) * 16;
-      const v4i lo = *(const v4i *)rp;
-      const v4i hi = *(const v4i *)(rp + 16);
-      const v8i b = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      float acc = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const v4f d = mfma_fp8(a[ht], b, (v4f){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc = fmaf(fmaxf(d[rr], 0.0f), wv[ht * 4 + rr], acc);
-      }
-      part[kt] = acc;
-    }
-    // lanes l, l^16, l^32, l^48 hold partial sums of the same 4 keys (one per kt);
-    // reduce-scatter so that lane l finishes key base + l.
-    const bool b5 = (lane & 32) != 0;
-    const bool b4 = (lane & 16) != 0;
-    float k0 = b5 ? part[2] : part[0];
-    float k1 = b5 ? part[3] : part[1];
-    const float s0 = b5 ? part[0] : part[2];
-    const float s1 = b5 ? part[1] : part[3];
-    k0 += __shfl_xor(s0, 32, 64);
-    k1 += __shfl_xor(s1, 32, 64);
-    float keep = b4 ? k1 : k0;
-    const float send = b4 ? k0 : k1;
-    keep += __shfl_xor(send, 16, 64);
-    keep += 0.0f;  // -0 -> +0
+    float part[1][4];
+    score_tiles<1>(a, tb, kg, c16, wv, part);
+    const float keep = tile_scores(part[0]);
     const int s = wbase + it * kIdxTileKeys + lane;
     // the tile buffer is free once this iteration's LDS reads completed
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
@@ -285,22 +331,31 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
 // --------------------------------------------------------------------------
 // Prefill: many queries of one sequence share every key tile.
 //
-// A workgroup owns a group of 16 query rows of one sequence (8 waves x 2
-// queries; each wave keeps its two 64 x 128 index matrices in VGPRs) and a
+// A workgroup owns a group of 8 query rows of one sequence (8 / kQpw waves of
+// kQpw queries; each wave keeps its 64 x 128 index matrices in VGPRs) and a
 // range of 8192 keys. Key tiles of 64 keys are copied once into LDS with
-// LDS-DMA (one 16-byte piece per thread, double-buffered) and reused by all 16
-// queries, so the pass is bound by MFMA and the ReLU/weight epilogue instead of
-// by HBM. Keys past a query's own position are neither scored nor stored.
+// LDS-DMA and reused by all 16 queries, so the pass is bound by the MFMAs and
+// the ReLU/weight epilogue instead of by HBM. Three tile buffers let one
+// barrier per tile both publish tile i and free the buffer that tile i + 2
+// overwrites. Keys past a query's own position are neither scored nor stored.
 // --------------------------------------------------------------------------
-constexpr int kPfWaves = kPfGroup / 2;
 constexpr int kPfChunk = 8192;  // keys per workgroup
+constexpr int kPfQpw = 1;       // queries per wave
+constexpr int kPfBufs = 3;
 
-__global__ __launch_bounds__(kPfWaves * 64) void k_index_fp8_pf(SeqMeta m, int T,
+// kQpw queries per wave, kPfGroup / kQpw waves per workgroup. MFMA and VALU
+// time add up on a SIMD, so latency is hidden by wave count: the register
+// budget is held to 6 waves per SIMD (3 workgroups per CU).
+template <int kQpw>
+__global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta m, int T,
                                                                 const uint8_t *__restrict__ q_idx,
                                                                 const float *__restrict__ w,
                                                                 const uint8_t *__restrict__ k_idx,
                                                                 float *__restrict__ scores,
                                                                 int64_t stride) {
+  constexpr int kThreads = kPfGroup / kQpw * 64;
+  static_assert(512 % kThreads == 0 || kThreads % 512 == 0, "a tile is 512 16-byte pieces");
+  constexpr int kDmaPer = kThreads >= 512 ? 1 : 512 / kThreads;  // DMA issues per thread per tile
   // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
   // explicit waits below instead of draining every DMA before each read
   extern __shared__ __attribute__((aligned(16))) unsigned char tiles[];
@@ -322,13 +377,13 @@ __global__ __launch_bounds__(kPfWaves * 64) void k_index_fp8_pf(SeqMeta m, int T
   if (c0 >= nmax) return;
   const int ntiles = (min(nmax, c0 + kPfChunk) - c0 + kIdxTileKeys - 1) / kIdxTileKeys;
 
-  // the wave's two queries (rows past T get n = 0)
-  int nq[2];
-  v8i a[2][4];
-  float wv[2][16];
+  // the wave's queries (rows past T get n = 0)
+  int nq[kQpw];
+  v8i a[kQpw][4];
+  float wv[kQpw][16];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = t0 + 2 * wave + j;
+  for (int j = 0; j < kQpw; ++j) {
+    const int t = t0 + kQpw * wave + j;
     nq[j] = t < T ? query_candidates(m, t, &start) : 0;
     const int tt = t < T ? t : t0;
 #pragma unroll
@@ -341,71 +396,47 @@ __global__ __launch_bounds__(kPfWaves * 64) void k_index_fp8_pf(SeqMeta m, int T
     }
   }
   query_candidates(m, t0, &start);  // the group's sequence start
-  // DMA piece of this thread: tile row r = tid / 8, swizzled 16-byte piece
-  const int r_dma = tid >> 3;
-  const int off_dma = r_dma * 128 + (((tid & 7) ^ key_swz(r_dma)) << 4);
+  // DMA pieces of this thread: piece p = u * kThreads + tid of the 8 KiB tile
+  // holds tile row p / 8 and its swizzled 16-byte piece
   auto issue = [&](int i) {
-    int key = c0 + i * kIdxTileKeys + r_dma;
-    key = key < nmax ? key : nmax - 1;
-    const uint8_t *src = k_idx + (start + key) * 128 + (off_dma & 127);
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(tiles + (i & 1) * kIdxTileBytes + wave * 1024),
-                                     16, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kDmaPer; ++u) {
+      const int p = u * kThreads + tid;
+      if (kThreads > 512 && p >= 512) break;  // wave-uniform: whole waves past the tile
+      const int r = p >> 3;
+      int key = c0 + i * kIdxTileKeys + r;
+      key = key < nmax ? key : nmax - 1;
+      const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
+      __builtin_amdgcn_global_load_lds(
+          src, (lds_void *)(tiles + (i % kPfBufs) * kIdxTileBytes + (u * kThreads + wave * 64) * 16),
+          16, 0, 0);
+    }
   };
   wait_vmcnt<0>();
   issue(0);
   if (ntiles > 1) issue(1);
   for (int i = 0; i < ntiles; ++i) {
-    // only DMA(i+1) may still be in flight; older score stores drain as well
-    if (i + 1 < ntiles) wait_vmcnt<1>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const unsigned char *tb = tiles + (i & 1) * kIdxTileBytes;
-    const int kbase = c0 + i * kIdxTileKeys;
-    v8i b[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int r = kt * 16 + c16;
-      const unsigned char *rp = tb + r * 128 + ((2 * kg) ^ key_swz(r)) * 16;
-      const v4i lo = *(const v4i *)rp, hi = *(const v4i *)(rp + 16);
-      b[kt] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (kbase >= nq[j]) continue;  // the whole tile is past this query (wave-uniform)
-      float part[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int ht = 0; ht < 4; ++ht) {
-          const v4f d = mfma_fp8(a[j][ht], b[kt], (v4f){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) acc = fmaf(fmaxf(d[rr], 0.0f), wv[j][ht * 4 + rr], acc);
-        }
-        part[kt] = acc;
-      }
-      const bool b5 = (lane & 32) != 0, b4 = (lane & 16) != 0;
-      float k0 = b5 ? part[2] : part[0];
-      float k1 = b5 ? part[3] : part[1];
-      const float s0 = b5 ? part[0] : part[2];
-      const float s1 = b5 ? part[1] : part[3];
-      k0 += __shfl_xor(s0, 32, 64);
-      k1 += __shfl_xor(s1, 32, 64);
-      float keep = b4 ? k1 : k0;
-      const float send = b4 ? k0 : k1;
-      keep += __shfl_xor(send, 16, 64);
-      keep += 0.0f;  // -0 -> +0
-      const int s = kbase + lane;
-      if (s < nq[j]) scores[(size_t)(t0 + 2 * wave + j) * stride + s] = keep;
-    }
-    // every wave is done with this buffer before it is refilled
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    // Tile i has landed once at most the kDmaPer copies of tile i + 1 (issued
+    // after it) are outstanding; score stores issued later only make this
+    // wait longer. The barrier then publishes every wave's part of tile i and
+    // certifies that all LDS reads of tile i - 1 are done, so the copy of
+    // tile i + 2 may overwrite that buffer.
+    if (i + 1 < ntiles) wait_vmcnt<kDmaPer>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i + 2 < ntiles) issue(i + 2);
+    const unsigned char *tb = tiles + (i % kPfBufs) * kIdxTileBytes;
+    const int kbase = c0 + i * kIdxTileKeys;
+    float part[kQpw][4];
+    score_tiles<kQpw>(a, tb, kg, c16, wv, part);
+    const int s = kbase + lane;
+#pragma unroll
+    for (int j = 0; j < kQpw; ++j) {
+      const float keep = tile_scores(part[j]);
+      if (s < nq[j]) scores[(size_t)(t0 + kQpw * wave + j) * stride + s] = keep;
+    }
   }
 }
 
@@ -457,8 +488,8 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   TopkWs none{};
   if (prefill) {
     dim3 pgrid((m.max_kv_len + kPfChunk - 1) / kPfChunk, (T + kPfGroup - 1) / kPfGroup);
-    hipLaunchKernelGGL(k_index_fp8_pf, pgrid, dim3(kPfWaves * 64), 2 * kIdxTileBytes, s, m, T,
-                       q_idx, w, k_idx, scores, stride);
+    hipLaunchKernelGGL(k_index_fp8_pf<kPfQpw>, pgrid, dim3(kPfGroup / kPfQpw * 64), kPfBufs * kIdxTileBytes,
+                       s, m, T, q_idx, w, k_idx, scores, stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,

@@ -114,12 +114,13 @@ def test_topk_small_k_and_continuous_scores():
 
 
 def test_index_scores_prefill_groups_mixed():
-    # 96 query rows over three sequences: 16-row groups that lie inside one
+    # 96 query rows over three sequences: 8-row groups that lie inside one
     # sequence go through the query-tiled prefill kernel, the two groups that
-    # straddle a sequence boundary through the per-query kernel
+    # straddle a sequence boundary (rows 32-39 and 80-87) through the
+    # per-query kernel
     lens = [9000, 20000, 3000]
-    qs = [(0, 8999 - i) for i in range(40)] + [(1, 19999 - 7 * i) for i in range(40)] + \
-         [(2, 2999 - i) for i in range(16)]
+    qs = [(0, 8999 - i) for i in range(37)] + [(1, 19999 - 7 * i) for i in range(45)] + \
+         [(2, 2999 - i) for i in range(14)]
     case = make_custom(lens, qs, dims=FULL_DIMS, precision="bf16", seed=41, device="cuda")
     say("case prefill index scores, mixed groups")
     _check_scores(case)
