@@ -48,7 +48,8 @@ COMMON = [
 PER_FILE = {
     # the indexer's ReLU runs on MFMA accumulators that are never NaN for finite
     # inputs; without this every max is preceded by a NaN-quieting max
-    "index_scores.hip": ["-fno-honor-nans"],
+    "index_scores.hip": ["-fno-honor-nans", "-Wno-nan-infinity-disabled"],
+    "index_prefill.hip": ["-fno-honor-nans", "-Wno-nan-infinity-disabled"],
 }
 
 

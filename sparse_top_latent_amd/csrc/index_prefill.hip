@@ -1,0 +1,141 @@
+// Indexer score pass for runs of query rows of one sequence (prefill):
+// I[t,s] = sum_h w[t,h] * max(0, qI[t,h,:] . kI[s,:]) for s < n_t, with every
+// LDS key tile shared by a group of query rows.
+//
+// Source: "A.X-K2: a sparse-attention upgrade that costs nothing, trained
+// natively in FP8", section "Sparse Gated Attention" (the indexer scores every
+// cached key for each query); "A.X-K2" model card, section "Sparse Gated
+// Attention (SGA)". The weighted-ReLU form is the reading this library
+// implements (see index_scores.hip).
+
+#include "index_common.h"
+
+namespace sga {
+
+namespace {
+
+// --------------------------------------------------------------------------
+// Prefill: many queries of one sequence share every key tile.
+//
+// A workgroup owns a group of 8 query rows of one sequence (8 / kQpw waves of
+// kQpw queries; each wave keeps its 64 x 128 index matrices in VGPRs) and a
+// range of 8192 keys. Key tiles of 64 keys are copied once into LDS with
+// LDS-DMA and reused by all 8 queries, so the pass is bound by the MFMAs and
+// the ReLU/weight epilogue instead of by HBM. Three tile buffers let one
+// barrier per tile both publish tile i and free the buffer that tile i + 2
+// overwrites. Keys past a query's own position are neither scored nor stored.
+// --------------------------------------------------------------------------
+constexpr int kPfChunk = 8192;  // keys per workgroup
+constexpr int kPfQpw = 1;       // queries per wave
+constexpr int kPfBufs = 3;
+
+// kQpw queries per wave, kPfGroup / kQpw waves per workgroup. MFMA and VALU
+// time add up on a SIMD, so latency is hidden by wave count: the register
+// budget is held to 6 waves per SIMD (3 workgroups per CU).
+template <int kQpw>
+__global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta m, int T,
+                                                                const uint8_t *__restrict__ q_idx,
+                                                                const float *__restrict__ w,
+                                                                const uint8_t *__restrict__ k_idx,
+                                                                float *__restrict__ scores,
+                                                                int64_t stride) {
+  constexpr int kThreads = kPfGroup / kQpw * 64;
+  static_assert(512 % kThreads == 0 || kThreads % 512 == 0, "a tile is 512 16-byte pieces");
+  constexpr int kDmaPer = kThreads >= 512 ? 1 : 512 / kThreads;  // DMA issues per thread per tile
+  // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
+  // explicit waits below instead of draining every DMA before each read
+  extern __shared__ __attribute__((aligned(16))) unsigned char tiles[];
+  __shared__ int s_nmax;
+  const int g = blockIdx.y;
+  if (!group_is_shared(m, T, g)) return;  // left to the per-query kernel
+  const int t0 = g * kPfGroup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, c16 = lane & 15;
+  int64_t start;
+  if (tid == 0) {
+    int mx = 0;
+    for (int t = t0; t < min(T, t0 + kPfGroup); ++t) mx = max(mx, query_candidates(m, t, &start));
+    s_nmax = mx;
+  }
+  __syncthreads();
+  const int nmax = s_nmax;
+  const int c0 = blockIdx.x * kPfChunk;
+  if (c0 >= nmax) return;
+  const int ntiles = (min(nmax, c0 + kPfChunk) - c0 + kIdxTileKeys - 1) / kIdxTileKeys;
+
+  // the wave's queries (rows past T get n = 0)
+  int nq[kQpw];
+  v8i a[kQpw][4];
+  float wv[kQpw][16];
+#pragma unroll
+  for (int j = 0; j < kQpw; ++j) {
+    const int t = t0 + kQpw * wave + j;
+    nq[j] = t < T ? query_candidates(m, t, &start) : 0;
+    const int tt = t < T ? t : t0;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const v4i *src = (const v4i *)(q_idx + ((size_t)tt * 64 + ht * 16 + c16) * 128 + kg * 32);
+      const v4i lo = src[0], hi = src[1];
+      a[j][ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[j][ht * 4 + r] = w[(size_t)tt * 64 + ht * 16 + 4 * kg + r];
+    }
+  }
+  query_candidates(m, t0, &start);  // the group's sequence start
+  // DMA pieces of this thread: piece p = u * kThreads + tid of the 8 KiB tile
+  // holds tile row p / 8 and its swizzled 16-byte piece
+  auto issue = [&](int i) {
+#pragma unroll
+    for (int u = 0; u < kDmaPer; ++u) {
+      const int p = u * kThreads + tid;
+      if (kThreads > 512 && p >= 512) break;  // wave-uniform: whole waves past the tile
+      const int r = p >> 3;
+      int key = c0 + i * kIdxTileKeys + r;
+      key = key < nmax ? key : nmax - 1;
+      const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
+      __builtin_amdgcn_global_load_lds(
+          src, (lds_void *)(tiles + (i % kPfBufs) * kIdxTileBytes + (u * kThreads + wave * 64) * 16),
+          16, 0, 0);
+    }
+  };
+  wait_vmcnt<0>();
+  issue(0);
+  if (ntiles > 1) issue(1);
+  for (int i = 0; i < ntiles; ++i) {
+    // Tile i has landed once at most the kDmaPer copies of tile i + 1 (issued
+    // after it) are outstanding; score stores issued later only make this
+    // wait longer. The barrier then publishes every wave's part of tile i and
+    // certifies that all LDS reads of tile i - 1 are done, so the copy of
+    // tile i + 2 may overwrite that buffer.
+    if (i + 1 < ntiles) wait_vmcnt<kDmaPer>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (i + 2 < ntiles) issue(i + 2);
+    const unsigned char *tb = tiles + (i % kPfBufs) * kIdxTileBytes;
+    const int kbase = c0 + i * kIdxTileKeys;
+    float part[kQpw][4];
+    score_tiles<kQpw>(a, tb, kg, c16, wv, part);
+    const int s = kbase + lane;
+#pragma unroll
+    for (int j = 0; j < kQpw; ++j) {
+      const float keep = tile_scores(part[j]);
+      if (s < nq[j]) scores[(size_t)(t0 + kQpw * wave + j) * stride + s] = keep;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
+                                    const uint8_t *k_idx, float *scores, int64_t stride,
+                                    hipStream_t s) {
+  dim3 grid((m.max_kv_len + kPfChunk - 1) / kPfChunk, (T + kPfGroup - 1) / kPfGroup);
+  hipLaunchKernelGGL(k_index_fp8_pf<kPfQpw>, grid, dim3(kPfGroup / kPfQpw * 64),
+                     kPfBufs * kIdxTileBytes, s, m, T, q_idx, w, k_idx, scores, stride);
+  return hipGetLastError();
+}
+
+
+}  // namespace sga

@@ -18,6 +18,11 @@ hipError_t launch_index_f32(const SeqMeta &m, int T, int k, int HI, int DI, cons
 hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx, const float *w,
                             const uint8_t *k_idx, float *scores, int64_t stride, const TopkWs *sel,
                             hipStream_t s);
+// Query-tiled FP8 scores for the query-row groups whose rows all name one
+// sequence (other groups are left untouched); used by launch_index_fp8.
+hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
+                                    const uint8_t *k_idx, float *scores, int64_t stride,
+                                    hipStream_t s);
 
 // --- top-k select -----------------------------------------------------------
 struct TopkWs {
