@@ -12,19 +12,9 @@ namespace {
 constexpr int kIdxTileKeys = 64;  // keys per LDS tile
 constexpr int kIdxTileBytes = kIdxTileKeys * 128;
 
-// Query rows are grouped in runs of kPfGroup for the prefill kernel. A group is
-// "shared" when all of its rows name the same sequence; the prefill kernel
-// scores exactly those groups and the per-query kernel skips them.
+// Query rows are grouped in runs of kPfGroup for the prefill kernel.
 constexpr int kPfGroup = 8;
 
-__device__ __forceinline__ bool group_is_shared(const SeqMeta &m, int T, int g) {
-  const int t0 = g * kPfGroup;
-  const int t1 = min(T, t0 + kPfGroup);
-  const int32_t b = m.q_seq[t0];
-  bool same = true;
-  for (int t = t0 + 1; t < t1; ++t) same = same && (m.q_seq[t] == b);
-  return same;
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -56,7 +46,7 @@ __device__ __forceinline__ v8i load_key_operand(const unsigned char *tb, int kt,
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-// Weighted-ReLU head sums of kQ queries over one 64-key LDS tile: part[j][kt]
+// Weighted-ReLU head sums of kQ queries over one 64-key tile: part[j][kt]
 // (lane l) is the sum, over the 16 heads this lane's accumulator rows cover,
 // of w[h] * max(0, qI[h] . k) for query j and key 16 kt + l % 16.
 //
@@ -64,15 +54,15 @@ __device__ __forceinline__ v8i load_key_operand(const unsigned char *tb, int kt,
 // overlap), so the epilogue (a max and an FMA per accumulator element) is
 // kept as short as it can be; each sum is split over two accumulators so
 // that consecutive FMAs do not wait on each other. The B operand is read
-// per key tile, which also bounds how many MFMA results are live at once.
-template <int kQ>
-__device__ __forceinline__ void score_tiles(const v8i (&a)[kQ][4], const unsigned char *tb, int kg,
-                                            int c16, const float (&wv)[kQ][16],
-                                            float (&part)[kQ][4]) {
+// per 16-key tile, which also bounds how many MFMA results are live at once.
+// load_b(kt) returns the B operand of key tile kt.
+template <int kQ, class LoadB>
+__device__ __forceinline__ void score_tiles(const v8i (&a)[kQ][4], LoadB load_b,
+                                            const float (&wv)[kQ][16], float (&part)[kQ][4]) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const v8i b = load_key_operand(tb, kt, kg, c16);
+    const v8i b = load_b(kt);
 #pragma unroll
     for (int j = 0; j < kQ; ++j) {
       float ev = 0.0f, od = 0.0f;

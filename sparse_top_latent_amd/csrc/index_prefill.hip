@@ -24,7 +24,19 @@ namespace {
 // the ReLU/weight epilogue instead of by HBM. Three tile buffers let one
 // barrier per tile both publish tile i and free the buffer that tile i + 2
 // overwrites. Keys past a query's own position are neither scored nor stored.
+// A group whose rows span a sequence boundary is scored by the same
+// workgroup, one row per wave, without sharing.
 // --------------------------------------------------------------------------
+// A group is "shared" when all of its rows name the same sequence.
+__device__ __forceinline__ bool group_is_shared(const SeqMeta &m, int T, int g) {
+  const int t0 = g * kPfGroup;
+  const int t1 = min(T, t0 + kPfGroup);
+  const int32_t b = m.q_seq[t0];
+  bool same = true;
+  for (int t = t0 + 1; t < t1; ++t) same = same && (m.q_seq[t] == b);
+  return same;
+}
+
 constexpr int kPfChunk = 8192;  // keys per workgroup
 constexpr int kPfQpw = 1;       // queries per wave
 constexpr int kPfBufs = 3;
@@ -47,11 +59,11 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
   extern __shared__ __attribute__((aligned(16))) unsigned char tiles[];
   __shared__ int s_nmax;
   const int g = blockIdx.y;
-  if (!group_is_shared(m, T, g)) return;  // left to the per-query kernel
+  const bool shared = group_is_shared(m, T, g);  // uniform over the workgroup
   const int t0 = g * kPfGroup;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kg = lane >> 4, c16 = lane & 15;
-  int64_t start;
+  int64_t start = 0;
   if (tid == 0) {
     int mx = 0;
     for (int t = t0; t < min(T, t0 + kPfGroup); ++t) mx = max(mx, query_candidates(m, t, &start));
@@ -80,6 +92,38 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
 #pragma unroll
       for (int r = 0; r < 4; ++r) wv[j][ht * 4 + r] = w[(size_t)tt * 64 + ht * 16 + 4 * kg + r];
     }
+  }
+  if (!shared) {
+    // The group's rows name several sequences (a sequence boundary falls
+    // inside it): each wave scores its own rows, with the B operands read
+    // straight from global memory (16 keys x 128 bytes, one coalesced 2 KiB
+    // block per operand); no LDS and no barrier.
+#pragma unroll
+    for (int j = 0; j < kQpw; ++j) {
+      const int t = t0 + kQpw * wave + j;
+      int64_t st = 0;
+      const int n = t < T ? query_candidates(m, t, &st) : 0;
+      const int cend = min(n, c0 + kPfChunk);
+      for (int kbase = c0; kbase < cend; kbase += kIdxTileKeys) {
+        float part[1][4];
+        const v8i(&aj)[1][4] = *reinterpret_cast<const v8i(*)[1][4]>(&a[j]);
+        const float(&wj)[1][16] = *reinterpret_cast<const float(*)[1][16]>(&wv[j]);
+        score_tiles<1>(
+            aj,
+            [&](int kt) {
+              int key = kbase + kt * 16 + c16;
+              key = key < n ? key : n - 1;
+              const v4i *src = (const v4i *)(k_idx + (st + key) * 128 + kg * 32);
+              const v4i lo = src[0], hi = src[1];
+              return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            },
+            wj, part);
+        const float keep = tile_scores(part[0]);
+        const int sidx = kbase + lane;
+        if (sidx < n) scores[(size_t)t * stride + sidx] = keep;
+      }
+    }
+    return;
   }
   query_candidates(m, t0, &start);  // the group's sequence start
   // DMA pieces of this thread: piece p = u * kThreads + tid of the 8 KiB tile
@@ -116,7 +160,7 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
     const unsigned char *tb = tiles + (i % kPfBufs) * kIdxTileBytes;
     const int kbase = c0 + i * kIdxTileKeys;
     float part[kQpw][4];
-    score_tiles<kQpw>(a, tb, kg, c16, wv, part);
+    score_tiles<kQpw>(a, [&](int kt) { return load_key_operand(tb, kt, kg, c16); }, wv, part);
     const int s = kbase + lane;
 #pragma unroll
     for (int j = 0; j < kQpw; ++j) {

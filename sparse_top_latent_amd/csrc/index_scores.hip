@@ -144,7 +144,6 @@ __device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t
 
 template <bool kHist>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int k, int iters,
-                                                              int skip_shared,
                                                               const uint8_t *__restrict__ q_idx,
                                                               const float *__restrict__ w,
                                                               const uint8_t *__restrict__ k_idx,
@@ -160,7 +159,6 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int wave_keys = iters * kIdxTileKeys;
   const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
   if (chunk0 >= n) return;
-  if (skip_shared && group_is_shared(m, T, t / kPfGroup)) return;  // scored by k_index_fp8_pf
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kg = lane >> 4, c16 = lane & 15;
@@ -203,7 +201,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
     asm volatile("" ::: "memory");
     const unsigned char *tb = mybuf + (it & 1) * kIdxTileBytes;
     float part[1][4];
-    score_tiles<1>(a, tb, kg, c16, wv, part);
+    score_tiles<1>(a, [&](int kt) { return load_key_operand(tb, kt, kg, c16); }, wv, part);
     const float keep = tile_scores(part[0]);
     const int s = wbase + it * kIdxTileKeys + lane;
     // the tile buffer is free once this iteration's LDS reads completed
@@ -265,27 +263,23 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     (void)hipGetLastError();
     attr = true;
   }
-  // many query rows per sequence: score shared kPfGroup-row groups with the
-  // query-tiled kernel, the rest with the per-query kernel
-  const bool prefill = T >= 4 * kPfGroup && T >= 4 * m.num_seqs;
+  // many query rows per sequence: the query-tiled kernel (it also scores the
+  // row groups that span a sequence boundary); the level-0 histogram then
+  // comes from a separate pass over the scores
+  if (T >= 4 * kPfGroup && T >= 4 * m.num_seqs) {
+    hipError_t e = launch_index_fp8_prefill(m, T, q_idx, w, k_idx, scores, stride, s);
+    if (e != hipSuccess || !sel) return e;
+    return launch_topk_hist0(m, T, scores, stride, *sel, s);
+  }
   const int iters = index_fp8_iters(T, m.max_kv_len);
   const int per_wg = kIdxWaves * iters * kIdxTileKeys;
   dim3 grid((m.max_kv_len + per_wg - 1) / per_wg, T);
   TopkWs none{};
-  if (prefill) {
-    hipError_t e = launch_index_fp8_prefill(m, T, q_idx, w, k_idx, scores, stride, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
-                       1, q_idx, w, k_idx, scores, stride, none);
-    e = hipGetLastError();
-    if (e != hipSuccess || !sel) return e;
-    return launch_topk_hist0(m, T, scores, stride, *sel, s);
-  }
   if (sel)
-    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters, 0,
+    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
                        q_idx, w, k_idx, scores, stride, *sel);
   else
-    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters, 0,
+    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
                        q_idx, w, k_idx, scores, stride, none);
   return hipGetLastError();
 }
