@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
   const int g = blockIdx.y;
   const bool shared = group_is_shared(m, T, g);  // uniform over the workgroup
   const int t0 = g * kPfGroup;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, c16 = lane & 15;
   int64_t start = 0;
   if (tid == 0) {

@@ -96,6 +96,8 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
 // the LDS banks; the swizzle is applied on the DMA source side.
 // --------------------------------------------------------------------------
 constexpr int kIdxWaves = 4;                 // waves per workgroup
+constexpr bool kIdxRegLoads = false;
+constexpr int kKeyLoadPolicy = 2;            // nontemporal (streamed) key copies
 constexpr int kIdxDmaPerTile = kIdxTileBytes / (64 * 16);  // 8 DMA issues per lane
 constexpr int kIdxBufs = 2;                  // tiles in flight per wave
 constexpr size_t kIdxSmem = (size_t)kIdxWaves * kIdxBufs * kIdxTileBytes;
@@ -128,7 +130,7 @@ __device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t
 #pragma unroll
     for (int i = 0; i < kIdxDmaPerTile; ++i)
       __builtin_amdgcn_global_load_lds(src + i * 1024 + lane_off[i & 1], (lds_void *)(buf + i * 1024),
-                                       16, 0, 0);
+                                       16, 0, kKeyLoadPolicy);
   } else {
     // sequence tail: rows past the end repeat the last key (their scores are dropped)
 #pragma unroll
@@ -137,7 +139,7 @@ __device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t
       int key = base + r;
       key = key < n ? key : n - 1;
       const uint8_t *src = k_idx + (start + key) * 128 + (lane_off[i & 1] & 127);
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, kKeyLoadPolicy);
     }
   }
 }
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
   if (chunk0 >= n) return;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform loop bounds
   const int kg = lane >> 4, c16 = lane & 15;
 
   // A tiles: head (ht*16 + c16), bytes [32*kg, 32*kg+32) of its 128-byte row
@@ -227,6 +229,95 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   }
 }
 
+// Register-load variant: no LDS for the keys. Each lane loads its own MFMA B
+// operand straight from global memory (key 16 kt + c16, bytes [32 kg, 32 kg
+// + 32): two 16-byte nontemporal loads; per 16-key operand the wave reads one
+// contiguous 2 KiB block), one 64-key tile ahead of the MFMAs. Loads past the
+// wave's last tile re-read that tile, so every iteration issues the same
+// number of loads and the compiler's vmcnt waits stay exact.
+template <bool kHist>
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8_reg(SeqMeta m, int T, int k, int iters,
+                                                                  const uint8_t *__restrict__ q_idx,
+                                                                  const float *__restrict__ w,
+                                                                  const uint8_t *__restrict__ k_idx,
+                                                                  float *__restrict__ scores,
+                                                                  int64_t stride, TopkWs sel) {
+  __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
+  const int t = blockIdx.y;
+  int64_t start;
+  const int n = query_candidates(m, t, &start);
+  const int wave_keys = iters * kIdxTileKeys;
+  const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
+  if (chunk0 >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform loop bounds
+  const int kg = lane >> 4, c16 = lane & 15;
+
+  v8i a[1][4];
+  float wv[1][16];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
+    const v4i lo = src[0], hi = src[1];
+    a[0][ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[0][ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
+  }
+  if (kHist) {
+    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
+    __syncthreads();
+  }
+
+  const int wbase = chunk0 + wave * wave_keys;
+  const int nit = wbase < n ? min(iters, (n - wbase + kIdxTileKeys - 1) / kIdxTileKeys) : 0;
+  const uint8_t *kbase = k_idx + start * 128 + kg * 32;
+  auto load = [&](v8i (&b)[4], int it) {
+    const int tb = wbase + min(it, nit - 1) * kIdxTileKeys;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = min(tb + kt * 16 + c16, n - 1);
+      const v4i *src = (const v4i *)(kbase + (size_t)key * 128);
+      const v4i lo = __builtin_nontemporal_load(src);
+      const v4i hi = __builtin_nontemporal_load(src + 1);
+      b[kt] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  };
+  float *srow = scores + t * stride;
+  auto consume = [&](const v8i (&b)[4], int it) {
+    float part[1][4];
+    score_tiles<1>(a, [&](int kt) { return b[kt]; }, wv, part);
+    const float keep = tile_scores(part[0]);
+    const int s = wbase + it * kIdxTileKeys + lane;
+    if (s < n) {
+      srow[s] = keep;
+      if (kHist) {
+        const uint32_t bin = score_key(keep) >> kHist0Shift;
+        lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
+      }
+    }
+  };
+  if (nit > 0) {
+    v8i b0[4], b1[4];
+    load(b0, 0);
+    for (int it = 0; it < nit; it += 2) {
+      load(b1, it + 1);
+      consume(b0, it);
+      if (it + 1 >= nit) break;
+      load(b0, it + 2);
+      consume(b1, it + 1);
+    }
+  }
+  if (kHist) {
+    __syncthreads();
+    uint32_t *g = sel.hist0 + (size_t)t * kHist0Bins;
+    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) {
+      const uint32_t c = hist[i];
+      if (c & 0xFFFFu) atomicAdd(g + 2 * i, c & 0xFFFFu);
+      if (c >> 16) atomicAdd(g + 2 * i + 1, c >> 16);
+    }
+  }
+}
+
 }  // namespace
 
 int index_fp8_iters(int T, int max_kv_len) {
@@ -275,7 +366,14 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   const int per_wg = kIdxWaves * iters * kIdxTileKeys;
   dim3 grid((m.max_kv_len + per_wg - 1) / per_wg, T);
   TopkWs none{};
-  if (sel)
+  if (kIdxRegLoads) {
+    if (sel)
+      hipLaunchKernelGGL(k_index_fp8_reg<true>, grid, dim3(kIdxWaves * 64), 0, s, m, T, k, iters,
+                         q_idx, w, k_idx, scores, stride, *sel);
+    else
+      hipLaunchKernelGGL(k_index_fp8_reg<false>, grid, dim3(kIdxWaves * 64), 0, s, m, T, k, iters,
+                         q_idx, w, k_idx, scores, stride, none);
+  } else if (sel)
     hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
                        q_idx, w, k_idx, scores, stride, *sel);
   else

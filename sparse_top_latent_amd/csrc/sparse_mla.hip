@@ -24,7 +24,8 @@
 //      accumulator layout, V^T is read column-wise from the LDS tile.
 //    It writes a partial (max, sum in fp32; O in bf16) per (query, split, head).
 //  * k_mla_combine: merges the splits of each (query, head) with the usual
-//    log-sum-exp rescaling and applies the gate in the epilogue.
+//    log-sum-exp rescaling and applies the gate in the epilogue; partials are
+//    stored and read in the split kernel's register order (coalesced).
 
 #include "kernels.h"
 
@@ -135,6 +136,7 @@ constexpr int kScales = kD / 32;              // 18 E8M0 scales per row
 constexpr int kKsteps = kD / 32;              // 18 MFMA k-steps for q . row
 constexpr int kCt = kDc / 16;                 // 32 channel tiles of the value
 constexpr float kRescaleSlack = 8.0f;         // log2 headroom before the running max moves
+constexpr bool kMlaEightWaves = true;         // bf16: two waves per SIMD (k_mla_split8)
 
 constexpr size_t kBfSmem = (size_t)kMaxTiles * kTileBytes;
 constexpr size_t kMxSmem = (size_t)kMaxTiles * kMxRawBytes + kTileBytes + kMlaRowsPerSplit * kScales;
@@ -150,10 +152,14 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf &a, const v8bf &b, const v4f
 
 __device__ __forceinline__ v8bf as_v8bf(const v4i &x) { return __builtin_bit_cast(v8bf, x); }
 
-// 16-byte chunk `chunk` of tile row `row` lives at chunk slot row*72 + (chunk ^ (row & 7)):
-// an XOR swizzle inside groups of 8 chunks that spreads same-column reads of
-// consecutive rows over the LDS banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowChunks + (chunk ^ (row & 7)); }
+// 16-byte chunk `chunk` of tile row `row` lives at chunk slot
+// row*72 + (chunk ^ row_swz(row)): an XOR swizzle inside aligned groups of 8
+// chunks that spreads same-column reads of consecutive rows over the LDS
+// banks. Chosen by measurement on gfx950 (two waves per SIMD): the S-operand
+// reads (ds_read_b128, 16 consecutive rows, one chunk) run at about 226 B per
+// clock and CU, the V^T reads (ds_read_b64_tr_b16) at about 126.
+__device__ __forceinline__ int row_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowChunks + (chunk ^ row_swz(row)); }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, uint16_t *__restri
       for (int j = 0; j < kBfDma; ++j) {
         const int c = j * 256 + tid;                 // chunk slot in the tile
         const int r = c / kRowChunks;
-        const int col = (c - r * kRowChunks) ^ (r & 7);
+        const int col = (c - r * kRowChunks) ^ row_swz(r);
         const void *src = gr[j] >= 0
                               ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
                               : (const void *)g_zero16;
@@ -373,23 +379,226 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, uint16_t *__restri
     }
   }
   // partial O^T in bf16 (the softmax weights are still unnormalised, so only
-  // relative precision matters): lane holds channels ct*16 + 4g + i of `head`
-  const size_t pbase = (((size_t)t * S + split) * kH + head) * kDc;
+  // relative precision matters), stored in register order: [t][split][wave]
+  // [ct][lane] x 4 channels, so that each store of a wave is 512 contiguous
+  // bytes. Lane (g, c16) holds channels ct*16 + 4g + i of head wave*16 + c16.
+  uint2 *pdst = (uint2 *)opart + ((((size_t)t * S + split) * 4 + wave) * kCt) * 64 + lane;
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) {
     const uint32_t lo = f32_to_bf16_bits(acc[ct][0]) | (f32_to_bf16_bits(acc[ct][1]) << 16);
     const uint32_t hi = f32_to_bf16_bits(acc[ct][2]) | (f32_to_bf16_bits(acc[ct][3]) << 16);
-    *(uint2 *)(opart + pbase + ct * 16 + 4 * g) = make_uint2(lo, hi);
+    pdst[ct * 64] = make_uint2(lo, hi);
   }
   if (g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m_run, l_run);
 }
 
-constexpr int kMaxSplits = 2048 / kMlaRowsPerSplit;
+// --------------------------------------------------------------------------
+// bf16 split kernel with two waves per SIMD.
+//
+// 8 waves: wave w serves heads 16 (w % 4) .. 16 (w % 4) + 15 for the tiles of
+// its set (w / 4): set 0 takes tiles 0 and 2, set 1 tiles 1 and 3, each with
+// its own running max, sum and output accumulator. Every tile of the split is
+// gathered up front (the set issues its own two tiles), so the second pair of
+// tiles streams in while the first pair is computed. At the end set 1 hands
+// its state to set 0 through LDS and set 0 merges and writes the partial.
+// --------------------------------------------------------------------------
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const uint16_t *__restrict__ opart,
-                                                     const float2 *__restrict__ ml, int S) {
-  const int h = blockIdx.x, t = blockIdx.y;
-  const int c = threadIdx.x * 4;
+// Eight transposed LDS reads (ds_read_b64_tr_b16) of four V^T operands at
+// base[i] + kOff (rows 4g.., lo) and base[i] + kOff + 16 rows (hi), waited for
+// in the same asm block. Issued as asm because the compiler otherwise drains
+// every outstanding global->LDS copy before a transposed read.
+template <int kOff>
+__device__ __forceinline__ void tr_reads(const uint32_t (&base)[4], v2u (&lo)[4], v2u (&hi)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]),
+        "=&v"(hi[2]), "=&v"(hi[3])
+      : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(kOff), "i"(kOff + 16 * kRowChunks * 16)
+      : "memory");
+}
+
+__device__ __forceinline__ v8bf cat_bf16(const v2u &lo, const v2u &hi) {
+  const v4i x = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+  return as_v8bf(x);
+}
+
+template <int kM>
+__device__ __forceinline__ void pv_block(const uint32_t (&base)[4], const v8bf &pb, v4f (&acc)[kCt]) {
+  v2u lo[4], hi[4];
+  tr_reads<kM * 128>(base, lo, hi);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[4 * kM + i] = mfma_bf16(cat_bf16(lo[i], hi[i]), pb, acc[4 * kM + i]);
+}
+
+__global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
+                                                    float2 *__restrict__ ml) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int64_t rows[kMlaRowsPerSplit];
+  const int split = blockIdx.x, t = blockIdx.y, S = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 3, set = wave >> 2, st = tid & 255;
+  const int g = lane >> 4, c16 = lane & 15;
+  int64_t start;
+  const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
+  const int r0 = split * kMlaRowsPerSplit;
+  const int nrows = min(kMlaRowsPerSplit, a.k - r0);
+  const int ntiles = (nrows + kTile - 1) / kTile;
+  if (tid < kMlaRowsPerSplit) {
+    int32_t pos = tid < nrows ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
+    rows[tid] = (pos >= 0 && pos < L) ? start + pos : -1;
+  }
+  __syncthreads();  // rows[] ready
+  const int head = hg * 16 + c16;
+  const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
+  v8bf qreg[kKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
+
+  // gather: the set's 256 threads copy its tiles set and set + 2 (tiles past
+  // ntiles read the zero block, so every thread issues 2 x kBfDma copies)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int tt = set + 2 * u;
+    unsigned char *tbase = smem + tt * kTileBytes;
+    int64_t gr[kBfDma];
+#pragma unroll
+    for (int j = 0; j < kBfDma; ++j)
+      gr[j] = tt < ntiles ? rows[tt * kTile + (j * 256 + st) / kRowChunks] : -1;
+#pragma unroll
+    for (int j = 0; j < kBfDma; ++j) {
+      const int c = j * 256 + st;
+      const int r = c / kRowChunks;
+      const int col = (c - r * kRowChunks) ^ row_swz(r);
+      const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
+                                   : (const void *)g_zero16;
+      dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
+    }
+  }
+
+  v4f acc[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float scale2 = a.tau * kLog2e;  // logits kept in the exp2 domain
+  // V^T read bases: lane (g, c16) reads rows vr, vr + 16, chunk 2 ct + q at
+  // sub-offset vsub; for ct = 4 m + i the address is base[i] + 128 m
+  const int vr = 4 * g + (c16 >> 2);
+  const int q = (c16 & 3) >> 1, vsub = (c16 & 1) * 8;
+
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (u == 0) wait_vmcnt<kBfDma>(); else wait_vmcnt<0>();
+    barrier_lds();  // tiles 2u and 2u + 1 have landed
+    const int tt = set + 2 * u;
+    if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
+    const unsigned char *tile = smem + tt * kTileBytes;
+    v4f sv[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      v4f sacc = {0.f, 0.f, 0.f, 0.f};
+      const int row = rt * 16 + c16;
+#pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks)
+        sacc = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(row, 4 * ks + g) * 16)), qreg[ks], sacc);
+      sv[rt] = sacc;
+    }
+    float lg[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int ri = tt * kTile + (j >> 2) * 16 + 4 * g + (j & 3);
+      bool ok = ri < nrows && rows[ri] >= 0;
+      lg[j] = ok ? sv[j >> 2][j & 3] * scale2 : -INFINITY;
+      mt = fmaxf(mt, lg[j]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    if (!(mt > -INFINITY)) continue;  // no selected row in this tile (uniform over heads)
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) acc[ct] *= alpha;
+      m_run = m_new;
+    }
+    float p[8], ps = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = exp2f(lg[j] - m_run);
+      ps += p[j];
+    }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run += ps;
+    v8bf pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
+    const uint32_t tl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)tile;
+    uint32_t base[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) base[i] = tl + (vr * kRowChunks + ((2 * i + q) ^ row_swz(vr))) * 16 + vsub;
+    pv_block<0>(base, pb, acc);
+    pv_block<1>(base, pb, acc);
+    pv_block<2>(base, pb, acc);
+    pv_block<3>(base, pb, acc);
+    pv_block<4>(base, pb, acc);
+    pv_block<5>(base, pb, acc);
+    pv_block<6>(base, pb, acc);
+    pv_block<7>(base, pb, acc);
+  }
+
+  // merge the two sets: set 1 -> LDS -> set 0 (the tile area is free now)
+  barrier_lds();
+  v4f *xch = (v4f *)smem;                           // [hg][ct][lane]
+  float2 *mlx = (float2 *)(smem + 4 * kCt * 64 * 16);  // [hg][lane]
+  if (set == 1) {
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) xch[(hg * kCt + ct) * 64 + lane] = acc[ct];
+    mlx[hg * 64 + lane] = make_float2(m_run, l_run);
+  }
+  barrier_lds();
+  if (set == 1) return;
+  const float2 other = mlx[hg * 64 + lane];
+  const float m = fmaxf(m_run, other.x);
+  const float sa = m > -INFINITY ? exp2f(m_run - m) : 0.0f;
+  const float sb = m > -INFINITY ? exp2f(other.x - m) : 0.0f;
+  const float l = l_run * sa + other.y * sb;
+  uint2 *pdst = (uint2 *)opart + ((((size_t)t * S + split) * 4 + hg) * kCt) * 64 + lane;
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    const v4f b = xch[(hg * kCt + ct) * 64 + lane];
+    const v4f o = acc[ct] * sa + b * sb;
+    const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+    pdst[ct * 64] = make_uint2(lo, hi);
+  }
+  if (g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m, l);
+}
+
+constexpr int kMaxSplits = 2048 / kMlaRowsPerSplit;
+constexpr int kCombCt = 4;  // channel tiles per combine workgroup (256 threads)
+
+// One workgroup per (query, head group of 16, 4 channel tiles); thread (ct,
+// lane) owns the same register slot the split kernel stored, so every partial
+// load of a wave is 512 contiguous bytes.
+__global__ __launch_bounds__(64 * kCombCt) void k_mla_combine(MlaArgs a, const uint16_t *__restrict__ opart,
+                                                              const float2 *__restrict__ ml, int S) {
+  const int ct = blockIdx.x * kCombCt + (threadIdx.x >> 6);
+  const int wave = blockIdx.y, t = blockIdx.z;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int h = wave * 16 + c16;
+  const int c = ct * 16 + 4 * g;
   // gate logits first: their loads overlap the partial loads below
   float gv[4] = {0.f, 0.f, 0.f, 0.f};
   if (a.gate) {
@@ -403,7 +612,7 @@ __global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const uint16_t *
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < S) {
       st[s] = ml[((size_t)t * S + s) * kH + h];
-      const uint2 b = *(const uint2 *)(opart + (((size_t)t * S + s) * kH + h) * kDc + c);
+      const uint2 b = ((const uint2 *)opart)[((((size_t)t * S + s) * 4 + wave) * kCt + ct) * 64 + lane];
       x[s] = (v4f){bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
                    bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16)};
     }
@@ -443,7 +652,7 @@ __global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, const uint16_t *
   } else {
     *(v4f *)((float *)a.out + oi) = (v4f){y[0], y[1], y[2], y[3]};
   }
-  if (a.lse && threadIdx.x == 0) a.lse[(size_t)t * kH + h] = lse;
+  if (a.lse && ct == 0 && g == 0) a.lse[(size_t)t * kH + h] = lse;
 }
 
 }  // namespace
@@ -474,11 +683,15 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
     (void)hipFuncSetAttribute((const void *)k_mla_split<true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxSmem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split8,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
     (void)hipGetLastError();
     attr = true;
   }
   if (a.kv_dtype == SGA_MXFP8_E4M3FN)
     hipLaunchKernelGGL(k_mla_split<true>, dim3(S, a.T), dim3(256), kMxSmem, s, a, opart, ml);
+  else if (kMlaEightWaves)
+    hipLaunchKernelGGL(k_mla_split8, dim3(S, a.T), dim3(512), kBfSmem, s, a, opart, ml);
   else
     hipLaunchKernelGGL(k_mla_split<false>, dim3(S, a.T), dim3(256), kBfSmem, s, a, opart, ml);
   return hipGetLastError();
@@ -489,7 +702,7 @@ hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s) {
   const int S = mla_splits(a.k);
   const uint16_t *opart = (const uint16_t *)ws;
   const float2 *ml = (const float2 *)((const char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
-  hipLaunchKernelGGL(k_mla_combine, dim3(kH, a.T), dim3(128), 0, s, a, opart, ml, S);
+  hipLaunchKernelGGL(k_mla_combine, dim3(kCt / kCombCt, 4, a.T), dim3(64 * kCombCt), 0, s, a, opart, ml, S);
   return hipGetLastError();
 }
 
