@@ -591,47 +591,60 @@ constexpr int kCombCt = 4;  // channel tiles per combine workgroup (256 threads)
 
 // One workgroup per (query, head group of 16, 4 channel tiles); thread (ct,
 // lane) owns the same register slot the split kernel stored, so every partial
-// load of a wave is 512 contiguous bytes.
+// load of a wave is 512 contiguous bytes. kS > 0 fixes the split count at
+// compile time (all loads issue before the first use); kS = 0 takes it from S.
+template <int kS>
 __global__ __launch_bounds__(64 * kCombCt) void k_mla_combine(MlaArgs a, const uint16_t *__restrict__ opart,
                                                               const float2 *__restrict__ ml, int S) {
+  if (kS > 0) S = kS;
   const int ct = blockIdx.x * kCombCt + (threadIdx.x >> 6);
   const int wave = blockIdx.y, t = blockIdx.z;
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const int h = wave * 16 + c16;
   const int c = ct * 16 + 4 * g;
-  // gate logits first: their loads overlap the partial loads below
-  float gv[4] = {0.f, 0.f, 0.f, 0.f};
+  const size_t oi = ((size_t)t * kH + h) * kDc + c;
+  // gate logits first, raw: their loads overlap the partial loads below and
+  // are only decoded after them
+  const bool gate_bf16 = a.gate_dtype == SGA_BF16;
+  v4i graw = {0, 0, 0, 0};
   if (a.gate) {
-    const size_t gi = ((size_t)t * kH + h) * kDc + c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gv[i] = load_as_f32(a.gate, a.gate_dtype, gi + i);
+    if (gate_bf16) {
+      const uint2 gb = *(const uint2 *)((const uint16_t *)a.gate + oi);
+      graw.x = (int)gb.x;
+      graw.y = (int)gb.y;
+    } else {
+      graw = *(const v4i *)((const float *)a.gate + oi);
+    }
   }
-  float2 st[kMaxSplits];
-  v4f x[kMaxSplits];
+  constexpr int kN = kS > 0 ? kS : kMaxSplits;
+  float2 st[kN];
+  uint2 xb[kN];
+  const uint2 *src = (const uint2 *)opart + ((((size_t)t * S) * 4 + wave) * kCt + ct) * 64 + lane;
+  const float2 *msrc = ml + (size_t)t * S * kH + h;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < S) {
-      st[s] = ml[((size_t)t * S + s) * kH + h];
-      const uint2 b = ((const uint2 *)opart)[((((size_t)t * S + s) * 4 + wave) * kCt + ct) * 64 + lane];
-      x[s] = (v4f){bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
-                   bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16)};
+  for (int s = 0; s < kN; ++s) {
+    if (kS > 0 || s < S) {
+      st[s] = msrc[(size_t)s * kH];
+      xb[s] = src[(size_t)s * 4 * kCt * 64];
     }
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
-    if (s < S) M = fmaxf(M, st[s].x);
+  for (int s = 0; s < kN; ++s)
+    if (kS > 0 || s < S) M = fmaxf(M, st[s].x);
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   float lse = -INFINITY;
   if (M > -INFINITY) {
     float wsum = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      if (s < S && st[s].x > -INFINITY) {
+    for (int s = 0; s < kN; ++s) {
+      if ((kS > 0 || s < S) && st[s].x > -INFINITY) {
         const float wgt = exp2f(st[s].x - M);
         wsum = fmaf(wgt, st[s].y, wsum);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = fmaf(wgt, x[s][i], o[i]);
+        o[0] = fmaf(wgt, bf16_bits_to_f32(xb[s].x & 0xFFFFu), o[0]);
+        o[1] = fmaf(wgt, bf16_bits_to_f32(xb[s].x >> 16), o[1]);
+        o[2] = fmaf(wgt, bf16_bits_to_f32(xb[s].y & 0xFFFFu), o[2]);
+        o[3] = fmaf(wgt, bf16_bits_to_f32(xb[s].y >> 16), o[3]);
       }
     }
     const float inv = 1.0f / wsum;
@@ -639,9 +652,18 @@ __global__ __launch_bounds__(64 * kCombCt) void k_mla_combine(MlaArgs a, const u
     for (int i = 0; i < 4; ++i) o[i] *= inv;
     lse = M / kLog2e + __logf(wsum);
   }
-  const size_t oi = ((size_t)t * kH + h) * kDc + c;
   float y[4] = {o[0], o[1], o[2], o[3]};
   if (a.gate) {
+    float gv[4];
+    if (gate_bf16) {
+      gv[0] = bf16_bits_to_f32((uint32_t)graw.x & 0xFFFFu);
+      gv[1] = bf16_bits_to_f32((uint32_t)graw.x >> 16);
+      gv[2] = bf16_bits_to_f32((uint32_t)graw.y & 0xFFFFu);
+      gv[3] = bf16_bits_to_f32((uint32_t)graw.y >> 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gv[i] = __int_as_float(graw[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] *= sigmoidf_exact_ends(gv[i]);
   }
@@ -702,7 +724,11 @@ hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s) {
   const int S = mla_splits(a.k);
   const uint16_t *opart = (const uint16_t *)ws;
   const float2 *ml = (const float2 *)((const char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
-  hipLaunchKernelGGL(k_mla_combine, dim3(kCt / kCombCt, 4, a.T), dim3(64 * kCombCt), 0, s, a, opart, ml, S);
+  const dim3 grid(kCt / kCombCt, 4, a.T), block(64 * kCombCt);
+  if (S == kMaxSplits)
+    hipLaunchKernelGGL(k_mla_combine<kMaxSplits>, grid, block, 0, s, a, opart, ml, S);
+  else
+    hipLaunchKernelGGL(k_mla_combine<0>, grid, block, 0, s, a, opart, ml, S);
   return hipGetLastError();
 }
 
