@@ -210,7 +210,7 @@ MlaArgs mla_args(const sga_problem *p, const void *q, const void *kv, const uint
 }
 
 sga_status run_index(const sga_problem *p, const Plan &plan, const void *q_idx, const float *w,
-                     const void *k_idx, float *scores, int64_t stride, const TopkWs *sel,
+                     const void *k_idx, float *scores, int64_t stride, TopkWs *sel,
                      hipStream_t s) {
   const SeqMeta m = meta_of(p);
   if (plan.idx == IdxPath::kFp8)
@@ -295,9 +295,7 @@ sga_status sga_topk_select(const sga_problem *p, const float *scores, int32_t *t
     hipStream_t s = (hipStream_t)stream;
     const SeqMeta m = meta_of(p);
     TopkWs w = topk_ws_carve(ws, p->num_q, p->max_kv_len);
-    SGA_TRY(launched(launch_zero_u32(w.hist0, w.zero_words, s), "zero"));
-    SGA_TRY(launched(launch_topk_hist0(m, p->num_q, scores, p->max_kv_len, w, s), "hist0"));
-    SGA_TRY(launched(launch_topk_thr0(m, p->num_q, p->topk, w, s), "topk threshold"));
+    SGA_TRY(launched(launch_topk_hist0(m, p->num_q, scores, p->max_kv_len, &w, s), "hist0"));
     SGA_TRY(launched(launch_topk_scan(m, p->num_q, p->topk, scores, p->max_kv_len, w, topk_idx, s),
                      "topk scan"));
     return launched(launch_topk_final(m, p->num_q, p->topk, w, topk_idx, s), "topk final");
@@ -360,11 +358,9 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
     TopkWs tw = topk_ws_carve(tws, T, p->max_kv_len);
     const bool prof = g_prof.used < g_prof.max_calls;
 
-    SGA_TRY(launched(launch_zero_u32(tw.hist0, tw.zero_words, s), "zero"));
     if (prof) prof_mark(s, 0);
     SGA_TRY(run_index(p, plan, q_idx, w, k_idx, scores, stride, &tw, s));
     if (prof) prof_mark(s, 1);
-    SGA_TRY(launched(launch_topk_thr0(m, T, p->topk, tw, s), "topk threshold"));
     SGA_TRY(launched(launch_topk_scan(m, T, p->topk, scores, stride, tw, idx, s), "topk scan"));
     SGA_TRY(launched(launch_topk_final(m, T, p->topk, tw, idx, s), "topk final"));
     if (prof) prof_mark(s, 2);

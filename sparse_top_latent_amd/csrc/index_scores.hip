@@ -25,23 +25,11 @@
 // re-reads the scores for it.
 
 #include "index_common.h"
+#include "select_common.h"
 
 namespace sga {
 
 namespace {
-
-__device__ __forceinline__ void hist_flush(uint32_t *lds_hist, uint32_t *g_hist) {
-  __syncthreads();
-  for (int i = threadIdx.x; i < kHist0Bins; i += blockDim.x) {
-    uint32_t c = lds_hist[i];
-    if (c) atomicAdd(g_hist + i, c);
-  }
-}
-
-__device__ __forceinline__ void hist_zero(uint32_t *lds_hist) {
-  for (int i = threadIdx.x; i < kHist0Bins; i += blockDim.x) lds_hist[i] = 0u;
-  __syncthreads();
-}
 
 // --------------------------------------------------------------------------
 // fp32 path
@@ -58,7 +46,8 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
   __shared__ float qs[kF32MaxQ];
   __shared__ float ws[64];
   __shared__ uint32_t hist[kHist0Bins];
-  const bool want_hist = sel.hist0 != nullptr;
+  __shared__ uint32_t scratch[kF32Block / 64 + 1];
+  const bool want_hist = sel.lists != nullptr;
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
@@ -66,7 +55,8 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
   if (base >= n) return;
   for (int i = threadIdx.x; i < HI * DI; i += kF32Block) qs[i] = q_idx[(size_t)t * HI * DI + i];
   for (int i = threadIdx.x; i < HI; i += kF32Block) ws[i] = w[(size_t)t * HI + i];
-  if (want_hist) hist_zero(hist);
+  if (want_hist)
+    for (int i = threadIdx.x; i < kHist0Bins; i += kF32Block) hist[i] = 0u;
   __syncthreads();
   const int s = base + threadIdx.x;
   if (s < n) {
@@ -81,7 +71,10 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
     scores[t * stride + s] = acc;
     if (want_hist) atomicAdd(&hist[score_key(acc) >> kHist0Shift], 1u);
   }
-  if (want_hist) hist_flush(hist, sel.hist0 + (size_t)t * kHist0Bins);
+  if (want_hist) {
+    __syncthreads();
+    write_hist0_list<false>(hist, sel, t, blockIdx.x, scratch);
+  }
 }
 
 // --------------------------------------------------------------------------
@@ -96,7 +89,6 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
 // the LDS banks; the swizzle is applied on the DMA source side.
 // --------------------------------------------------------------------------
 constexpr int kIdxWaves = 4;                 // waves per workgroup
-constexpr bool kIdxRegLoads = false;
 constexpr int kKeyLoadPolicy = 2;            // nontemporal (streamed) key copies
 constexpr int kIdxDmaPerTile = kIdxTileBytes / (64 * 16);  // 8 DMA issues per lane
 constexpr int kIdxBufs = 2;                  // tiles in flight per wave
@@ -155,6 +147,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   // level-0 histogram with two 16-bit bins per word (a workgroup scores at most
   // 4 x 32 x 64 = 8192 keys, so a bin cannot overflow)
   __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
+  __shared__ uint32_t scratch[kIdxWaves + 1];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
@@ -220,101 +213,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   }
   if (kHist) {
     __syncthreads();
-    uint32_t *g = sel.hist0 + (size_t)t * kHist0Bins;
-    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) {
-      const uint32_t c = hist[i];
-      if (c & 0xFFFFu) atomicAdd(g + 2 * i, c & 0xFFFFu);
-      if (c >> 16) atomicAdd(g + 2 * i + 1, c >> 16);
-    }
-  }
-}
-
-// Register-load variant: no LDS for the keys. Each lane loads its own MFMA B
-// operand straight from global memory (key 16 kt + c16, bytes [32 kg, 32 kg
-// + 32): two 16-byte nontemporal loads; per 16-key operand the wave reads one
-// contiguous 2 KiB block), one 64-key tile ahead of the MFMAs. Loads past the
-// wave's last tile re-read that tile, so every iteration issues the same
-// number of loads and the compiler's vmcnt waits stay exact.
-template <bool kHist>
-__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8_reg(SeqMeta m, int T, int k, int iters,
-                                                                  const uint8_t *__restrict__ q_idx,
-                                                                  const float *__restrict__ w,
-                                                                  const uint8_t *__restrict__ k_idx,
-                                                                  float *__restrict__ scores,
-                                                                  int64_t stride, TopkWs sel) {
-  __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
-  const int t = blockIdx.y;
-  int64_t start;
-  const int n = query_candidates(m, t, &start);
-  const int wave_keys = iters * kIdxTileKeys;
-  const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
-  if (chunk0 >= n) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform loop bounds
-  const int kg = lane >> 4, c16 = lane & 15;
-
-  v8i a[1][4];
-  float wv[1][16];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
-    const v4i lo = src[0], hi = src[1];
-    a[0][ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wv[0][ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
-  }
-  if (kHist) {
-    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
-    __syncthreads();
-  }
-
-  const int wbase = chunk0 + wave * wave_keys;
-  const int nit = wbase < n ? min(iters, (n - wbase + kIdxTileKeys - 1) / kIdxTileKeys) : 0;
-  const uint8_t *kbase = k_idx + start * 128 + kg * 32;
-  auto load = [&](v8i (&b)[4], int it) {
-    const int tb = wbase + min(it, nit - 1) * kIdxTileKeys;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = min(tb + kt * 16 + c16, n - 1);
-      const v4i *src = (const v4i *)(kbase + (size_t)key * 128);
-      const v4i lo = __builtin_nontemporal_load(src);
-      const v4i hi = __builtin_nontemporal_load(src + 1);
-      b[kt] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-  };
-  float *srow = scores + t * stride;
-  auto consume = [&](const v8i (&b)[4], int it) {
-    float part[1][4];
-    score_tiles<1>(a, [&](int kt) { return b[kt]; }, wv, part);
-    const float keep = tile_scores(part[0]);
-    const int s = wbase + it * kIdxTileKeys + lane;
-    if (s < n) {
-      srow[s] = keep;
-      if (kHist) {
-        const uint32_t bin = score_key(keep) >> kHist0Shift;
-        lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
-      }
-    }
-  };
-  if (nit > 0) {
-    v8i b0[4], b1[4];
-    load(b0, 0);
-    for (int it = 0; it < nit; it += 2) {
-      load(b1, it + 1);
-      consume(b0, it);
-      if (it + 1 >= nit) break;
-      load(b0, it + 2);
-      consume(b1, it + 1);
-    }
-  }
-  if (kHist) {
-    __syncthreads();
-    uint32_t *g = sel.hist0 + (size_t)t * kHist0Bins;
-    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) {
-      const uint32_t c = hist[i];
-      if (c & 0xFFFFu) atomicAdd(g + 2 * i, c & 0xFFFFu);
-      if (c >> 16) atomicAdd(g + 2 * i + 1, c >> 16);
-    }
+    write_hist0_list<true>(hist, sel, t, blockIdx.x, scratch);
   }
 }
 
@@ -332,9 +231,21 @@ int index_fp8_iters(int T, int max_kv_len) {
 
 hipError_t launch_index_f32(const SeqMeta &m, int T, int k, int HI, int DI, const float *q_idx,
                             const float *w, const float *k_idx, float *scores, int64_t stride,
-                            const TopkWs *sel, hipStream_t s) {
+                            TopkWs *sel, hipStream_t s) {
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   TopkWs none{};
+  if (sel && (m.max_kv_len + kF32Block - 1) / kF32Block > kTopkMaxSlots) {
+    // too many 256-position slots for the list merge: histogram in a separate pass
+    hipLaunchKernelGGL(k_index_f32, dim3((m.max_kv_len + kF32Block - 1) / kF32Block, T), dim3(kF32Block), 0,
+                       s, m, k, HI, DI, q_idx, w, k_idx, scores, stride, none);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_topk_hist0(m, T, scores, stride, sel, s);
+  }
+  if (sel) {
+    sel->slot_keys = kF32Block;
+    sel->slot_words = 4 + kF32Block;
+  }
   dim3 grid((m.max_kv_len + kF32Block - 1) / kF32Block, T);
   hipLaunchKernelGGL(k_index_f32, grid, dim3(kF32Block), 0, s, m, k, HI, DI, q_idx, w, k_idx,
                      scores, stride, sel ? *sel : none);
@@ -342,7 +253,7 @@ hipError_t launch_index_f32(const SeqMeta &m, int T, int k, int HI, int DI, cons
 }
 
 hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx, const float *w,
-                            const uint8_t *k_idx, float *scores, int64_t stride, const TopkWs *sel,
+                            const uint8_t *k_idx, float *scores, int64_t stride, TopkWs *sel,
                             hipStream_t s) {
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   static bool attr = false;
@@ -360,20 +271,17 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   if (T >= 4 * kPfGroup && T >= 4 * m.num_seqs) {
     hipError_t e = launch_index_fp8_prefill(m, T, q_idx, w, k_idx, scores, stride, s);
     if (e != hipSuccess || !sel) return e;
-    return launch_topk_hist0(m, T, scores, stride, *sel, s);
+    return launch_topk_hist0(m, T, scores, stride, sel, s);
   }
   const int iters = index_fp8_iters(T, m.max_kv_len);
   const int per_wg = kIdxWaves * iters * kIdxTileKeys;
   dim3 grid((m.max_kv_len + per_wg - 1) / per_wg, T);
   TopkWs none{};
-  if (kIdxRegLoads) {
-    if (sel)
-      hipLaunchKernelGGL(k_index_fp8_reg<true>, grid, dim3(kIdxWaves * 64), 0, s, m, T, k, iters,
-                         q_idx, w, k_idx, scores, stride, *sel);
-    else
-      hipLaunchKernelGGL(k_index_fp8_reg<false>, grid, dim3(kIdxWaves * 64), 0, s, m, T, k, iters,
-                         q_idx, w, k_idx, scores, stride, none);
-  } else if (sel)
+  if (sel) {
+    sel->slot_keys = per_wg;
+    sel->slot_words = 4 + (per_wg < kHist0Bins ? per_wg : kHist0Bins);
+  }
+  if (sel)
     hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
                        q_idx, w, k_idx, scores, stride, *sel);
   else

@@ -5,18 +5,16 @@
 
 namespace sga {
 
-// --- workspace utility -----------------------------------------------------
-hipError_t launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
-
 // --- indexer score pass ----------------------------------------------------
-// scores[t * stride + s] for s < n_t; hist0 (T x 4096, zeroed) optional.
+// scores[t * stride + s] for s < n_t.
 struct TopkWs;
-// With `sel` set, the indexer also builds the level-0 histogram (sel->hist0).
+// With `sel` set, the indexer also writes the level-0 histogram lists of the
+// top-k select (and records their slot geometry in *sel).
 hipError_t launch_index_f32(const SeqMeta &m, int T, int k, int HI, int DI, const float *q_idx,
                             const float *w, const float *k_idx, float *scores, int64_t stride,
-                            const TopkWs *sel, hipStream_t s);
+                            TopkWs *sel, hipStream_t s);
 hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx, const float *w,
-                            const uint8_t *k_idx, float *scores, int64_t stride, const TopkWs *sel,
+                            const uint8_t *k_idx, float *scores, int64_t stride, TopkWs *sel,
                             hipStream_t s);
 // Query-tiled FP8 scores for the query-row groups whose rows all name one
 // sequence (other groups are left untouched); used by launch_index_fp8.
@@ -25,20 +23,27 @@ hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_id
                                     hipStream_t s);
 
 // --- top-k select -----------------------------------------------------------
+// The level-0 histogram of a query (4096 bins of the top 12 key bits) arrives
+// as lists, one per producer workgroup ("slot") covering slot_keys positions.
+// Slot `slot` of query t starts at word t * list_q_stride + slot * slot_words
+// of `lists` (16-byte aligned): its entry count, then the entries
+// (bin << 20 | count) in descending bin order. No global atomics and no
+// pre-zeroed memory are involved; the scan kernel merges the lists.
+constexpr int kTopkMaxSlots = 4096;  // level-0 list slots one query may use
 struct TopkWs {
-  uint32_t *hist0;    // [T, 4096]  level-0 histogram (zeroed before the indexer)
-  uint32_t *hist1;    // [T, 1024]  level-1 histogram of bin b0 (zeroed with hist0)
-  uint2 *thr;         // [T]        (b0, count above bin b0)
-  uint32_t *counts;   // [T, nchunk]
-  uint2 *entries;     // [T, nchunk * kTopkChunk] (position, key)
-  int32_t nchunk;     // ceil(max_kv_len / kTopkChunk)
-  size_t zero_words;  // hist0 + hist1 words to clear before each selection
+  uint32_t *lists;        // [T, list_q_stride]
+  int32_t list_q_stride;  // words reserved per query
+  int32_t slot_keys;      // positions one slot covers (set by the producer's launcher)
+  int32_t slot_words;     // words per slot: 4 + at most 4096 entries (set by the producer's launcher)
+  uint2 *thr;             // [T]        (b0, count above bin b0)
+  uint32_t *counts;       // [T, nchunk]
+  uint2 *entries;         // [T, nchunk * kTopkChunk] (position, key)
+  int32_t nchunk;         // ceil(max_kv_len / kTopkChunk)
 };
 size_t topk_ws_bytes(int T, int max_kv_len);
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len);
 hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
-                             const TopkWs &w, hipStream_t s);
-hipError_t launch_topk_thr0(const SeqMeta &m, int T, int k, const TopkWs &w, hipStream_t s);
+                             TopkWs *w, hipStream_t s);
 hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
                             const TopkWs &w, int32_t *topk_idx, hipStream_t s);
 hipError_t launch_topk_final(const SeqMeta &m, int T, int k, const TopkWs &w, int32_t *topk_idx,

@@ -8,20 +8,21 @@
 //
 // Exact radix select on the order-preserving 32-bit key of each fp32 score,
 // most significant digit first (12 + 10 + 10 bits):
-//  1. level-0 histogram of key bits 31..20 (built by the indexer in the fused
-//     layer, or by k_topk_hist0);
-//  2. k_topk_thr0, one workgroup per query: the level-0 threshold bin b0 (the
-//     bin holding the k-th largest key) and the count of keys above it;
-//  3. k_topk_scan, many workgroups per query: compacts, in position order, the
-//     (position, key) pairs of its chunk whose digit is >= b0 (everything above
-//     b0 is certainly selected; bin b0 holds the threshold) and adds the
-//     level-1 histogram (key bits 19..10) of the bin-b0 keys;
-//  4. k_topk_final, one workgroup per query: takes the level-1 bin from that
-//     histogram, lists the pairs that share the top 22 bits of the threshold
-//     while staging all pairs in LDS, resolves the last 10 bits with a third
-//     histogram, giving the exact k-th key K* and how many ties at K* to take;
-//     an ordered pass then emits key > K* plus the first `take` ties, which are
-//     the lowest positions because chunks and their pairs are visited in
+//  1. level-0 histogram of key bits 31..20, as one list of nonzero bins per
+//     producer workgroup (written by the indexer in the fused layer, or by
+//     k_topk_hist0): no global atomics and nothing to clear beforehand;
+//  2. k_topk_scan, one workgroup per 4096 positions: merges the query's lists
+//     into the level-0 histogram (every workgroup of a query reaches the same
+//     result; the first publishes it), finds the threshold bin b0 (the bin
+//     holding the k-th largest key) and compacts, in position order, the
+//     (position, key) pairs of its chunk whose digit is >= b0 (everything
+//     above b0 is certainly selected; bin b0 holds the threshold);
+//  3. k_topk_final, one workgroup per query: stages all pairs in LDS while
+//     building the level-1 histogram (key bits 19..10) of bin b0, then the
+//     level-2 histogram of the pairs sharing the top 22 bits of the threshold,
+//     giving the exact k-th key K* and how many ties at K* to take; an ordered
+//     pass then emits key > K* plus the first `take` ties, which are the
+//     lowest positions because chunks and their pairs are visited in
 //     position order.
 // No atomics decide the output, so it is deterministic.
 
@@ -38,15 +39,10 @@ constexpr int kFinalBlock = 512;
 constexpr int kFinalCap = 12288;                     // pairs staged in LDS (96 KiB)
 constexpr int kMaxChunks = 1024;                     // max_kv_len <= 4M
 
-__global__ void k_zero_u32(uint32_t *p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
-}
-
 __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__restrict__ scores,
                                                     int64_t stride, TopkWs ws) {
   __shared__ uint32_t hist[kHist0Bins];
+  __shared__ uint32_t scratch[256 / 64 + 1];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
@@ -60,20 +56,7 @@ __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__re
     if (s < n) atomicAdd(&hist[score_key(row[s]) >> kHist0Shift], 1u);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kHist0Bins; i += 256) {
-    uint32_t c = hist[i];
-    if (c) atomicAdd(ws.hist0 + (size_t)t * kHist0Bins + i, c);
-  }
-}
-
-// One workgroup per query: level-0 threshold bin from the finished histogram.
-__global__ __launch_bounds__(256) void k_topk_thr0(SeqMeta m, int k, TopkWs ws) {
-  __shared__ uint32_t scratch[256 / 64 + 1];
-  const int t = blockIdx.x;
-  int64_t start;
-  const int n = query_candidates(m, t, &start);
-  if (n <= k) return;
-  publish_threshold0(ws, t, k, scratch, nullptr);
+  write_hist0_list<false>(hist, ws, t, blockIdx.x, scratch);
 }
 
 template <bool kVec>
@@ -81,8 +64,10 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
                                                           const float *__restrict__ scores,
                                                           int64_t stride, TopkWs ws,
                                                           int32_t *__restrict__ topk_idx) {
-  __shared__ uint32_t h1[kHist12Bins];
+  __shared__ uint32_t hist[kHist0Bins];
   __shared__ uint32_t scratch[kScanBlock / 64 + 1];
+  __shared__ int res[2];
+  __shared__ int floor_max;
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
@@ -112,8 +97,12 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) v[j] = p0 + j < n ? row[p0 + j] : 0.0f;
   }
-  const uint2 thr = ws.thr[t];
-  const int b0 = (int)thr.x;
+  // level-0 threshold of the query from its lists (every workgroup of the
+  // query derives the same b0; the first one publishes it for k_topk_final)
+  for (int i = threadIdx.x; i < kHist0Bins; i += kScanBlock) hist[i] = 0u;
+  uint32_t above0;
+  const int b0 = merge_lists_threshold<kScanBlock>(ws, t, n, k, hist, &floor_max, scratch, res, &above0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ws.thr[t] = make_uint2((uint32_t)b0, above0);
 
   uint32_t keys[kPerThread];
   uint32_t cnt = 0;
@@ -123,13 +112,6 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
     keys[j] = key;
     cnt += (p0 + j < n && (int)(key >> kHist0Shift) >= b0) ? 1u : 0u;
   }
-  // level-1 histogram (key bits 19..10) of this chunk's keys in bin b0
-  for (int i = threadIdx.x; i < kHist12Bins; i += kScanBlock) h1[i] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (p0 + j < n && (int)(keys[j] >> kHist0Shift) == b0)
-      atomicAdd(&h1[(keys[j] >> (kHist0Shift - 10)) & 1023u], 1u);
   uint32_t total;
   uint32_t off = block_exclusive_scan(cnt, scratch, &total);  // includes barriers
   uint2 *dst = ws.entries + ((size_t)t * ws.nchunk + blockIdx.x) * kTopkChunk;
@@ -137,11 +119,6 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
   for (int j = 0; j < kPerThread; ++j) {
     if (p0 + j < n && (int)(keys[j] >> kHist0Shift) >= b0)
       dst[off++] = make_uint2((uint32_t)(p0 + j), keys[j]);
-  }
-  uint32_t *g1 = ws.hist1 + (size_t)t * kHist12Bins;
-  for (int i = threadIdx.x; i < kHist12Bins; i += kScanBlock) {
-    const uint32_t c = h1[i];
-    if (c) atomicAdd(g1 + i, c);
   }
   if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunk + blockIdx.x] = total;
 }
@@ -157,17 +134,13 @@ __device__ __forceinline__ int chunk_of(const uint32_t *offs, int nch, uint32_t 
 }
 
 constexpr int kBatch = 8;    // independent loads in flight per thread
-constexpr int kL2Cap = 2048;  // pairs sharing the top 22 key bits of the threshold
-
 __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, TopkWs ws,
                                                             int32_t *__restrict__ topk_idx) {
   extern __shared__ uint2 pairs[];  // kFinalCap entries
   __shared__ uint32_t hist[kHist12Bins];
   __shared__ uint32_t offs[kMaxChunks + 1];
-  __shared__ uint32_t l2keys[kL2Cap];
   __shared__ uint32_t scratch[kFinalBlock / 64 + 1];
   __shared__ int res[2];
-  __shared__ uint32_t l2n;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   int64_t start;
@@ -175,28 +148,23 @@ __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, To
   if (n <= k) return;
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
   const uint32_t *cnts = ws.counts + (size_t)t * ws.nchunk;
-  // chunk counts (<= 2 per thread), the level-1 histogram and the level-0 result
+  // chunk counts (<= 2 per thread) and the level-0 result
   const uint32_t c_a = 2 * tid < nch ? cnts[2 * tid] : 0u;
   const uint32_t c_b = 2 * tid + 1 < nch ? cnts[2 * tid + 1] : 0u;
-  const uint32_t *h1 = ws.hist1 + (size_t)t * kHist12Bins;
-  for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = h1[i];
+  for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
   const uint2 thr = ws.thr[t];
   const uint32_t b0 = thr.x;
   uint32_t want = (uint32_t)k - thr.y;
-  if (tid == 0) l2n = 0u;
   __syncthreads();
   uint32_t total;
   const uint32_t ex = block_exclusive_scan(c_a + c_b, scratch, &total);
   if (2 * tid < nch) offs[2 * tid] = ex;
   if (2 * tid + 1 < nch) offs[2 * tid + 1] = ex + c_a;
   if (tid == 0) offs[nch] = total;
-  uint32_t above1;
-  const int b1 = find_threshold_bin<kHist12Bins>(hist, want, &above1, scratch, res);
-  want -= above1;
-  const uint32_t prefix22 = (b0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
+  __syncthreads();
 
-  // stage the pairs in position order: a group of threads per chunk, no search;
-  // pairs that share the top 22 bits of K* are also listed for level 2
+  // stage the pairs in position order (a group of threads per chunk, no
+  // search) and build the level-1 histogram (key bits 19..10) of bin b0
   const uint2 *src = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
   const bool staged = total <= (uint32_t)kFinalCap;
   int gsz = kFinalBlock;
@@ -221,29 +189,28 @@ __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, To
           const uint32_t i = i0 + u * gsz;
           if (i < cnt) {
             if (staged) pairs[offs[c] + i] = v[u];
-            if ((v[u].y >> 10) == prefix22) {
-              const uint32_t slot = atomicAdd(&l2n, 1u);
-              if (slot < (uint32_t)kL2Cap) l2keys[slot] = v[u].y;
-            }
+            if ((v[u].y >> kHist0Shift) == b0) atomicAdd(&hist[(v[u].y >> 10) & 1023u], 1u);
           }
         }
       }
     }
   }
   __syncthreads();
-  // level 2: the last 10 bits among the listed pairs
+  uint32_t above1;
+  const int b1 = find_threshold_bin<kHist12Bins>(hist, want, &above1, scratch, res);
+  want -= above1;
+  const uint32_t prefix22 = (b0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
+  auto pair_at = [&](uint32_t f) -> uint2 {
+    if (staged) return pairs[f];
+    const int c = chunk_of(offs, nch, f);
+    return src[(size_t)c * kTopkChunk + (f - offs[c])];
+  };
+  // level 2: the last 10 bits among the pairs that share the top 22 bits
   for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
   __syncthreads();
-  const uint32_t nl2 = l2n;
-  if (nl2 <= (uint32_t)kL2Cap) {
-    for (uint32_t i = tid; i < nl2; i += kFinalBlock) atomicAdd(&hist[l2keys[i] & 1023u], 1u);
-  } else {
-    // more than kL2Cap pairs share 22 bits: histogram them from the pair list
-    for (uint32_t f = tid; f < total; f += kFinalBlock) {
-      const int c = chunk_of(offs, nch, f);
-      const uint32_t key = src[(size_t)c * kTopkChunk + (f - offs[c])].y;
-      if ((key >> 10) == prefix22) atomicAdd(&hist[key & 1023u], 1u);
-    }
+  for (uint32_t f = tid; f < total; f += kFinalBlock) {
+    const uint32_t key = pair_at(f).y;
+    if ((key >> 10) == prefix22) atomicAdd(&hist[key & 1023u], 1u);
   }
   __syncthreads();
   uint32_t above2;
@@ -252,11 +219,6 @@ __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, To
   const uint32_t kstar = (prefix22 << 10) | (uint32_t)b2;  // the exact k-th largest key
   const uint32_t take = want;                                 // ties at kstar to keep
 
-  auto pair_at = [&](uint32_t f) -> uint2 {
-    if (staged) return pairs[f];
-    const int c = chunk_of(offs, nch, f);
-    return src[(size_t)c * kTopkChunk + (f - offs[c])];
-  };
   // ordered emission: each thread owns a contiguous run of pairs
   const uint32_t seg = (total + kFinalBlock - 1) / kFinalBlock;
   const uint32_t s0 = min(total, tid * seg), s1 = min(total, s0 + seg);
@@ -287,30 +249,31 @@ __global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, To
 
 }  // namespace
 
-hipError_t launch_zero_u32(uint32_t *p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// list geometry: at most ceil(n / 256) + 1 slots per query (the smallest
+// producer slot covers 256 positions); a slot of K positions takes
+// 4 + min(K, 4096) words, so a query needs at most
+// max_kv_len + 8192 + 4 * slots words (one partly used slot of at most 8192
+// positions beyond max_kv_len)
+static size_t list_slots(int max_kv_len) { return ((size_t)max_kv_len + 255) / 256 + 1; }
+static size_t list_q_stride(int max_kv_len) {
+  return (((size_t)max_kv_len + 8192 + 4 * list_slots(max_kv_len)) + 3) / 4 * 4;
+}
 
 size_t topk_ws_bytes(int T, int max_kv_len) {
   size_t nch = ((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk;
-  return align256((size_t)T * (kHist0Bins + kHist12Bins) * 4) + align256((size_t)T * sizeof(uint2)) +
+  return align256((size_t)T * list_q_stride(max_kv_len) * 4) + align256((size_t)T * sizeof(uint2)) +
          align256((size_t)T * nch * 4) + align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
 }
 
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
-  TopkWs w;
+  TopkWs w{};
   w.nchunk = (int32_t)(((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk);
+  w.list_q_stride = (int32_t)list_q_stride(max_kv_len);
   char *p = (char *)ws;
-  w.hist0 = (uint32_t *)p;
-  w.hist1 = w.hist0 + (size_t)T * kHist0Bins;
-  w.zero_words = (size_t)T * (kHist0Bins + kHist12Bins);
-  p += align256((size_t)T * (kHist0Bins + kHist12Bins) * 4);
+  w.lists = (uint32_t *)p;
+  p += align256((size_t)T * w.list_q_stride * 4);
   w.thr = (uint2 *)p;
   p += align256((size_t)T * sizeof(uint2));
   w.counts = (uint32_t *)p;
@@ -320,22 +283,20 @@ TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
 }
 
 hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
-                             const TopkWs &w, hipStream_t s) {
+                             TopkWs *w, hipStream_t s) {
+  w->slot_keys = kTopkChunk;
+  w->slot_words = 4 + (kTopkChunk < kHist0Bins ? kTopkChunk : kHist0Bins);
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   dim3 grid((m.max_kv_len + kTopkChunk - 1) / kTopkChunk, T);
-  hipLaunchKernelGGL(k_topk_hist0, grid, dim3(256), 0, s, m, scores, stride, w);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_thr0(const SeqMeta &m, int T, int k, const TopkWs &w, hipStream_t s) {
-  if (T == 0 || m.max_kv_len <= k) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_thr0, dim3(T), dim3(256), 0, s, m, k, w);
+  hipLaunchKernelGGL(k_topk_hist0, grid, dim3(256), 0, s, m, scores, stride, *w);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
                             const TopkWs &w, int32_t *topk_idx, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (m.max_kv_len > k && (w.slot_keys <= 0 || (m.max_kv_len + w.slot_keys - 1) / w.slot_keys > kTopkMaxSlots))
+    return hipErrorInvalidValue;  // level-0 lists missing or with too many slots
   int nch = m.max_kv_len > 0 ? (m.max_kv_len + kTopkChunk - 1) / kTopkChunk : 1;
   dim3 grid(nch, T);
   const bool vec = (stride % 4 == 0) && (((uintptr_t)scores & 15) == 0);

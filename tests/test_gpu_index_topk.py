@@ -134,3 +134,16 @@ def test_index_scores_prefill_single_sequence_chunk():
                        precision="bf16", seed=42, device="cuda")
     say("case prefill index scores, one sequence")
     _check_scores(case, [0, 1, 17, 100, 150, 199])
+
+
+def test_topk_threshold_deep_in_wide_histograms():
+    # scores spread over hundreds of level-0 bins per 4096-position chunk and
+    # k near n / 2: the threshold lies far below the 15 highest bins of every
+    # chunk's list, so the select must read the lists in full
+    g = torch.Generator().manual_seed(3)
+    rows = []
+    for n in (5000, 9000, 20000):
+        x = torch.randn(n, generator=g) * torch.exp(3 * torch.randn(n, generator=g))
+        rows.append(x.tolist())
+    _check_topk(rows, 2048, "wide histograms, k ~ n/2 and below")
+    _check_topk([r[:4100] for r in rows], 2048, "wide histograms, k = n/2")
