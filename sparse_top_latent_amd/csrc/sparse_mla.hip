@@ -397,10 +397,11 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, uint16_t *__restri
 //
 // 8 waves: wave w serves heads 16 (w % 4) .. 16 (w % 4) + 15 for the tiles of
 // its set (w / 4): set 0 takes tiles 0 and 2, set 1 tiles 1 and 3, each with
-// its own running max, sum and output accumulator. Every tile of the split is
-// gathered up front (the set issues its own two tiles), so the second pair of
-// tiles streams in while the first pair is computed. At the end set 1 hands
-// its state to set 0 through LDS and set 0 merges and writes the partial.
+// its own running max, sum and output accumulator. Each set gathers its first
+// tile, and once the first pair has landed issues its second tile, which
+// streams in while the first pair is computed. At the end the sets swap half
+// of their accumulators through LDS and each merges and writes half of the
+// partial.
 // --------------------------------------------------------------------------
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
@@ -465,10 +466,8 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
 
   // gather: the set's 256 threads copy its tiles set and set + 2 (tiles past
-  // ntiles read the zero block, so every thread issues 2 x kBfDma copies)
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int tt = set + 2 * u;
+  // ntiles read the zero block, so every thread issues kBfDma copies a tile)
+  auto issue_tile = [&](int tt) {
     unsigned char *tbase = smem + tt * kTileBytes;
     int64_t gr[kBfDma];
 #pragma unroll
@@ -483,7 +482,8 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
                                    : (const void *)g_zero16;
       dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
     }
-  }
+  };
+  issue_tile(set);
 
   v4f acc[kCt];
 #pragma unroll
@@ -497,8 +497,10 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
 
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (u == 0) wait_vmcnt<kBfDma>(); else wait_vmcnt<0>();
+    wait_vmcnt<0>();
     barrier_lds();  // tiles 2u and 2u + 1 have landed
+    // the second pair of tiles streams in while the first pair is computed
+    if (u == 0) issue_tile(set + 2);
     const int tt = set + 2 * u;
     if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
     const unsigned char *tile = smem + tt * kTileBytes;
@@ -558,32 +560,43 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     pv_block<7>(base, pb, acc);
   }
 
-  // merge the two sets: set 1 -> LDS -> set 0 (the tile area is free now)
+  // merge the two sets through LDS (the tile area is free now): set 0 finishes
+  // channel tiles 0..15 and set 1 channel tiles 16..31, each with the other
+  // set's half of the accumulators
   barrier_lds();
-  v4f *xch = (v4f *)smem;                           // [hg][ct][lane]
-  float2 *mlx = (float2 *)(smem + 4 * kCt * 64 * 16);  // [hg][lane]
-  if (set == 1) {
+  v4f *xch = (v4f *)smem;                              // [hg][ct][lane]
+  float2 *mlx = (float2 *)(smem + 4 * kCt * 64 * 16);  // [set][hg][lane]
+  // (register indices stay compile-time constants: one branch per set)
+  if (set == 0) {
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) xch[(hg * kCt + ct) * 64 + lane] = acc[ct];
-    mlx[hg * 64 + lane] = make_float2(m_run, l_run);
+    for (int ct = kCt / 2; ct < kCt; ++ct) xch[(hg * kCt + ct) * 64 + lane] = acc[ct];
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < kCt / 2; ++ct) xch[(hg * kCt + ct) * 64 + lane] = acc[ct];
   }
+  mlx[(set * 4 + hg) * 64 + lane] = make_float2(m_run, l_run);
   barrier_lds();
-  if (set == 1) return;
-  const float2 other = mlx[hg * 64 + lane];
+  const float2 other = mlx[((1 - set) * 4 + hg) * 64 + lane];
   const float m = fmaxf(m_run, other.x);
   const float sa = m > -INFINITY ? exp2f(m_run - m) : 0.0f;
   const float sb = m > -INFINITY ? exp2f(other.x - m) : 0.0f;
   const float l = l_run * sa + other.y * sb;
   uint2 *pdst = (uint2 *)opart + ((((size_t)t * S + split) * 4 + hg) * kCt) * 64 + lane;
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
+  auto finish = [&](int ct) {
     const v4f b = xch[(hg * kCt + ct) * 64 + lane];
     const v4f o = acc[ct] * sa + b * sb;
     const uint32_t lo = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
     const uint32_t hi = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
     pdst[ct * 64] = make_uint2(lo, hi);
+  };
+  if (set == 0) {
+#pragma unroll
+    for (int ct = 0; ct < kCt / 2; ++ct) finish(ct);
+  } else {
+#pragma unroll
+    for (int ct = kCt / 2; ct < kCt; ++ct) finish(ct);
   }
-  if (g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m, l);
+  if (set == 0 && g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m, l);
 }
 
 constexpr int kMaxSplits = 2048 / kMlaRowsPerSplit;
