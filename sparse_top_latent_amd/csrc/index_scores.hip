@@ -11,12 +11,12 @@
 //  * k_index_f32: generic fp32 path, one thread per (query, key).
 //  * k_index_fp8: MI355X path for 64 index heads x 128 dims in E4M3FN, one
 //    query per workgroup row of the grid (decode). Each wave keeps the
-//    query's 64 x 128 index matrix in registers as four 16 x 128 MFMA A tiles
-//    and streams its own range of keys through LDS (LDS-DMA, two 8 KiB tiles
-//    in flight). One 16x16x128 FP8 MFMA per (head tile, 16-key tile) gives 16
-//    heads x 16 keys; the ReLU and the weighted head sum run on the
-//    accumulators, and lane-swap additions leave one finished score per lane,
-//    stored coalesced.
+//    query's 64 x 128 index matrix in registers as four 16 x 128 MFMA A tiles;
+//    the workgroup streams one range of keys through an LDS ring (LDS-DMA,
+//    three 8 KiB tiles in flight). One 16x16x128 FP8 MFMA per (head tile,
+//    16-key tile) gives 16 heads x 16 keys; the ReLU and the weighted head
+//    sum run on the accumulators, and lane-swap additions leave the finished
+//    score of each key in 16 lanes, stored coalesced.
 //  * k_index_fp8_pf (index_prefill.hip): the same arithmetic for runs of
 //    query rows of one sequence (prefill): the waves of a workgroup share
 //    each LDS key tile.
@@ -78,137 +78,138 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
 }
 
 // --------------------------------------------------------------------------
-// FP8 MFMA path (HI = 64, DI = 128)
+// FP8 MFMA path (HI = 64, DI = 128), one query per grid row (decode)
 //
-// Each wave streams its own contiguous range of keys. 64-key tiles (8 KiB)
-// are copied global -> LDS with LDS-DMA (global_load_lds_dwordx4): every DMA
-// instruction moves 1 KiB of consecutive bytes, and two tiles per wave are in
-// flight. The MFMA B operand is then read from LDS in the layout the
-// 16x16x128 FP8 MFMA wants. Within a 128-byte key row the 32-byte segments are
-// XOR-swizzled by key so that the 16 keys read by one instruction spread over
-// the LDS banks; the swizzle is applied on the DMA source side.
+// The 4 waves of a workgroup stream one contiguous key range of the query
+// through a ring of kIdxRing 8 KiB tiles (64 keys) in LDS. Every thread copies
+// two 16-byte pieces of each tile with LDS-DMA (global_load_lds_dwordx4), so
+// kIdxRing - 1 tiles are in flight while the workgroup computes. Within a
+// 128-byte key row the 16-byte pieces are XOR-swizzled by key (applied on the
+// DMA source side) so that the B-operand reads spread over the LDS banks.
+// Wave w scores keys 16 w .. 16 w + 15 of each tile with four 16x16x128 MFMAs
+// (one per 16-head tile). One barrier per tile both publishes the tile and
+// frees the buffer that the next copy overwrites.
 // --------------------------------------------------------------------------
-constexpr int kIdxWaves = 4;                 // waves per workgroup
-constexpr int kKeyLoadPolicy = 2;            // nontemporal (streamed) key copies
-constexpr int kIdxDmaPerTile = kIdxTileBytes / (64 * 16);  // 8 DMA issues per lane
-constexpr int kIdxBufs = 2;                  // tiles in flight per wave
-constexpr size_t kIdxSmem = (size_t)kIdxWaves * kIdxBufs * kIdxTileBytes;
+constexpr int kIdxWaves = 4;       // waves per workgroup
+constexpr int kKeyLoadPolicy = 2;  // nontemporal (streamed) key copies
+constexpr int kIdxRing = 4;        // tiles in the LDS ring
 
 // LDS atomic add without a return value, issued as inline asm so that the
-// compiler does not make it wait for the wave's in-flight LDS-DMA copies
-// (it cannot tell that the histogram and the DMA buffers do not overlap).
-// It has no result register; later lgkmcnt waits cover its completion.
+// compiler does not make it wait for the in-flight LDS-DMA copies (it cannot
+// tell that the histogram and the DMA buffers do not overlap). It has no
+// result register; later lgkmcnt waits cover its completion.
 __device__ __forceinline__ void lds_add_u32(uint32_t *p, uint32_t v) {
   const uint32_t addr =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)p;
   asm volatile("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-// Global byte offset of the 16-byte piece that lane `lane` copies with DMA
-// issue i, relative to row 8 i of the tile: piece 64 i + lane of the LDS tile
-// holds key row r = 8 i + lane / 8 and global piece (lane % 8) ^ key_swz(r);
-// key_swz(r) only depends on the lane and on the parity of i.
-__device__ __forceinline__ int key_dma_offset(int lane, int i) {
-  const int r = 8 * i + (lane >> 3);
-  return (lane >> 3) * 128 + (((lane & 7) ^ key_swz(r)) << 4);
-}
-
-// Issue the DMA of one 64-key tile (keys base.., clamped to n-1) into `buf`.
-__device__ __forceinline__ void issue_key_tile(unsigned char *buf, const uint8_t *__restrict__ k_idx,
-                                               int64_t start, int n, int base, int lane,
-                                               const int (&lane_off)[2]) {
-  if (base + kIdxTileKeys <= n) {
-    const uint8_t *src = k_idx + (start + base) * 128;
-#pragma unroll
-    for (int i = 0; i < kIdxDmaPerTile; ++i)
-      __builtin_amdgcn_global_load_lds(src + i * 1024 + lane_off[i & 1], (lds_void *)(buf + i * 1024),
-                                       16, 0, kKeyLoadPolicy);
-  } else {
-    // sequence tail: rows past the end repeat the last key (their scores are dropped)
-#pragma unroll
-    for (int i = 0; i < kIdxDmaPerTile; ++i) {
-      const int r = i * 8 + (lane >> 3);
-      int key = base + r;
-      key = key < n ? key : n - 1;
-      const uint8_t *src = k_idx + (start + key) * 128 + (lane_off[i & 1] & 127);
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + i * 1024), 16, 0, kKeyLoadPolicy);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  // s_waitcnt needs an immediate: dispatch n = 0 .. N to a constant wait
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmcnt<N>();
+      return;
     }
+    wait_vmcnt_upto<N - 1>(n);
+  } else {
+    wait_vmcnt<0>();
   }
 }
 
-template <bool kHist>
-__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int k, int iters,
+template <bool kHist, int kR>
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int tiles_per_wg,
                                                               const uint8_t *__restrict__ q_idx,
                                                               const float *__restrict__ w,
                                                               const uint8_t *__restrict__ k_idx,
                                                               float *__restrict__ scores,
                                                               int64_t stride, TopkWs sel) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
+  // explicit waits below instead of draining every DMA before each read
+  extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   // level-0 histogram with two 16-bit bins per word (a workgroup scores at most
-  // 4 x 32 x 64 = 8192 keys, so a bin cannot overflow)
+  // 128 x 64 = 8192 keys, so a bin cannot overflow)
   __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
   __shared__ uint32_t scratch[kIdxWaves + 1];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
-  const int wave_keys = iters * kIdxTileKeys;
-  const int chunk0 = blockIdx.x * kIdxWaves * wave_keys;
-  if (chunk0 >= n) return;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform loop bounds
+  const int c0 = blockIdx.x * tiles_per_wg * kIdxTileKeys;
+  if (c0 >= n) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform loop bounds
   const int kg = lane >> 4, c16 = lane & 15;
-
-  // A tiles: head (ht*16 + c16), bytes [32*kg, 32*kg+32) of its 128-byte row
-  v8i a[1][4];
-  float wv[1][16];
+  // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row;
+  // accumulator row r of this lane is head ht*16 + 4 kg + r
+  v8i a[4];
+  float wv[16];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
     const v4i lo = src[0], hi = src[1];
-    a[0][ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    // accumulator row r of this lane is head ht*16 + 4*kg + r
+    a[ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) wv[0][ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
+    for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
   }
   if (kHist) {
-    for (int i = threadIdx.x; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
+    for (int i = tid; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
     __syncthreads();
   }
-
-  const int wbase = chunk0 + wave * wave_keys;
-  const int nit = wbase < n ? min(iters, (n - wbase + kIdxTileKeys - 1) / kIdxTileKeys) : 0;
-  unsigned char *mybuf = smem + (size_t)wave * kIdxBufs * kIdxTileBytes;
-  const int lane_off[2] = {key_dma_offset(lane, 0), key_dma_offset(lane, 1)};
-  // the q/w loads above must have landed before the DMA counting starts
-  wait_vmcnt<0>();
-  if (nit > 0) issue_key_tile(mybuf, k_idx, start, n, wbase, lane, lane_off);
-  if (nit > 1) issue_key_tile(mybuf + kIdxTileBytes, k_idx, start, n, wbase + kIdxTileKeys, lane, lane_off);
+  const int ntiles = min(tiles_per_wg, (n - c0 + kIdxTileKeys - 1) / kIdxTileKeys);
+  // piece p = u * 256 + tid of a tile holds key row p / 8 and its swizzled
+  // 16-byte piece; rows past the sequence repeat its last key (their scores
+  // are dropped)
+  auto issue = [&](int i) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = u * 256 + tid;
+      const int r = p >> 3;
+      const int key = min(c0 + i * kIdxTileKeys + r, n - 1);
+      const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
+      __builtin_amdgcn_global_load_lds(
+          src, (lds_void *)(ring + (i % kR) * kIdxTileBytes + (u * 256 + wave * 64) * 16), 16, 0,
+          kKeyLoadPolicy);
+    }
+  };
+  wait_vmcnt<0>();  // the query loads have landed; from here vmcnt counts copies and stores
+  for (int i = 0; i < kR - 1; ++i)
+    if (i < ntiles) issue(i);
   float *srow = scores + t * stride;
-  for (int it = 0; it < nit; ++it) {
-    // Outstanding vector-memory ops issued after tile `it`: the score store of
-    // iteration it-1 (if any) and the DMA of tile it+1 (if any). They retire in
-    // order, so waiting down to that many guarantees tile `it` has landed.
-    const int later = (it > 0 ? 1 : 0) + (it + 1 < nit ? kIdxDmaPerTile : 0);
-    if (later == kIdxDmaPerTile + 1) wait_vmcnt<kIdxDmaPerTile + 1>();
-    else if (later == kIdxDmaPerTile) wait_vmcnt<kIdxDmaPerTile>();
-    else if (later == 1) wait_vmcnt<1>();
-    else wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    const unsigned char *tb = mybuf + (it & 1) * kIdxTileBytes;
-    float part[1][4];
-    score_tiles<1>(a, [&](int kt) { return load_key_operand(tb, kt, kg, c16); }, wv, part);
-    const float keep = tile_scores(part[0]);
-    const int s = wbase + it * kIdxTileKeys + lane;
-    // the tile buffer is free once this iteration's LDS reads completed
+  for (int i = 0; i < ntiles; ++i) {
+    // tile i has landed once at most the copies of the tiles issued after it
+    // are outstanding (score stores issued in between only lengthen the wait)
+    wait_vmcnt_upto<2 * (kR - 2)>(2 * (min(ntiles - 1, i + kR - 2) - i));
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     asm volatile("" ::: "memory");
-    if (s < n) srow[s] = keep;
-    if (it + 2 < nit)
-      issue_key_tile(mybuf + (it & 1) * kIdxTileBytes, k_idx, start, n,
-                     wbase + (it + 2) * kIdxTileKeys, lane, lane_off);
-    if (kHist && s < n) {
-      const uint32_t bin = score_key(keep) >> kHist0Shift;
-      lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (i + kR - 1 < ntiles) issue(i + kR - 1);
+    const unsigned char *tb = ring + (i % kR) * kIdxTileBytes;
+    const v8i b = load_key_operand(tb, wave, kg, c16);
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // each head sum split over two accumulators so consecutive FMAs do not wait
+    float ev = 0.0f, od = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const v4f x = mfma_fp8(a[ht], b, zero);
+      ev = fmaf(fmaxf(x[0], 0.0f), wv[ht * 4 + 0], ev);
+      od = fmaf(fmaxf(x[1], 0.0f), wv[ht * 4 + 1], od);
+      ev = fmaf(fmaxf(x[2], 0.0f), wv[ht * 4 + 2], ev);
+      od = fmaf(fmaxf(x[3], 0.0f), wv[ht * 4 + 3], od);
+    }
+    // sum over the four lane groups that hold the same key: every lane ends
+    // with the score of key 16 wave + c16 (-0 becomes +0)
+    const float x = ev + od;
+    const float y = add_swapped(x, x, true);
+    const float keep = add_swapped(y, y, false) + 0.0f;
+    const int s = c0 + i * kIdxTileKeys + wave * 16 + lane;
+    if (lane < 16 && s < n) {
+      srow[s] = keep;
+      if (kHist) {
+        const uint32_t bin = score_key(keep) >> kHist0Shift;
+        lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
+      }
     }
   }
   if (kHist) {
@@ -220,9 +221,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
 }  // namespace
 
 int index_fp8_iters(int T, int max_kv_len) {
-  // aim for about eight 4-wave workgroups per CU over the whole batch
+  // aim for about two 4-wave workgroups per CU over the whole batch
   const int64_t keys = (int64_t)T * max_kv_len;
-  const int64_t per_iter = 2048LL * kIdxWaves * kIdxTileKeys;
+  const int64_t per_iter = 512LL * kIdxWaves * kIdxTileKeys;
   int64_t it = (keys + per_iter - 1) / per_iter;
   if (it < 2) it = 2;
   if (it > 32) it = 32;
@@ -258,10 +259,10 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void *)k_index_fp8<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIdxSmem);
-    (void)hipFuncSetAttribute((const void *)k_index_fp8<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kIdxSmem);
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxTileBytes);
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxTileBytes);
     (void)hipGetLastError();
     attr = true;
   }
@@ -281,11 +282,14 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     sel->slot_keys = per_wg;
     sel->slot_words = 4 + (per_wg < kHist0Bins ? per_wg : kHist0Bins);
   }
+  // one workgroup copies and scores kIdxWaves * iters tiles
+  const int tiles = kIdxWaves * iters;
+  const size_t smem = (size_t)kIdxRing * kIdxTileBytes;
   if (sel)
-    hipLaunchKernelGGL(k_index_fp8<true>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
+    hipLaunchKernelGGL((k_index_fp8<true, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, tiles,
                        q_idx, w, k_idx, scores, stride, *sel);
   else
-    hipLaunchKernelGGL(k_index_fp8<false>, grid, dim3(kIdxWaves * 64), kIdxSmem, s, m, T, k, iters,
+    hipLaunchKernelGGL((k_index_fp8<false, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, tiles,
                        q_idx, w, k_idx, scores, stride, none);
   return hipGetLastError();
 }
