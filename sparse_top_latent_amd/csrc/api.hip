@@ -296,9 +296,8 @@ sga_status sga_topk_select(const sga_problem *p, const float *scores, int32_t *t
     const SeqMeta m = meta_of(p);
     TopkWs w = topk_ws_carve(ws, p->num_q, p->max_kv_len);
     SGA_TRY(launched(launch_topk_hist0(m, p->num_q, scores, p->max_kv_len, &w, s), "hist0"));
-    SGA_TRY(launched(launch_topk_scan(m, p->num_q, p->topk, scores, p->max_kv_len, w, topk_idx, s),
-                     "topk scan"));
-    return launched(launch_topk_final(m, p->num_q, p->topk, w, topk_idx, s), "topk final");
+    return launched(launch_topk_select(m, p->num_q, p->topk, scores, p->max_kv_len, w, topk_idx, s),
+                    "topk select");
   } catch (...) {
     return fail(SGA_ERR_DEVICE, "internal error");
   }
@@ -361,8 +360,7 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
     if (prof) prof_mark(s, 0);
     SGA_TRY(run_index(p, plan, q_idx, w, k_idx, scores, stride, &tw, s));
     if (prof) prof_mark(s, 1);
-    SGA_TRY(launched(launch_topk_scan(m, T, p->topk, scores, stride, tw, idx, s), "topk scan"));
-    SGA_TRY(launched(launch_topk_final(m, T, p->topk, tw, idx, s), "topk final"));
+    SGA_TRY(launched(launch_topk_select(m, T, p->topk, scores, stride, tw, idx, s), "topk select"));
     if (prof) prof_mark(s, 2);
     MlaArgs a = mla_args(p, q, kv, kv_scale, idx, gate, out, lse);
     SGA_TRY(run_mla(a, plan, mws, s, prof));

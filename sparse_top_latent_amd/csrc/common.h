@@ -126,41 +126,43 @@ __device__ __forceinline__ float sigmoidf_exact_ends(float g) {
 }
 
 // ---------------------------------------------------------------------------
-// block-wide exclusive scan of one uint32 per thread (blockDim a multiple of 64)
-// `scratch` needs blockDim/64 + 1 words of LDS.
+// prefix sums
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
+// 16 lanes (DPP row_shr 1, 2, 4, 8), then the row totals carried with the
+// gfx9 row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3).
+// Lanes a DPP move has no source for add 0.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
+// Block-wide exclusive scan of one uint32 per thread (blockDim a multiple of
+// 64, at most 1024); *total receives the block sum. `scratch` needs
+// blockDim / 64 words of LDS. Two barriers; the second lets the caller reuse
+// `scratch` right away.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
                                                          uint32_t *total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  uint32_t inc = wave_inclusive_scan(v);
+  const uint32_t inc = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int i = 0; i < nw; ++i) {
-      uint32_t x = scratch[i];
-      scratch[i] = acc;
-      acc += x;
-    }
-    scratch[nw] = acc;
+  uint32_t base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t x = scratch[i];
+    base += i < wave ? x : 0u;
+    tot += x;
   }
+  *total = tot;
   __syncthreads();
-  uint32_t res = scratch[wave] + inc - v;
-  *total = scratch[nw];
-  __syncthreads();
-  return res;
+  return base + inc - v;
 }
 
 }  // namespace sga

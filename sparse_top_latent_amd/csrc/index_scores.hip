@@ -51,6 +51,7 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
+  if (want_hist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = n;
   const int base = blockIdx.x * kF32Block;
   if (base >= n) return;
   for (int i = threadIdx.x; i < HI * DI; i += kF32Block) qs[i] = q_idx[(size_t)t * HI * DI + i];
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
+  if (kHist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = n;
   const int c0 = blockIdx.x * tiles_per_wg * kIdxTileKeys;
   if (c0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63;

@@ -27,27 +27,28 @@ hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_id
 // as lists, one per producer workgroup ("slot") covering slot_keys positions.
 // Slot `slot` of query t starts at word t * list_q_stride + slot * slot_words
 // of `lists` (16-byte aligned): its entry count, then the entries
-// (bin << 20 | count) in descending bin order. No global atomics and no
-// pre-zeroed memory are involved; the scan kernel merges the lists.
+// (bin << 20 | count) in descending bin order. No global atomics build them
+// and nothing is cleared beforehand. A producer also records n_t in ncand[t]
+// (from its workgroup 0 of query t).
 constexpr int kTopkMaxSlots = 4096;  // level-0 list slots one query may use
 struct TopkWs {
   uint32_t *lists;        // [T, list_q_stride]
   int32_t list_q_stride;  // words reserved per query
   int32_t slot_keys;      // positions one slot covers (set by the producer's launcher)
   int32_t slot_words;     // words per slot: 4 + at most 4096 entries (set by the producer's launcher)
-  uint2 *thr;             // [T]        (b0, count above bin b0)
-  uint32_t *counts;       // [T, nchunk]
-  uint2 *entries;         // [T, nchunk * kTopkChunk] (position, key)
+  uint4 *thr;             // [T] (b0, keys above bin b0, candidates, 0)
+  int32_t *ncand;         // [T] candidate count n_t
+  uint2 *entries;         // [T, nchunk * kTopkChunk] candidates (position, key)
   int32_t nchunk;         // ceil(max_kv_len / kTopkChunk)
 };
 size_t topk_ws_bytes(int T, int max_kv_len);
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len);
 hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64_t stride,
                              TopkWs *w, hipStream_t s);
-hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
-                            const TopkWs &w, int32_t *topk_idx, hipStream_t s);
-hipError_t launch_topk_final(const SeqMeta &m, int T, int k, const TopkWs &w, int32_t *topk_idx,
-                             hipStream_t s);
+// Select (one workgroup per (slot, query)) and finish (one per query); needs
+// the lists and ncand from a producer launched earlier on the same stream.
+hipError_t launch_topk_select(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
+                              const TopkWs &w, int32_t *topk_idx, hipStream_t s);
 
 // --- sparse MLA + gate ---------------------------------------------------------
 struct MlaArgs {

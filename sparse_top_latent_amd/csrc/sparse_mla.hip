@@ -440,6 +440,22 @@ __device__ __forceinline__ void pv_block(const uint32_t (&base)[4], const v8bf &
   for (int i = 0; i < 4; ++i) acc[4 * kM + i] = mfma_bf16(cat_bf16(lo[i], hi[i]), pb, acc[4 * kM + i]);
 }
 
+// The same block with the compiler's transposed-read builtin, which it can
+// schedule freely; only usable where no global->LDS copy is outstanding.
+template <int kM>
+__device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int (&voff)[4], const v8bf &pb,
+                                           v4f (&acc)[kCt]) {
+  typedef __attribute__((address_space(3))) v4bf lds_v4bf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf *)(tile + voff[i] + kM * 128));
+    const v4bf hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4bf *)(tile + voff[i] + kM * 128 + 16 * kRowChunks * 16));
+    const v8bf va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    acc[4 * kM + i] = mfma_bf16(va, pb, acc[4 * kM + i]);
+  }
+}
+
 __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
                                                     float2 *__restrict__ ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -449,16 +465,19 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave & 3, set = wave >> 2, st = tid & 255;
   const int g = lane >> 4, c16 = lane & 15;
+  const int r0 = split * kMlaRowsPerSplit;
+  const int nrows = min(kMlaRowsPerSplit, a.k - r0);  // >= 1: one split per 128 selected rows
+  const int ntiles = (nrows + kTile - 1) / kTile;
+  // the selected positions are requested first (clamped, unconditional) so
+  // that their latency overlaps the sequence lookup
+  int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(tid & (kMlaRowsPerSplit - 1), nrows - 1)];
   int64_t start;
   const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
-  const int r0 = split * kMlaRowsPerSplit;
-  const int nrows = min(kMlaRowsPerSplit, a.k - r0);
-  const int ntiles = (nrows + kTile - 1) / kTile;
-  if (tid < kMlaRowsPerSplit) {
-    int32_t pos = tid < nrows ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
-    rows[tid] = (pos >= 0 && pos < L) ? start + pos : -1;
-  }
+  if (tid < kMlaRowsPerSplit) rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? start + pos : -1;
   __syncthreads();  // rows[] ready
+  // validity of the 128 rows as two wave-wide bit masks (rows past nrows are -1)
+  const uint64_t valid01 = __ballot(rows[lane] >= 0);
+  const uint64_t valid23 = __ballot(rows[64 + lane] >= 0);
   const int head = hg * 16 + c16;
   const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
   v8bf qreg[kKsteps];
@@ -504,22 +523,21 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     const int tt = set + 2 * u;
     if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
     const unsigned char *tile = smem + tt * kTileBytes;
-    v4f sv[2];
+    const uint32_t tvalid = (uint32_t)((tt < 2 ? valid01 : valid23) >> (32 * (tt & 1)));
+    if (tvalid == 0u) continue;  // no selected row in this tile (uniform)
+    // the two 16-row halves are independent accumulation chains, interleaved
+    // so that consecutive MFMAs do not wait on each other
+    v4f sv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      v4f sacc = {0.f, 0.f, 0.f, 0.f};
-      const int row = rt * 16 + c16;
+    for (int ks = 0; ks < kKsteps; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks)
-        sacc = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(row, 4 * ks + g) * 16)), qreg[ks], sacc);
-      sv[rt] = sacc;
-    }
+      for (int rt = 0; rt < 2; ++rt)
+        sv[rt] = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(rt * 16 + c16, 4 * ks + g) * 16)), qreg[ks], sv[rt]);
     float lg[8];
     float mt = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      int ri = tt * kTile + (j >> 2) * 16 + 4 * g + (j & 3);
-      bool ok = ri < nrows && rows[ri] >= 0;
+      const bool ok = (tvalid >> ((j >> 2) * 16 + 4 * g + (j & 3))) & 1u;
       lg[j] = ok ? sv[j >> 2][j & 3] * scale2 : -INFINITY;
       mt = fmaxf(mt, lg[j]);
     }
@@ -546,18 +564,33 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     v8bf pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-    const uint32_t tl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)tile;
-    uint32_t base[4];
+    int voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) base[i] = tl + (vr * kRowChunks + ((2 * i + q) ^ row_swz(vr))) * 16 + vsub;
-    pv_block<0>(base, pb, acc);
-    pv_block<1>(base, pb, acc);
-    pv_block<2>(base, pb, acc);
-    pv_block<3>(base, pb, acc);
-    pv_block<4>(base, pb, acc);
-    pv_block<5>(base, pb, acc);
-    pv_block<6>(base, pb, acc);
-    pv_block<7>(base, pb, acc);
+    for (int i = 0; i < 4; ++i) voff[i] = (vr * kRowChunks + ((2 * i + q) ^ row_swz(vr))) * 16 + vsub;
+    if (u == 0) {
+      // the second tile pair is still streaming into LDS: asm reads
+      const uint32_t tl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)tile;
+      uint32_t base[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[i] = tl + voff[i];
+      pv_block<0>(base, pb, acc);
+      pv_block<1>(base, pb, acc);
+      pv_block<2>(base, pb, acc);
+      pv_block<3>(base, pb, acc);
+      pv_block<4>(base, pb, acc);
+      pv_block<5>(base, pb, acc);
+      pv_block<6>(base, pb, acc);
+      pv_block<7>(base, pb, acc);
+    } else {
+      pv_block_b<0>(tile, voff, pb, acc);
+      pv_block_b<1>(tile, voff, pb, acc);
+      pv_block_b<2>(tile, voff, pb, acc);
+      pv_block_b<3>(tile, voff, pb, acc);
+      pv_block_b<4>(tile, voff, pb, acc);
+      pv_block_b<5>(tile, voff, pb, acc);
+      pv_block_b<6>(tile, voff, pb, acc);
+      pv_block_b<7>(tile, voff, pb, acc);
+    }
   }
 
   // merge the two sets through LDS (the tile area is free now): set 0 finishes

@@ -9,21 +9,24 @@
 // Exact radix select on the order-preserving 32-bit key of each fp32 score,
 // most significant digit first (12 + 10 + 10 bits):
 //  1. level-0 histogram of key bits 31..20, as one list of nonzero bins per
-//     producer workgroup (written by the indexer in the fused layer, or by
-//     k_topk_hist0): no global atomics and nothing to clear beforehand;
-//  2. k_topk_scan, one workgroup per 4096 positions: merges the query's lists
-//     into the level-0 histogram (every workgroup of a query reaches the same
-//     result; the first publishes it), finds the threshold bin b0 (the bin
-//     holding the k-th largest key) and compacts, in position order, the
-//     (position, key) pairs of its chunk whose digit is >= b0 (everything
-//     above b0 is certainly selected; bin b0 holds the threshold);
-//  3. k_topk_final, one workgroup per query: stages all pairs in LDS while
-//     building the level-1 histogram (key bits 19..10) of bin b0, then the
-//     level-2 histogram of the pairs sharing the top 22 bits of the threshold,
-//     giving the exact k-th key K* and how many ties at K* to take; an ordered
-//     pass then emits key > K* plus the first `take` ties, which are the
-//     lowest positions because chunks and their pairs are visited in
-//     position order.
+//     producer workgroup ("slot", written by the indexer in the fused layer,
+//     or by k_topk_hist0): no global atomics and nothing cleared beforehand.
+//     The producer also records the query's candidate count n_t.
+//  2. k_topk_select, one workgroup per (slot, query):
+//     a. merges the heads of the query's lists into the level-0 histogram and
+//        finds the threshold bin b0 (the bin holding the k-th largest key);
+//        every workgroup of a query reaches the same result;
+//     b. the same heads give each slot's number of keys with digit >= b0, so
+//        the workgroup knows where its candidates go in position order: it
+//        writes its (position, key) pairs with digit >= b0 straight to their
+//        final place in the query's candidate array.
+//  3. k_topk_finish, one workgroup per query, holds the candidates (at most a
+//     few thousand for k = 2048) in registers: the level-1 histogram (key bits
+//     19..10) of bin b0 and then the level-2 histogram of the pairs sharing the
+//     top 22 bits of the threshold give the exact k-th key K* and how many ties
+//     at K* to take; an ordered pass emits key > K* plus the first `take` ties,
+//     which are the lowest positions because the candidates are in position
+//     order.
 // No atomics decide the output, so it is deterministic.
 
 #include "kernels.h"
@@ -33,25 +36,27 @@ namespace sga {
 
 namespace {
 
-constexpr int kScanBlock = 256;
-constexpr int kPerThread = kTopkChunk / kScanBlock;  // 16 consecutive scores per thread
-constexpr int kFinalBlock = 512;
-constexpr int kFinalCap = 12288;                     // pairs staged in LDS (96 KiB)
-constexpr int kMaxChunks = 1024;                     // max_kv_len <= 4M
+constexpr int kSelBlock = 256;
+constexpr int kSelWaves = kSelBlock / 64;
+constexpr int kSelPer = 16;                        // consecutive scores per thread and batch
+constexpr int kSelBatch = kSelBlock * kSelPer;     // 4096 positions
+constexpr int kFinPer = 16;                        // candidates per thread and round of the last pass
+constexpr int kFinRound = kSelBlock * kFinPer;     // 4096 candidates
 
 __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__restrict__ scores,
                                                     int64_t stride, TopkWs ws) {
   __shared__ uint32_t hist[kHist0Bins];
-  __shared__ uint32_t scratch[256 / 64 + 1];
+  __shared__ uint32_t scratch[256 / 64];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ws.ncand[t] = n;
   const int c0 = blockIdx.x * kTopkChunk;
   if (c0 >= n) return;
   for (int i = threadIdx.x; i < kHist0Bins; i += 256) hist[i] = 0u;
   __syncthreads();
   const float *row = scores + t * stride;
-  for (int j = 0; j < kPerThread; ++j) {
+  for (int j = 0; j < kTopkChunk / 256; ++j) {
     int s = c0 + j * 256 + threadIdx.x;
     if (s < n) atomicAdd(&hist[score_key(row[s]) >> kHist0Shift], 1u);
   }
@@ -59,35 +64,17 @@ __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__re
   write_hist0_list<false>(hist, ws, t, blockIdx.x, scratch);
 }
 
+// kSelPer consecutive scores from position p on; positions at or past the end
+// of the row read its last element (their values are never used).
 template <bool kVec>
-__global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
-                                                          const float *__restrict__ scores,
-                                                          int64_t stride, TopkWs ws,
-                                                          int32_t *__restrict__ topk_idx) {
-  __shared__ uint32_t hist[kHist0Bins];
-  __shared__ uint32_t scratch[kScanBlock / 64 + 1];
-  __shared__ int res[2];
-  __shared__ int floor_max;
-  const int t = blockIdx.y;
-  int64_t start;
-  const int n = query_candidates(m, t, &start);
-  if (n <= k) {
-    // every candidate is kept: positions 0..n-1, then -1
-    if (blockIdx.x == 0)
-      for (int i = threadIdx.x; i < k; i += kScanBlock)
-        topk_idx[(size_t)t * k + i] = i < n ? i : -1;
-    return;
-  }
-  const int c0 = blockIdx.x * kTopkChunk;
-  if (c0 >= n) return;
-  // this thread's 16 consecutive scores, requested before the threshold search
-  const float *row = scores + t * stride;
-  const int p0 = c0 + threadIdx.x * kPerThread;
-  float v[kPerThread];
-  if (kVec && p0 + kPerThread <= n) {
+__device__ __forceinline__ void load_scores(const float *row, int64_t stride, int64_t p, float (&v)[kSelPer]) {
+  if (kVec) {
+    // stride % 4 == 0 and p % 4 == 0: a float4 either lies inside the row or
+    // starts at or past its end
 #pragma unroll
-    for (int q = 0; q < kPerThread / 4; ++q) {
-      const float4 x = *(const float4 *)(row + p0 + 4 * q);
+    for (int q = 0; q < kSelPer / 4; ++q) {
+      const int64_t a = p + 4 * q;
+      const float4 x = *(const float4 *)(row + (a < stride - 4 ? a : stride - 4));
       v[4 * q] = x.x;
       v[4 * q + 1] = x.y;
       v[4 * q + 2] = x.z;
@@ -95,155 +82,340 @@ __global__ __launch_bounds__(kScanBlock) void k_topk_scan(SeqMeta m, int k,
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) v[j] = p0 + j < n ? row[p0 + j] : 0.0f;
+    for (int j = 0; j < kSelPer; ++j) v[j] = row[p + j < stride ? p + j : stride - 1];
   }
-  // level-0 threshold of the query from its lists (every workgroup of the
-  // query derives the same b0; the first one publishes it for k_topk_final)
-  for (int i = threadIdx.x; i < kHist0Bins; i += kScanBlock) hist[i] = 0u;
-  uint32_t above0;
-  const int b0 = merge_lists_threshold<kScanBlock>(ws, t, n, k, hist, &floor_max, scratch, res, &above0);
-  if (blockIdx.x == 0 && threadIdx.x == 0) ws.thr[t] = make_uint2((uint32_t)b0, above0);
-
-  uint32_t keys[kPerThread];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const uint32_t key = score_key(v[j]);
-    keys[j] = key;
-    cnt += (p0 + j < n && (int)(key >> kHist0Shift) >= b0) ? 1u : 0u;
-  }
-  uint32_t total;
-  uint32_t off = block_exclusive_scan(cnt, scratch, &total);  // includes barriers
-  uint2 *dst = ws.entries + ((size_t)t * ws.nchunk + blockIdx.x) * kTopkChunk;
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    if (p0 + j < n && (int)(keys[j] >> kHist0Shift) >= b0)
-      dst[off++] = make_uint2((uint32_t)(p0 + j), keys[j]);
-  }
-  if (threadIdx.x == 0) ws.counts[(size_t)t * ws.nchunk + blockIdx.x] = total;
 }
 
-// Chunk holding flat pair index f (offs ascending, offs[0] = 0, offs[nch] = total > f).
-__device__ __forceinline__ int chunk_of(const uint32_t *offs, int nch, uint32_t f) {
-  int lo = 0, hi = nch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (offs[mid] <= f) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+// Sum of the counts of the list entries with bin >= b0 among the first `cnt`
+// entries of a list (entries in descending bin order).
+__device__ __forceinline__ uint32_t head_count_ge(const uint32_t (&wd)[16], uint32_t b0) {
+  const uint32_t cnt = wd[0];
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 1; i < 16; ++i)
+    if ((uint32_t)i <= cnt && (wd[i] >> 20) >= b0) c += wd[i] & 0xFFFFFu;
+  return c;
 }
 
-constexpr int kBatch = 8;    // independent loads in flight per thread
-__global__ __launch_bounds__(kFinalBlock) void k_topk_final(SeqMeta m, int k, TopkWs ws,
-                                                            int32_t *__restrict__ topk_idx) {
-  extern __shared__ uint2 pairs[];  // kFinalCap entries
-  __shared__ uint32_t hist[kHist12Bins];
-  __shared__ uint32_t offs[kMaxChunks + 1];
-  __shared__ uint32_t scratch[kFinalBlock / 64 + 1];
+__device__ __forceinline__ uint32_t list_count_ge(const uint32_t *l, uint32_t b0) {
+  const uint32_t cnt = l[0];
+  uint32_t c = 0;
+  for (uint32_t i = 1; i <= cnt; ++i) {
+    const uint32_t e = l[i];
+    if ((e >> 20) < b0) break;
+    c += e & 0xFFFFFu;
+  }
+  return c;
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kSelBlock) void k_topk_select(SeqMeta m, int k,
+                                                           const float *__restrict__ scores,
+                                                           int64_t stride, TopkWs ws,
+                                                           int32_t *__restrict__ topk_idx) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHist0Bins];  // level 0; levels 1 and 2 in the last workgroup
+  __shared__ uint32_t scratch[kSelWaves];
+  __shared__ int res[2];
+  __shared__ int floor_max;
+  __shared__ uint32_t s_base;
+  __shared__ uint32_t s_misc[2];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.y, slot = blockIdx.x;
+  const int skeys = ws.slot_keys;
+  const int max_slots = gridDim.x;
+  const float *row = scores + (int64_t)t * stride;
+  const uint32_t *lbase = ws.lists + (size_t)t * ws.list_q_stride;
+  const int64_t c0 = (int64_t)slot * skeys;
+  if (m.max_kv_len <= k) {
+    // every query keeps all its candidates (no lists were needed)
+    int64_t start;
+    const int n = query_candidates(m, t, &start);
+    if (slot == 0)
+      for (int i = tid; i < k; i += kSelBlock) topk_idx[(size_t)t * k + i] = i < n ? i : -1;
+    return;
+  }
+
+  // Requested first, before anything waits on the sequence lookup: the head
+  // (count and 15 highest bins) of list `tid` and this thread's first scores.
+  const int hs = tid < max_slots ? tid : max_slots - 1;
+  const uint4 *hp = (const uint4 *)(lbase + (size_t)hs * ws.slot_words);
+  const uint4 h0 = hp[0], h1 = hp[1], h2 = hp[2], h3 = hp[3];
+  float v[kSelPer];
+  load_scores<kVec>(row, stride, c0 + tid * kSelPer, v);
+
+  const int n = ws.ncand[t];
+  if (n <= k) {
+    // every candidate is kept: positions 0..n-1, then -1 (no candidates for
+    // k_topk_finish)
+    if (slot == 0) {
+      for (int i = tid; i < k; i += kSelBlock) topk_idx[(size_t)t * k + i] = i < n ? i : -1;
+      if (tid == 0) ws.thr[t] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
+  if (c0 >= n) return;
+  const int nslots = (n + skeys - 1) / skeys;  // lists written for this query
+
+  const uint32_t wd[16] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w,
+                           h2.x, h2.y, h2.z, h2.w, h3.x, h3.y, h3.z, h3.w};
+  uint32_t ub0, above0, total;  // threshold bin, keys above it, candidates of the query
+
+  // ---- a./b. (at most 64 slots) one wave merges the heads, finds b0 and the
+  // start of this slot's candidates, without a barrier in between
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  bool done = false;
+  if (nslots <= 64) {
+    if (wave == 0) {
+#pragma unroll
+      for (int q = 0; q < kHist0Bins / 256; ++q) *(uint4 *)(hist + 4 * (lane * (kHist0Bins / 256) + q)) = make_uint4(0u, 0u, 0u, 0u);
+      // (the LDS operations of one wave take effect in order)
+      if (lane < nslots) {
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+          if ((uint32_t)i <= wd[0]) atomicAdd(&hist[wd[i] >> 20], wd[i] & 0xFFFFFu);
+      }
+      uint32_t ab;
+      const int b = wave_find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &ab);
+      // the heads are exact down to the lowest bin read from every cut list
+      const bool cut = __ballot(lane < nslots && wd[0] > 15u && (int)(wd[15] >> 20) > b) != 0;
+      const uint32_t cnt = lane < nslots ? head_count_ge(wd, (uint32_t)b) : 0u;
+      const uint32_t inc = wave_inclusive_scan(cnt);
+      // (lane reads with every lane active: inside the lane-0 branch below the
+      // other lanes' values would not be computed)
+      const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(inc - cnt), slot);
+      if (lane == 0) {
+        res[0] = cut ? 0 : 1;
+        res[1] = b;
+        s_misc[0] = ab;
+        s_misc[1] = all;
+        s_base = base;
+      }
+    }
+    __syncthreads();
+    done = res[0] != 0;
+    ub0 = (uint32_t)res[1];
+    above0 = s_misc[0];
+    total = s_misc[1];
+  }
+  if (!done) {
+    // ---- a. level-0 threshold from the list heads
+    __syncthreads();  // the wave path's LDS results have been read
+    for (int i = tid; i < kHist0Bins; i += kSelBlock) hist[i] = 0u;
+    if (tid == 0) floor_max = -1;
+    __syncthreads();
+    int floor = -1;
+    auto add_head = [&](const uint32_t (&e)[16]) {
+      const uint32_t cnt = e[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i)
+        if ((uint32_t)i <= cnt) atomicAdd(&hist[e[i] >> 20], e[i] & 0xFFFFFu);
+      if (cnt > 15u) floor = max(floor, (int)(e[15] >> 20));
+    };
+    if (tid < nslots) add_head(wd);
+    for (int sl = tid + kSelBlock; sl < nslots; sl += kSelBlock) {
+      const uint4 *p = (const uint4 *)(lbase + (size_t)sl * ws.slot_words);
+      const uint4 a0 = p[0], a1 = p[1], a2 = p[2], a3 = p[3];
+      const uint32_t e[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                              a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+      add_head(e);
+    }
+    if (floor >= 0) atomicMax(&floor_max, floor);
+    __syncthreads();
+    int b0 = find_threshold_bin<kHist0Bins, kSelBlock>(hist, (uint32_t)k, &above0, scratch, res);
+    // The heads are exact down to the lowest bin read from every cut list; if
+    // b0 lies below that, add the rest of the lists and search again (uniform).
+    const bool full = b0 < floor_max;
+    if (full) {
+      for (int sl = tid; sl < nslots; sl += kSelBlock) {
+        const uint32_t *l = lbase + (size_t)sl * ws.slot_words;
+        const uint32_t cnt = l[0];
+        for (uint32_t i = 16; i <= cnt; ++i) atomicAdd(&hist[l[i] >> 20], l[i] & 0xFFFFFu);
+      }
+      __syncthreads();
+      b0 = find_threshold_bin<kHist0Bins, kSelBlock>(hist, (uint32_t)k, &above0, scratch, res);
+    }
+    ub0 = (uint32_t)b0;
+
+    // ---- b. where this slot's candidates start: the candidates of all earlier
+    // slots. Thread tid sums the slots [tid * per, (tid + 1) * per).
+    const int per = (nslots + kSelBlock - 1) / kSelBlock;
+    const int s_lo = min(nslots, tid * per), s_hi = min(nslots, s_lo + per);
+    uint32_t mine = 0, upto = 0;  // candidates of my slots, and of my slots before `slot`
+    if (per == 1 && !full) {
+      if (tid < nslots) mine = head_count_ge(wd, ub0);
+    } else {
+      for (int sl = s_lo; sl < s_hi; ++sl) {
+        if (sl == slot) upto = mine;
+        mine += list_count_ge(lbase + (size_t)sl * ws.slot_words, ub0);
+      }
+    }
+    const uint32_t before = block_exclusive_scan(mine, scratch, &total);
+    if (slot >= s_lo && slot < s_hi) s_base = before + upto;
+    __syncthreads();
+  }
+  if (slot == 0 && tid == 0) ws.thr[t] = make_uint4(ub0, above0, total, 0u);
+
+  // ---- write this slot's candidates (position order) at their final place
+  uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
+  const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;  // >= max_kv_len >= n >= total
+  const int64_t send = min((int64_t)n, c0 + skeys);
+  uint32_t o = s_base;
+  for (int64_t b = c0; b < send; b += kSelBatch) {
+    if (b != c0) load_scores<kVec>(row, stride, b + tid * kSelPer, v);
+    const int64_t p0 = b + tid * kSelPer;
+    uint32_t keys[kSelPer];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+      keys[j] = score_key(v[j]);
+      cnt += (p0 + j < send && (keys[j] >> kHist0Shift) >= ub0) ? 1u : 0u;
+    }
+    uint32_t btot;
+    uint32_t q = o + block_exclusive_scan(cnt, scratch, &btot);
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j)
+      if (p0 + j < send && (keys[j] >> kHist0Shift) >= ub0) {
+        if (q < cap) cand[q] = make_uint2((uint32_t)(p0 + j), keys[j]);
+        ++q;
+      }
+    o += btot;
+  }
+}
+
+// One workgroup per query: the exact threshold among the candidates written
+// by k_topk_select and the ordered output.
+__global__ __launch_bounds__(kSelBlock) void k_topk_finish(int k, TopkWs ws, int32_t *__restrict__ topk_idx) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2 * kHist12Bins];  // levels 1 and 2
+  __shared__ uint32_t scratch[kSelWaves];
   __shared__ int res[2];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  int64_t start;
-  const int n = query_candidates(m, t, &start);
-  if (n <= k) return;
-  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
-  const uint32_t *cnts = ws.counts + (size_t)t * ws.nchunk;
-  // chunk counts (<= 2 per thread) and the level-0 result
-  const uint32_t c_a = 2 * tid < nch ? cnts[2 * tid] : 0u;
-  const uint32_t c_b = 2 * tid + 1 < nch ? cnts[2 * tid + 1] : 0u;
-  for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
-  const uint2 thr = ws.thr[t];
-  const uint32_t b0 = thr.x;
-  uint32_t want = (uint32_t)k - thr.y;
-  __syncthreads();
-  uint32_t total;
-  const uint32_t ex = block_exclusive_scan(c_a + c_b, scratch, &total);
-  if (2 * tid < nch) offs[2 * tid] = ex;
-  if (2 * tid + 1 < nch) offs[2 * tid + 1] = ex + c_a;
-  if (tid == 0) offs[nch] = total;
-  __syncthreads();
-
-  // stage the pairs in position order (a group of threads per chunk, no
-  // search) and build the level-1 histogram (key bits 19..10) of bin b0
-  const uint2 *src = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
-  const bool staged = total <= (uint32_t)kFinalCap;
-  int gsz = kFinalBlock;
-  while (gsz > 1 && gsz > kFinalBlock / nch) gsz >>= 1;  // threads per chunk (power of 2)
-  if (gsz * nch > kFinalBlock) gsz = 1;
-  const int groups = kFinalBlock / gsz;
-  const int gid = tid / gsz, gl = tid % gsz;
-  for (int c0 = 0; c0 < nch; c0 += groups) {
-    const int c = c0 + gid;
-    if (c < nch) {
-      const uint32_t cnt = offs[c + 1] - offs[c];
-      const uint2 *cs = src + (size_t)c * kTopkChunk;
-      for (uint32_t i0 = gl; i0 < cnt; i0 += gsz * kBatch) {
-        uint2 v[kBatch];
+  const uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
+  const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;
+  // Round r holds candidates [r * 4096, r * 4096 + 4096), thread tid the 16
+  // consecutive ones from r * 4096 + 16 tid; round 0 stays in registers and is
+  // requested before the query's totals arrive (reads past the end are
+  // clamped into the array and not used)
+  auto load_round = [&](int r, uint32_t lim, uint2 (&pr)[kFinPer]) {
+    const uint32_t f0 = (uint32_t)r * kFinRound + tid * kFinPer;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const uint32_t i = i0 + u * gsz;
-          if (i < cnt) v[u] = cs[i];
-        }
+    for (int i = 0; i < kFinPer; i += 2) {
+      const uint32_t f = min(f0 + i, lim - 2);
+      const uint4 x = *(const uint4 *)(cand + f);
+      pr[i] = make_uint2(x.x, x.y);
+      pr[i + 1] = make_uint2(x.z, x.w);
+    }
+  };
+  uint2 p0r[kFinPer];
+  load_round(0, cap, p0r);
+  const uint4 th = ws.thr[t];  // no candidates for a query that keeps all of its n_t <= k
+  const uint32_t ub0 = th.x, above0 = th.y;
+  const uint32_t total = min(th.z, cap);
+  for (int i = tid; i < 2 * kHist12Bins; i += kSelBlock) hist[i] = 0u;
+  __syncthreads();
+  const int rounds = (int)((total + kFinRound - 1) / kFinRound);
+  auto valid = [&](int r, int i) { return (uint32_t)r * kFinRound + tid * kFinPer + i < total; };
+  uint32_t *hist1 = hist, *hist2 = hist + kHist12Bins;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Keep the candidates in the registers they were loaded into: without this
+  // the compiler may load them again for each pass.
+  auto pin = [&](uint2 (&pr)[kFinPer]) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const uint32_t i = i0 + u * gsz;
-          if (i < cnt) {
-            if (staged) pairs[offs[c] + i] = v[u];
-            if ((v[u].y >> kHist0Shift) == b0) atomicAdd(&hist[(v[u].y >> 10) & 1023u], 1u);
-          }
-        }
+    for (int i = 0; i < kFinPer; ++i) asm volatile("" : "+v"(pr[i].x), "+v"(pr[i].y));
+  };
+  // threshold bin of a level histogram, found by wave 0 and shared
+  auto find_bin = [&](const uint32_t *h, uint32_t want, uint32_t *above) {
+    if (wave == 0) {
+      uint32_t a;
+      const int b = wave_find_threshold_bin<kHist12Bins>(h, want, &a);
+      if (lane == 0) {
+        res[0] = b;
+        res[1] = (int)a;
       }
     }
+    __syncthreads();
+    *above = (uint32_t)res[1];
+    return res[0];
+  };
+  pin(p0r);
+  // level 1: key bits 19..10 of the keys in bin b0
+  auto level1 = [&](int r, const uint2 (&pr)[kFinPer]) {
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+      if (valid(r, i) && (pr[i].y >> kHist0Shift) == ub0) atomicAdd(&hist1[(pr[i].y >> 10) & 1023u], 1u);
+  };
+  level1(0, p0r);
+  for (int r = 1; r < rounds; ++r) {
+    uint2 pr[kFinPer];
+    load_round(r, cap, pr);
+    pin(pr);
+    level1(r, pr);
   }
   __syncthreads();
+  uint32_t want = (uint32_t)k - above0;
   uint32_t above1;
-  const int b1 = find_threshold_bin<kHist12Bins>(hist, want, &above1, scratch, res);
+  const int b1 = find_bin(hist1, want, &above1);
   want -= above1;
-  const uint32_t prefix22 = (b0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
-  auto pair_at = [&](uint32_t f) -> uint2 {
-    if (staged) return pairs[f];
-    const int c = chunk_of(offs, nch, f);
-    return src[(size_t)c * kTopkChunk + (f - offs[c])];
+  const uint32_t prefix22 = (ub0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
+  // level 2: the last 10 bits among the keys that share the top 22 bits
+  auto level2 = [&](int r, const uint2 (&pr)[kFinPer]) {
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+      if (valid(r, i) && (pr[i].y >> 10) == prefix22) atomicAdd(&hist2[pr[i].y & 1023u], 1u);
   };
-  // level 2: the last 10 bits among the pairs that share the top 22 bits
-  for (int i = tid; i < kHist12Bins; i += kFinalBlock) hist[i] = 0u;
-  __syncthreads();
-  for (uint32_t f = tid; f < total; f += kFinalBlock) {
-    const uint32_t key = pair_at(f).y;
-    if ((key >> 10) == prefix22) atomicAdd(&hist[key & 1023u], 1u);
+  level2(0, p0r);
+  for (int r = 1; r < rounds; ++r) {
+    uint2 pr[kFinPer];
+    load_round(r, cap, pr);
+    pin(pr);
+    level2(r, pr);
   }
   __syncthreads();
   uint32_t above2;
-  const int b2 = find_threshold_bin<kHist12Bins>(hist, want, &above2, scratch, res);
+  const int b2 = find_bin(hist2, want, &above2);
   want -= above2;
   const uint32_t kstar = (prefix22 << 10) | (uint32_t)b2;  // the exact k-th largest key
   const uint32_t take = want;                                 // ties at kstar to keep
 
-  // ordered emission: each thread owns a contiguous run of pairs
-  const uint32_t seg = (total + kFinalBlock - 1) / kFinalBlock;
-  const uint32_t s0 = min(total, tid * seg), s1 = min(total, s0 + seg);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (uint32_t f = s0; f < s1; ++f) {
-    const uint32_t key = pair_at(f).y;
-    n_gt += key > kstar;
-    n_eq += key == kstar;
-  }
-  uint32_t tmp;
-  const uint32_t tie_base = block_exclusive_scan(n_eq, scratch, &tmp);
-  const uint32_t ties_here = tie_base >= take ? 0u : min(n_eq, take - tie_base);
-  const uint32_t out_base = block_exclusive_scan(n_gt + ties_here, scratch, &tmp);
-  uint32_t o = out_base, tr = tie_base;
-  for (uint32_t f = s0; f < s1; ++f) {
-    const uint2 pk = pair_at(f);
-    bool sel = pk.y > kstar;
-    if (pk.y == kstar) {
-      sel = tr < take;
-      ++tr;
+  // ordered emission, round by round
+  int32_t *out = topk_idx + (size_t)t * k;
+  uint32_t out_run = 0, tie_run = 0;
+  auto emit = [&](int r, const uint2 (&pr)[kFinPer]) {
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      const bool ok = valid(r, i);
+      n_gt += ok && pr[i].y > kstar;
+      n_eq += ok && pr[i].y == kstar;
     }
-    if (sel) {
-      if (o < (uint32_t)k) topk_idx[(size_t)t * k + o] = (int32_t)pk.x;
-      ++o;
+    uint32_t eq_tot, sel_tot;
+    const uint32_t tie_base = tie_run + block_exclusive_scan(n_eq, scratch, &eq_tot);
+    const uint32_t ties_here = tie_base >= take ? 0u : min(n_eq, take - tie_base);
+    uint32_t o2 = out_run + block_exclusive_scan(n_gt + ties_here, scratch, &sel_tot);
+    uint32_t tr = tie_base;
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      if (!valid(r, i)) continue;
+      bool sel = pr[i].y > kstar;
+      if (pr[i].y == kstar) {
+        sel = tr < take;
+        ++tr;
+      }
+      if (sel) {
+        if (o2 < (uint32_t)k) out[o2] = (int32_t)pr[i].x;
+        ++o2;
+      }
     }
+    tie_run += eq_tot;
+    out_run += sel_tot;
+  };
+  emit(0, p0r);
+  for (int r = 1; r < rounds; ++r) {
+    uint2 pr[kFinPer];
+    load_round(r, cap, pr);
+    pin(pr);
+    emit(r, pr);
   }
 }
 
@@ -263,8 +435,8 @@ static size_t list_q_stride(int max_kv_len) {
 
 size_t topk_ws_bytes(int T, int max_kv_len) {
   size_t nch = ((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk;
-  return align256((size_t)T * list_q_stride(max_kv_len) * 4) + align256((size_t)T * sizeof(uint2)) +
-         align256((size_t)T * nch * 4) + align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
+  return align256((size_t)T * list_q_stride(max_kv_len) * 4) + align256((size_t)T * sizeof(uint4)) +
+         align256((size_t)T * sizeof(int32_t)) + align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
 }
 
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
@@ -274,10 +446,10 @@ TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
   char *p = (char *)ws;
   w.lists = (uint32_t *)p;
   p += align256((size_t)T * w.list_q_stride * 4);
-  w.thr = (uint2 *)p;
-  p += align256((size_t)T * sizeof(uint2));
-  w.counts = (uint32_t *)p;
-  p += align256((size_t)T * w.nchunk * 4);
+  w.thr = (uint4 *)p;
+  p += align256((size_t)T * sizeof(uint4));
+  w.ncand = (int32_t *)p;
+  p += align256((size_t)T * sizeof(int32_t));
   w.entries = (uint2 *)p;
   return w;
 }
@@ -292,36 +464,26 @@ hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64
   return hipGetLastError();
 }
 
-hipError_t launch_topk_scan(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
-                            const TopkWs &w, int32_t *topk_idx, hipStream_t s) {
+hipError_t launch_topk_select(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
+                              const TopkWs &w, int32_t *topk_idx, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (m.max_kv_len > k && (w.slot_keys <= 0 || (m.max_kv_len + w.slot_keys - 1) / w.slot_keys > kTopkMaxSlots))
-    return hipErrorInvalidValue;  // level-0 lists missing or with too many slots
-  int nch = m.max_kv_len > 0 ? (m.max_kv_len + kTopkChunk - 1) / kTopkChunk : 1;
-  dim3 grid(nch, T);
-  const bool vec = (stride % 4 == 0) && (((uintptr_t)scores & 15) == 0);
-  if (vec)
-    hipLaunchKernelGGL(k_topk_scan<true>, grid, dim3(kScanBlock), 0, s, m, k, scores, stride, w,
-                       topk_idx);
-  else
-    hipLaunchKernelGGL(k_topk_scan<false>, grid, dim3(kScanBlock), 0, s, m, k, scores, stride, w,
-                       topk_idx);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_final(const SeqMeta &m, int T, int k, const TopkWs &w, int32_t *topk_idx,
-                             hipStream_t s) {
-  if (T == 0 || m.max_kv_len <= k) return hipSuccess;
-  const size_t dyn = (size_t)kFinalCap * sizeof(uint2);
-  static bool attr_set = false;
-  if (!attr_set) {
-    // allow more than the default dynamic LDS; a refusal surfaces at launch
-    (void)hipFuncSetAttribute((const void *)k_topk_final,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    (void)hipGetLastError();
-    attr_set = true;
+  int slots = 1;
+  if (m.max_kv_len > k) {
+    if (w.slot_keys <= 0 || (m.max_kv_len + w.slot_keys - 1) / w.slot_keys > kTopkMaxSlots)
+      return hipErrorInvalidValue;  // level-0 lists missing or with too many slots
+    slots = (m.max_kv_len + w.slot_keys - 1) / w.slot_keys;
   }
-  hipLaunchKernelGGL(k_topk_final, dim3(T), dim3(kFinalBlock), dyn, s, m, k, w, topk_idx);
+  // (with max_kv_len <= k every query takes the n <= k path before touching
+  // the lists or the scores)
+  dim3 grid(slots, T);
+  const bool vec = stride >= 4 && (stride % 4 == 0) && (((uintptr_t)scores & 15) == 0) && (w.slot_keys % 4 == 0);
+  if (vec)
+    hipLaunchKernelGGL(k_topk_select<true>, grid, dim3(kSelBlock), 0, s, m, k, scores, stride, w, topk_idx);
+  else
+    hipLaunchKernelGGL(k_topk_select<false>, grid, dim3(kSelBlock), 0, s, m, k, scores, stride, w, topk_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || m.max_kv_len <= k) return e;
+  hipLaunchKernelGGL(k_topk_finish, dim3(T), dim3(kSelBlock), 0, s, k, w, topk_idx);
   return hipGetLastError();
 }
 
