@@ -378,9 +378,11 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_finish(int k, TopkWs ws, int
   const uint32_t kstar = (prefix22 << 10) | (uint32_t)b2;  // the exact k-th largest key
   const uint32_t take = want;                                 // ties at kstar to keep
 
-  // ordered emission, round by round
+  // ordered emission, round by round: one scan gives, per thread, the keys
+  // above K* and the ties at K* in front of its run (16 bits each: a round
+  // holds at most 4096 candidates)
   int32_t *out = topk_idx + (size_t)t * k;
-  uint32_t out_run = 0, tie_run = 0;
+  uint32_t gt_run = 0, tie_run = 0;
   auto emit = [&](int r, const uint2 (&pr)[kFinPer]) {
     uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
@@ -389,11 +391,10 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_finish(int k, TopkWs ws, int
       n_gt += ok && pr[i].y > kstar;
       n_eq += ok && pr[i].y == kstar;
     }
-    uint32_t eq_tot, sel_tot;
-    const uint32_t tie_base = tie_run + block_exclusive_scan(n_eq, scratch, &eq_tot);
-    const uint32_t ties_here = tie_base >= take ? 0u : min(n_eq, take - tie_base);
-    uint32_t o2 = out_run + block_exclusive_scan(n_gt + ties_here, scratch, &sel_tot);
-    uint32_t tr = tie_base;
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan((n_eq << 16) | n_gt, scratch, &tot);
+    uint32_t tr = tie_run + (pre >> 16);                          // ties in front of this run
+    uint32_t o2 = gt_run + (pre & 0xFFFFu) + min(tr, take);       // outputs in front of it
 #pragma unroll
     for (int i = 0; i < kFinPer; ++i) {
       if (!valid(r, i)) continue;
@@ -407,8 +408,8 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_finish(int k, TopkWs ws, int
         ++o2;
       }
     }
-    tie_run += eq_tot;
-    out_run += sel_tot;
+    gt_run += tot & 0xFFFFu;
+    tie_run += tot >> 16;
   };
   emit(0, p0r);
   for (int r = 1; r < rounds; ++r) {
