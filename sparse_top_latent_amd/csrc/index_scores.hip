@@ -142,22 +142,6 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform loop bounds
   const int kg = lane >> 4, c16 = lane & 15;
-  // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row;
-  // accumulator row r of this lane is head ht*16 + 4 kg + r
-  v8i a[4];
-  float wv[16];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
-    const v4i lo = src[0], hi = src[1];
-    a[ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
-  }
-  if (kHist) {
-    for (int i = tid; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
-    __syncthreads();
-  }
   const int ntiles = min(tiles_per_wg, (n - c0 + kIdxTileKeys - 1) / kIdxTileKeys);
   // piece p = u * 256 + tid of a tile holds key row p / 8 and its swizzled
   // 16-byte piece; rows past the sequence repeat its last key (their scores
@@ -174,9 +158,26 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
           kKeyLoadPolicy);
     }
   };
-  wait_vmcnt<0>();  // the query loads have landed; from here vmcnt counts copies and stores
+  // the key stream starts first; the query's index matrix and weights load
+  // while the first tiles are in flight
   for (int i = 0; i < kR - 1; ++i)
     if (i < ntiles) issue(i);
+  // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row;
+  // accumulator row r of this lane is head ht*16 + 4 kg + r
+  v8i a[4];
+  float wv[16];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
+    const v4i lo = src[0], hi = src[1];
+    a[ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
+  }
+  // (cleared before the first barrier of the loop; no wave adds to it earlier)
+  if (kHist)
+    for (int i = tid; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
+  wait_vmcnt<0>();  // query loads and the first tiles have landed; from here vmcnt counts copies and stores
   float *srow = scores + t * stride;
   for (int i = 0; i < ntiles; ++i) {
     // tile i has landed once at most the copies of the tiles issued after it
