@@ -74,26 +74,30 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
   }
   if (want_hist) {
     __syncthreads();
-    write_hist0_list<false>(hist, sel, t, blockIdx.x, scratch);
+    write_hist0_list<false, kF32Block>(hist, sel, t, blockIdx.x, scratch);
   }
 }
 
 // --------------------------------------------------------------------------
 // FP8 MFMA path (HI = 64, DI = 128), one query per grid row (decode)
 //
-// The 4 waves of a workgroup stream one contiguous key range of the query
-// through a ring of kIdxRing 8 KiB tiles (64 keys) in LDS. Every thread copies
-// two 16-byte pieces of each tile with LDS-DMA (global_load_lds_dwordx4), so
-// kIdxRing - 1 tiles are in flight while the workgroup computes. Within a
-// 128-byte key row the 16-byte pieces are XOR-swizzled by key (applied on the
-// DMA source side) so that the B-operand reads spread over the LDS banks.
-// Wave w scores keys 16 w .. 16 w + 15 of each tile with four 16x16x128 MFMAs
-// (one per 16-head tile). One barrier per tile both publishes the tile and
-// frees the buffer that the next copy overwrites.
+// The waves of a workgroup stream one contiguous key range of the query
+// through a ring of kIdxRing steps in LDS; a step is kIdxWaves / 4 tiles of 64
+// keys (8 KiB each). Every thread copies two 16-byte pieces of each step with
+// LDS-DMA (global_load_lds_dwordx4), so kIdxRing - 1 steps are in flight while
+// the workgroup computes. Within a 128-byte key row the 16-byte pieces are
+// XOR-swizzled by key (applied on the DMA source side) so that the B-operand
+// reads spread over the LDS banks. Wave w scores keys 16 (w % 4) .. +15 of
+// tile w / 4 of each step with four 16x16x128 MFMAs (one per 16-head tile).
+// One barrier per step both publishes the step and frees the buffer that the
+// next copy overwrites.
 // --------------------------------------------------------------------------
-constexpr int kIdxWaves = 4;       // waves per workgroup
+constexpr int kIdxWaves = 4;       // waves per workgroup (4 or 8)
 constexpr int kKeyLoadPolicy = 2;  // nontemporal (streamed) key copies
-constexpr int kIdxRing = 4;        // tiles in the LDS ring
+constexpr int kIdxRing = 4;        // steps in the LDS ring
+constexpr int kIdxStepTiles = kIdxWaves / 4;
+constexpr int kIdxStepKeys = kIdxStepTiles * kIdxTileKeys;
+constexpr int kIdxStepBytes = kIdxStepTiles * kIdxTileBytes;
 
 // LDS atomic add without a return value, issued as inline asm so that the
 // compiler does not make it wait for the in-flight LDS-DMA copies (it cannot
@@ -120,48 +124,49 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
 }
 
 template <bool kHist, int kR>
-__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int tiles_per_wg,
+__global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int steps_per_wg,
                                                               const uint8_t *__restrict__ q_idx,
                                                               const float *__restrict__ w,
                                                               const uint8_t *__restrict__ k_idx,
                                                               float *__restrict__ scores,
                                                               int64_t stride, TopkWs sel) {
+  constexpr int kThreads = kIdxWaves * 64;
   // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
   // explicit waits below instead of draining every DMA before each read
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
   // level-0 histogram with two 16-bit bins per word (a workgroup scores at most
-  // 128 x 64 = 8192 keys, so a bin cannot overflow)
+  // 8192 keys, so a bin cannot overflow)
   __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
   __shared__ uint32_t scratch[kIdxWaves + 1];
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
   if (kHist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = n;
-  const int c0 = blockIdx.x * tiles_per_wg * kIdxTileKeys;
+  const int c0 = blockIdx.x * steps_per_wg * kIdxStepKeys;
   if (c0 >= n) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform loop bounds
   const int kg = lane >> 4, c16 = lane & 15;
-  const int ntiles = min(tiles_per_wg, (n - c0 + kIdxTileKeys - 1) / kIdxTileKeys);
-  // piece p = u * 256 + tid of a tile holds key row p / 8 and its swizzled
-  // 16-byte piece; rows past the sequence repeat its last key (their scores
-  // are dropped)
+  const int nsteps = min(steps_per_wg, (n - c0 + kIdxStepKeys - 1) / kIdxStepKeys);
+  // piece p = u * kThreads + tid of a step holds key row p / 8 of the step and
+  // its swizzled 16-byte piece; rows past the sequence repeat its last key
+  // (their scores are dropped)
   auto issue = [&](int i) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int p = u * 256 + tid;
+      const int p = u * kThreads + tid;
       const int r = p >> 3;
-      const int key = min(c0 + i * kIdxTileKeys + r, n - 1);
+      const int key = min(c0 + i * kIdxStepKeys + r, n - 1);
       const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
       __builtin_amdgcn_global_load_lds(
-          src, (lds_void *)(ring + (i % kR) * kIdxTileBytes + (u * 256 + wave * 64) * 16), 16, 0,
+          src, (lds_void *)(ring + (i % kR) * kIdxStepBytes + (u * kThreads + wave * 64) * 16), 16, 0,
           kKeyLoadPolicy);
     }
   };
   // the key stream starts first; the query's index matrix and weights load
-  // while the first tiles are in flight
+  // while the first steps are in flight
   for (int i = 0; i < kR - 1; ++i)
-    if (i < ntiles) issue(i);
+    if (i < nsteps) issue(i);
   // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row;
   // accumulator row r of this lane is head ht*16 + 4 kg + r
   v8i a[4];
@@ -176,20 +181,21 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   }
   // (cleared before the first barrier of the loop; no wave adds to it earlier)
   if (kHist)
-    for (int i = tid; i < kHist0Bins / 2; i += kIdxWaves * 64) hist[i] = 0u;
-  wait_vmcnt<0>();  // query loads and the first tiles have landed; from here vmcnt counts copies and stores
+    for (int i = tid; i < kHist0Bins / 2; i += kThreads) hist[i] = 0u;
+  wait_vmcnt<0>();  // query loads and the first steps have landed; from here vmcnt counts copies and stores
   float *srow = scores + t * stride;
-  for (int i = 0; i < ntiles; ++i) {
-    // tile i has landed once at most the copies of the tiles issued after it
+  const int wtile = wave >> 2, wkt = wave & 3;  // this wave's tile in a step and its 16 keys
+  for (int i = 0; i < nsteps; ++i) {
+    // step i has landed once at most the copies of the steps issued after it
     // are outstanding (score stores issued in between only lengthen the wait)
-    wait_vmcnt_upto<2 * (kR - 2)>(2 * (min(ntiles - 1, i + kR - 2) - i));
+    wait_vmcnt_upto<2 * (kR - 2)>(2 * (min(nsteps - 1, i + kR - 2) - i));
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (i + kR - 1 < ntiles) issue(i + kR - 1);
-    const unsigned char *tb = ring + (i % kR) * kIdxTileBytes;
-    const v8i b = load_key_operand(tb, wave, kg, c16);
+    if (i + kR - 1 < nsteps) issue(i + kR - 1);
+    const unsigned char *tb = ring + (i % kR) * kIdxStepBytes + wtile * kIdxTileBytes;
+    const v8i b = load_key_operand(tb, wkt, kg, c16);
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     // each head sum split over two accumulators so consecutive FMAs do not wait
     float ev = 0.0f, od = 0.0f;
@@ -202,11 +208,11 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
       od = fmaf(fmaxf(x[3], 0.0f), wv[ht * 4 + 3], od);
     }
     // sum over the four lane groups that hold the same key: every lane ends
-    // with the score of key 16 wave + c16 (-0 becomes +0)
+    // with the score of its key (-0 becomes +0)
     const float x = ev + od;
     const float y = add_swapped(x, x, true);
     const float keep = add_swapped(y, y, false) + 0.0f;
-    const int s = c0 + i * kIdxTileKeys + wave * 16 + lane;
+    const int s = c0 + i * kIdxStepKeys + wtile * kIdxTileKeys + wkt * 16 + lane;
     if (lane < 16 && s < n) {
       srow[s] = keep;
       if (kHist) {
@@ -217,16 +223,17 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   }
   if (kHist) {
     __syncthreads();
-    write_hist0_list<true>(hist, sel, t, blockIdx.x, scratch);
+    write_hist0_list<true, kThreads>(hist, sel, t, blockIdx.x, scratch);
   }
 }
 
 }  // namespace
 
 int index_fp8_iters(int T, int max_kv_len) {
-  // aim for about two 4-wave workgroups per CU over the whole batch
+  // a workgroup scores 4 * iters tiles of 64 keys; aim for about two
+  // workgroups per CU over the whole batch (4096 keys each for 16 x 128K)
   const int64_t keys = (int64_t)T * max_kv_len;
-  const int64_t per_iter = 512LL * kIdxWaves * kIdxTileKeys;
+  const int64_t per_iter = 2048LL * kIdxTileKeys;
   int64_t it = (keys + per_iter - 1) / per_iter;
   if (it < 2) it = 2;
   if (it > 32) it = 32;
@@ -263,9 +270,9 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxTileBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxStepBytes);
     (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxTileBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxStepBytes);
     (void)hipGetLastError();
     attr = true;
   }
@@ -277,22 +284,21 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     if (e != hipSuccess || !sel) return e;
     return launch_topk_hist0(m, T, scores, stride, sel, s);
   }
-  const int iters = index_fp8_iters(T, m.max_kv_len);
-  const int per_wg = kIdxWaves * iters * kIdxTileKeys;
+  // aim for about two workgroups per CU; a workgroup scores whole steps
+  const int steps = index_fp8_iters(T, m.max_kv_len) * 4 / kIdxStepTiles;
+  const int per_wg = steps * kIdxStepKeys;
   dim3 grid((m.max_kv_len + per_wg - 1) / per_wg, T);
   TopkWs none{};
   if (sel) {
     sel->slot_keys = per_wg;
     sel->slot_words = 4 + (per_wg < kHist0Bins ? per_wg : kHist0Bins);
   }
-  // one workgroup copies and scores kIdxWaves * iters tiles
-  const int tiles = kIdxWaves * iters;
-  const size_t smem = (size_t)kIdxRing * kIdxTileBytes;
+  const size_t smem = (size_t)kIdxRing * kIdxStepBytes;
   if (sel)
-    hipLaunchKernelGGL((k_index_fp8<true, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, tiles,
+    hipLaunchKernelGGL((k_index_fp8<true, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, steps,
                        q_idx, w, k_idx, scores, stride, *sel);
   else
-    hipLaunchKernelGGL((k_index_fp8<false, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, tiles,
+    hipLaunchKernelGGL((k_index_fp8<false, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, steps,
                        q_idx, w, k_idx, scores, stride, none);
   return hipGetLastError();
 }

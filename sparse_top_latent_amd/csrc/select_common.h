@@ -101,35 +101,38 @@ __device__ __forceinline__ int wave_find_threshold_bin(const uint32_t *hist, uin
 
 // Writes the nonzero bins of a 4096-bin LDS level-0 histogram as the list of
 // slot `slot` of query t: the entry count, then entries (bin << 20 | count)
-// in descending bin order. Needs blockDim.x == 256 (each thread scans 16
-// consecutive bins) and a completed histogram (the caller synchronises).
-// kPacked: two 16-bit bins per LDS word. A slot never holds more entries than
-// the positions it covers, which bounds them by w.slot_words - 4.
-template <bool kPacked>
+// in descending bin order. kBlock threads (blockDim.x) scan 4096 / kBlock
+// consecutive bins each; the histogram must be complete (the caller
+// synchronises). kPacked: two 16-bit bins per LDS word. A slot never holds
+// more entries than the positions it covers, which bounds them by
+// w.slot_words - 4.
+template <bool kPacked, int kBlock>
 __device__ __forceinline__ void write_hist0_list(const uint32_t *hist, const TopkWs &w, int t,
                                                  int slot, uint32_t *scratch) {
+  constexpr int kPer = kHist0Bins / kBlock;
+  static_assert(kPer * kBlock == kHist0Bins && kPer % 2 == 0, "bins per thread");
   const int tid = threadIdx.x;
-  uint32_t c[16];
+  uint32_t c[kPer];
   if (kPacked) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t v = hist[tid * 8 + q];
+    for (int q = 0; q < kPer / 2; ++q) {
+      const uint32_t v = hist[tid * (kPer / 2) + q];
       c[2 * q] = v & 0xFFFFu;
       c[2 * q + 1] = v >> 16;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = hist[tid * 16 + i];
+    for (int i = 0; i < kPer; ++i) c[i] = hist[tid * kPer + i];
   }
   uint32_t nz = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) nz += c[i] != 0u;
+  for (int i = 0; i < kPer; ++i) nz += c[i] != 0u;
   uint32_t total;
   uint32_t asc = block_exclusive_scan(nz, scratch, &total);  // ascending rank of my first entry
   uint32_t *list = w.lists + (size_t)t * w.list_q_stride + (size_t)slot * w.slot_words;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    if (c[i]) list[1 + (total - 1 - asc++)] = ((uint32_t)(tid * 16 + i) << 20) | c[i];
+  for (int i = 0; i < kPer; ++i)
+    if (c[i]) list[1 + (total - 1 - asc++)] = ((uint32_t)(tid * kPer + i) << 20) | c[i];
   if (tid == 0) list[0] = total;
 }
 

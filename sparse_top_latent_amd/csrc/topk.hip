@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__re
     if (s < n) atomicAdd(&hist[score_key(row[s]) >> kHist0Shift], 1u);
   }
   __syncthreads();
-  write_hist0_list<false>(hist, ws, t, blockIdx.x, scratch);
+  write_hist0_list<false, 256>(hist, ws, t, blockIdx.x, scratch);
 }
 
 // kSelPer consecutive scores from position p on; positions at or past the end
