@@ -38,10 +38,11 @@ namespace {
 
 constexpr int kSelBlock = 256;
 constexpr int kSelWaves = kSelBlock / 64;
-constexpr int kSelPer = 16;                        // consecutive scores per thread and batch
+constexpr int kSelPer = 4096 / kSelBlock;          // consecutive scores per thread and batch
 constexpr int kSelBatch = kSelBlock * kSelPer;     // 4096 positions
-constexpr int kFinPer = 16;                        // candidates per thread and round of the last pass
-constexpr int kFinRound = kSelBlock * kFinPer;     // 4096 candidates
+constexpr int kFinBlock = 1024;                    // threads of the finishing workgroup
+constexpr int kFinPer = 4096 / kFinBlock;          // candidates per thread and round of the last pass
+constexpr int kFinRound = kFinBlock * kFinPer;     // 4096 candidates
 
 __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__restrict__ scores,
                                                     int64_t stride, TopkWs ws) {
@@ -285,16 +286,16 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_select(SeqMeta m, int k,
 
 // One workgroup per query: the exact threshold among the candidates written
 // by k_topk_select and the ordered output.
-__global__ __launch_bounds__(kSelBlock) void k_topk_finish(int k, TopkWs ws, int32_t *__restrict__ topk_idx) {
+__global__ __launch_bounds__(kFinBlock) void k_topk_finish(int k, TopkWs ws, int32_t *__restrict__ topk_idx) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[2 * kHist12Bins];  // levels 1 and 2
-  __shared__ uint32_t scratch[kSelWaves];
+  __shared__ uint32_t scratch[kFinBlock / 64];
   __shared__ int res[2];
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   const uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
   const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;
-  // Round r holds candidates [r * 4096, r * 4096 + 4096), thread tid the 16
-  // consecutive ones from r * 4096 + 16 tid; round 0 stays in registers and is
+  // Round r holds candidates [r * 4096, r * 4096 + 4096), thread tid the
+  // kFinPer consecutive ones from r * 4096 + kFinPer tid; round 0 stays in registers and is
   // requested before the query's totals arrive (reads past the end are
   // clamped into the array and not used)
   auto load_round = [&](int r, uint32_t lim, uint2 (&pr)[kFinPer]) {
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_finish(int k, TopkWs ws, int
   const uint4 th = ws.thr[t];  // no candidates for a query that keeps all of its n_t <= k
   const uint32_t ub0 = th.x, above0 = th.y;
   const uint32_t total = min(th.z, cap);
-  for (int i = tid; i < 2 * kHist12Bins; i += kSelBlock) hist[i] = 0u;
+  for (int i = tid; i < 2 * kHist12Bins; i += kFinBlock) hist[i] = 0u;
   __syncthreads();
   const int rounds = (int)((total + kFinRound - 1) / kFinRound);
   auto valid = [&](int r, int i) { return (uint32_t)r * kFinRound + tid * kFinPer + i < total; };
@@ -484,7 +485,7 @@ hipError_t launch_topk_select(const SeqMeta &m, int T, int k, const float *score
     hipLaunchKernelGGL(k_topk_select<false>, grid, dim3(kSelBlock), 0, s, m, k, scores, stride, w, topk_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || m.max_kv_len <= k) return e;
-  hipLaunchKernelGGL(k_topk_finish, dim3(T), dim3(kSelBlock), 0, s, k, w, topk_idx);
+  hipLaunchKernelGGL(k_topk_finish, dim3(T), dim3(kFinBlock), 0, s, k, w, topk_idx);
   return hipGetLastError();
 }
 
