@@ -14,10 +14,12 @@
 //
 // Kernels:
 //  * k_mla_f32: generic fp32 path, one workgroup per (query, head).
-//  * k_mla_split (MI355X path, H = 64, Dc = 512, Dr = 64): the selected rows of
-//    a query are cut into splits of 128; one workgroup per (split, query)
-//    gathers 32-row tiles into LDS (bf16, or MXFP8 expanded exactly to bf16),
-//    and each of its 4 waves owns 16 heads:
+//  * k_mla_split8 / k_mla_split (MI355X path, H = 64, Dc = 512, Dr = 64): the
+//    selected rows of a query are cut into splits of 128; one workgroup per
+//    (split, query) gathers 32-row tiles into LDS (bf16, or MXFP8 expanded
+//    exactly to bf16). In k_mla_split (MXFP8) each of 4 waves owns 16 heads;
+//    k_mla_split8 (bf16) has 8 waves, two sets of 4 that take alternate tiles
+//    and merge at the end. Per wave:
 //      S^T = rows . Q^T  with bf16 16x16x32 MFMA (the query slice stays in VGPRs),
 //      online softmax per head in fp32 (exp2 domain),
 //      O^T += V^T . P^T  with bf16 MFMA; P^T comes straight from the S^T
