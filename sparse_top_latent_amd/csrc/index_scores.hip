@@ -82,22 +82,27 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
 // FP8 MFMA path (HI = 64, DI = 128), one query per grid row (decode)
 //
 // The waves of a workgroup stream one contiguous key range of the query
-// through a ring of kIdxRing steps in LDS; a step is kIdxWaves / 4 tiles of 64
-// keys (8 KiB each). Every thread copies two 16-byte pieces of each step with
-// LDS-DMA (global_load_lds_dwordx4), so kIdxRing - 1 steps are in flight while
-// the workgroup computes. Within a 128-byte key row the 16-byte pieces are
-// XOR-swizzled by key (applied on the DMA source side) so that the B-operand
-// reads spread over the LDS banks. Wave w scores keys 16 (w % 4) .. +15 of
-// tile w / 4 of each step with four 16x16x128 MFMAs (one per 16-head tile).
+// through a ring of kIdxRing steps in LDS; a step is kIdxStepTiles tiles of 64
+// keys (8 KiB each). Every thread copies kIdxPieces 16-byte pieces of each step
+// with LDS-DMA (global_load_lds_dwordx4), so kIdxRing - 1 steps are in flight
+// while the workgroup computes. Within a 128-byte key row the 16-byte pieces
+// are XOR-swizzled by key (applied on the DMA source side) so that the
+// B-operand reads spread over the LDS banks. A step has 4 kIdxStepTiles groups
+// of 16 keys; wave w scores groups w, w + kIdxWaves, .. with four 16x16x128
+// MFMAs each (one per 16-head tile).
 // One barrier per step both publishes the step and frees the buffer that the
 // next copy overwrites.
 // --------------------------------------------------------------------------
 constexpr int kIdxWaves = 4;       // waves per workgroup (4 or 8)
 constexpr int kKeyLoadPolicy = 2;  // nontemporal (streamed) key copies
 constexpr int kIdxRing = 4;        // steps in the LDS ring
-constexpr int kIdxStepTiles = kIdxWaves / 4;
+constexpr int kIdxStepTiles = 1;   // 64-key tiles per step
 constexpr int kIdxStepKeys = kIdxStepTiles * kIdxTileKeys;
 constexpr int kIdxStepBytes = kIdxStepTiles * kIdxTileBytes;
+constexpr int kIdxGroups = kIdxStepTiles * 4 / kIdxWaves;        // 16-key groups per wave and step
+constexpr int kIdxPieces = kIdxStepBytes / (kIdxWaves * 64 * 16);  // DMA pieces per thread and step
+static_assert(kIdxGroups >= 1 && kIdxGroups * kIdxWaves == kIdxStepTiles * 4, "groups per wave");
+static_assert(kIdxPieces >= 1 && kIdxPieces * kIdxWaves * 64 * 16 == kIdxStepBytes, "pieces per thread");
 
 // LDS atomic add without a return value, issued as inline asm so that the
 // compiler does not make it wait for the in-flight LDS-DMA copies (it cannot
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   // (their scores are dropped)
   auto issue = [&](int i) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kIdxPieces; ++u) {
       const int p = u * kThreads + tid;
       const int r = p >> 3;
       const int key = min(c0 + i * kIdxStepKeys + r, n - 1);
@@ -184,40 +189,52 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
     for (int i = tid; i < kHist0Bins / 2; i += kThreads) hist[i] = 0u;
   wait_vmcnt<0>();  // query loads and the first steps have landed; from here vmcnt counts copies and stores
   float *srow = scores + t * stride;
-  const int wtile = wave >> 2, wkt = wave & 3;  // this wave's tile in a step and its 16 keys
   for (int i = 0; i < nsteps; ++i) {
     // step i has landed once at most the copies of the steps issued after it
     // are outstanding (score stores issued in between only lengthen the wait)
-    wait_vmcnt_upto<2 * (kR - 2)>(2 * (min(nsteps - 1, i + kR - 2) - i));
+    wait_vmcnt_upto<kIdxPieces * (kR - 2)>(kIdxPieces * (min(nsteps - 1, i + kR - 2) - i));
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i + kR - 1 < nsteps) issue(i + kR - 1);
-    const unsigned char *tb = ring + (i % kR) * kIdxStepBytes + wtile * kIdxTileBytes;
-    const v8i b = load_key_operand(tb, wkt, kg, c16);
+    // group g of this wave: 16-key group wave + g * kIdxWaves of the step
+    v8i b[kIdxGroups];
+#pragma unroll
+    for (int g = 0; g < kIdxGroups; ++g) {
+      const int q = wave + g * kIdxWaves;
+      b[g] = load_key_operand(ring + (i % kR) * kIdxStepBytes + (q >> 2) * kIdxTileBytes, q & 3, kg, c16);
+    }
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     // each head sum split over two accumulators so consecutive FMAs do not wait
-    float ev = 0.0f, od = 0.0f;
+    float ev[kIdxGroups], od[kIdxGroups];
+#pragma unroll
+    for (int g = 0; g < kIdxGroups; ++g) ev[g] = od[g] = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-      const v4f x = mfma_fp8(a[ht], b, zero);
-      ev = fmaf(fmaxf(x[0], 0.0f), wv[ht * 4 + 0], ev);
-      od = fmaf(fmaxf(x[1], 0.0f), wv[ht * 4 + 1], od);
-      ev = fmaf(fmaxf(x[2], 0.0f), wv[ht * 4 + 2], ev);
-      od = fmaf(fmaxf(x[3], 0.0f), wv[ht * 4 + 3], od);
+#pragma unroll
+      for (int g = 0; g < kIdxGroups; ++g) {
+        const v4f x = mfma_fp8(a[ht], b[g], zero);
+        ev[g] = fmaf(fmaxf(x[0], 0.0f), wv[ht * 4 + 0], ev[g]);
+        od[g] = fmaf(fmaxf(x[1], 0.0f), wv[ht * 4 + 1], od[g]);
+        ev[g] = fmaf(fmaxf(x[2], 0.0f), wv[ht * 4 + 2], ev[g]);
+        od[g] = fmaf(fmaxf(x[3], 0.0f), wv[ht * 4 + 3], od[g]);
+      }
     }
-    // sum over the four lane groups that hold the same key: every lane ends
-    // with the score of its key (-0 becomes +0)
-    const float x = ev + od;
-    const float y = add_swapped(x, x, true);
-    const float keep = add_swapped(y, y, false) + 0.0f;
-    const int s = c0 + i * kIdxStepKeys + wtile * kIdxTileKeys + wkt * 16 + lane;
-    if (lane < 16 && s < n) {
-      srow[s] = keep;
-      if (kHist) {
-        const uint32_t bin = score_key(keep) >> kHist0Shift;
-        lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
+#pragma unroll
+    for (int g = 0; g < kIdxGroups; ++g) {
+      // sum over the four lane groups that hold the same key: every lane ends
+      // with the score of its key (-0 becomes +0)
+      const float x = ev[g] + od[g];
+      const float y = add_swapped(x, x, true);
+      const float keep = add_swapped(y, y, false) + 0.0f;
+      const int s = c0 + i * kIdxStepKeys + (wave + g * kIdxWaves) * 16 + lane;
+      if (lane < 16 && s < n) {
+        srow[s] = keep;
+        if (kHist) {
+          const uint32_t bin = score_key(keep) >> kHist0Shift;
+          lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
+        }
       }
     }
   }
