@@ -139,9 +139,9 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
   // explicit waits below instead of draining every DMA before each read
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
-  // level-0 histogram with two 16-bit bins per word (a workgroup scores at most
-  // 8192 keys, so a bin cannot overflow)
-  __shared__ uint32_t hist[kHist ? kHist0Bins / 2 : 1];
+  // level-0 histogram, one word per bin (two bins per word measured slower:
+  // more same-address atomics)
+  __shared__ uint32_t hist[kHist ? kHist0Bins : 1];
   __shared__ uint32_t scratch[kIdxWaves + 1];
   const int t = blockIdx.y;
   int64_t start;
@@ -186,14 +186,16 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   }
   // (cleared before the first barrier of the loop; no wave adds to it earlier)
   if (kHist)
-    for (int i = tid; i < kHist0Bins / 2; i += kThreads) hist[i] = 0u;
+    for (int i = tid; i < kHist0Bins; i += kThreads) hist[i] = 0u;
   wait_vmcnt<0>();  // query loads and the first steps have landed; from here vmcnt counts copies and stores
   float *srow = scores + t * stride;
   for (int i = 0; i < nsteps; ++i) {
     // step i has landed once at most the copies of the steps issued after it
     // are outstanding (score stores issued in between only lengthen the wait)
     wait_vmcnt_upto<kIdxPieces * (kR - 2)>(kIdxPieces * (min(nsteps - 1, i + kR - 2) - i));
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    // (no lgkmcnt wait: this wave's B-operand reads of the buffer the next
+    // copy overwrites completed before its MFMAs; only histogram atomics,
+    // which touch no ring buffer, can still be in flight)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -233,14 +235,14 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
         srow[s] = keep;
         if (kHist) {
           const uint32_t bin = score_key(keep) >> kHist0Shift;
-          lds_add_u32(&hist[bin >> 1], (bin & 1) ? 65536u : 1u);
+          lds_add_u32(&hist[bin], 1u);
         }
       }
     }
   }
   if (kHist) {
     __syncthreads();
-    write_hist0_list<true, kThreads>(hist, sel, t, blockIdx.x, scratch);
+    write_hist0_list<false, kThreads>(hist, sel, t, blockIdx.x, scratch);
   }
 }
 
