@@ -399,11 +399,10 @@ __global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, uint16_t *__restri
 //
 // 8 waves: wave w serves heads 16 (w % 4) .. 16 (w % 4) + 15 for the tiles of
 // its set (w / 4): set 0 takes tiles 0 and 2, set 1 tiles 1 and 3, each with
-// its own running max, sum and output accumulator. Each set gathers its first
-// tile, and once the first pair has landed issues its second tile, which
-// streams in while the first pair is computed. At the end the sets swap half
-// of their accumulators through LDS and each merges and writes half of the
-// partial.
+// its own running max, sum and output accumulator. Each set requests both of
+// its tiles at once; the second pair streams in while the first pair is
+// computed. At the end the sets swap half of their accumulators through LDS
+// and each merges and writes half of the partial.
 // --------------------------------------------------------------------------
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
@@ -504,7 +503,10 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
       dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
     }
   };
+  // both tiles of the set at once: with 8 waves issuing, the gather runs near
+  // the random-row rate of the memory system
   issue_tile(set);
+  issue_tile(set + 2);
 
   v4f acc[kCt];
 #pragma unroll
@@ -518,10 +520,8 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
 
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    wait_vmcnt<0>();
+    if (u == 0) wait_vmcnt<kBfDma>(); else wait_vmcnt<0>();
     barrier_lds();  // tiles 2u and 2u + 1 have landed
-    // the second pair of tiles streams in while the first pair is computed
-    if (u == 0) issue_tile(set + 2);
     const int tt = set + 2 * u;
     if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
     const unsigned char *tile = smem + tt * kTileBytes;
