@@ -106,6 +106,15 @@ def test_topk_one_dense_bin_beyond_lds_staging():
     _check_topk([vals, vals[: n // 2]], 2048, "dense level-0 bin")
 
 
+def test_topk_many_slots_block_path():
+    # 74 and 269 level-0 slots of 4,096 positions: more slots than one wave
+    # merges, and more than one slot per thread of the block-wide merge
+    g = torch.Generator().manual_seed(3)
+    a = (torch.randint(-50, 50, (300_000,), generator=g).float() * 0.25).numpy()
+    b = torch.randn(1_100_000, generator=g).numpy()
+    _check_topk([a, b], 2048, "many slots")
+
+
 def test_topk_small_k_and_continuous_scores():
     g = torch.Generator().manual_seed(2)
     rows = [torch.randn(n, generator=g).tolist() for n in (3, 100, 5000, 70000)]
