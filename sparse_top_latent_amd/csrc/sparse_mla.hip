@@ -669,11 +669,26 @@ __global__ __launch_bounds__(64 * kCombCt) void k_mla_combine(MlaArgs a, const u
   uint2 xb[kN];
   const uint2 *src = (const uint2 *)opart + ((((size_t)t * S) * 4 + wave) * kCt + ct) * 64 + lane;
   const float2 *msrc = ml + (size_t)t * S * kH + h;
+  if constexpr (kS > 0 && kS * 16 <= 64 * kCombCt) {
+    // the (m, l) pairs of the workgroup's 16 heads are loaded once, one per
+    // thread, and shared through LDS (every lane would otherwise load all kS)
+    __shared__ float2 s_ml[kS * 16];
+    const int tid = threadIdx.x;
+    float2 mine = make_float2(0.f, 0.f);
+    if (tid < kS * 16) mine = ml[((size_t)t * S + tid / 16) * kH + wave * 16 + (tid & 15)];
 #pragma unroll
-  for (int s = 0; s < kN; ++s) {
-    if (kS > 0 || s < S) {
-      st[s] = msrc[(size_t)s * kH];
-      xb[s] = src[(size_t)s * 4 * kCt * 64];
+    for (int s = 0; s < kN; ++s) xb[s] = src[(size_t)s * 4 * kCt * 64];
+    if (tid < kS * 16) s_ml[tid] = mine;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kN; ++s) st[s] = s_ml[s * 16 + c16];
+  } else {
+#pragma unroll
+    for (int s = 0; s < kN; ++s) {
+      if (kS > 0 || s < S) {
+        st[s] = msrc[(size_t)s * kH];
+        xb[s] = src[(size_t)s * 4 * kCt * 64];
+      }
     }
   }
   float M = -INFINITY;
