@@ -97,6 +97,9 @@ constexpr int kIdxWaves = 4;       // waves per workgroup (4 or 8)
 constexpr int kKeyLoadPolicy = 2;  // nontemporal (streamed) key copies
 constexpr int kIdxRing = 4;        // steps in the LDS ring
 constexpr int kIdxStepTiles = 1;   // 64-key tiles per step
+// The workgroup's scores collect in LDS and leave in one coalesced burst at
+// its end instead of one 64-byte store per wave and tile.
+constexpr bool kIdxStageScores = true;
 constexpr int kIdxStepKeys = kIdxStepTiles * kIdxTileKeys;
 constexpr int kIdxStepBytes = kIdxStepTiles * kIdxTileBytes;
 constexpr int kIdxGroups = kIdxStepTiles * 4 / kIdxWaves;        // 16-key groups per wave and step
@@ -139,6 +142,8 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
   // explicit waits below instead of draining every DMA before each read
   extern __shared__ __attribute__((aligned(16))) unsigned char ring[];
+  // the score stage follows the ring in the same allocation
+  float *stage = (float *)(ring + kR * kIdxStepBytes);
   // level-0 histogram, one word per bin (two bins per word measured slower:
   // more same-address atomics)
   __shared__ uint32_t hist[kHist ? kHist0Bins : 1];
@@ -232,7 +237,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
       const float keep = add_swapped(y, y, false) + 0.0f;
       const int s = c0 + i * kIdxStepKeys + (wave + g * kIdxWaves) * 16 + lane;
       if (lane < 16 && s < n) {
-        srow[s] = keep;
+        if (kIdxStageScores)
+          stage[s - c0] = keep;
+        else
+          srow[s] = keep;
         if (kHist) {
           const uint32_t bin = score_key(keep) >> kHist0Shift;
           lds_add_u32(&hist[bin], 1u);
@@ -240,10 +248,22 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
       }
     }
   }
-  if (kHist) {
-    __syncthreads();
-    write_hist0_list<false, kThreads>(hist, sel, t, blockIdx.x, scratch);
+  if (kHist || kIdxStageScores) __syncthreads();
+  if (kIdxStageScores) {
+    const int nk = min(n - c0, steps_per_wg * kIdxStepKeys);
+    const bool vec = ((stride | c0) & 3) == 0 && ((uintptr_t)srow & 15) == 0;  // 16-byte aligned stores
+    if (vec) {
+      for (int j = 4 * tid; j < nk; j += 4 * kThreads) {
+        if (j + 4 <= nk)
+          *(float4 *)(srow + c0 + j) = *(const float4 *)(stage + j);
+        else
+          for (int e = j; e < nk; ++e) srow[c0 + e] = stage[e];
+      }
+    } else {
+      for (int j = tid; j < nk; j += kThreads) srow[c0 + j] = stage[j];
+    }
   }
+  if (kHist) write_hist0_list<false, kThreads>(hist, sel, t, blockIdx.x, scratch);
 }
 
 }  // namespace
@@ -288,10 +308,12 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   static bool attr = false;
   if (!attr) {
+    // ring plus the largest score stage (128 tiles)
+    const int max_smem = kIdxRing * kIdxStepBytes + (kIdxStageScores ? 128 * kIdxTileKeys * 4 : 0);
     (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxStepBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
     (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kIdxRing * kIdxStepBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
     (void)hipGetLastError();
     attr = true;
   }
@@ -312,7 +334,7 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     sel->slot_keys = per_wg;
     sel->slot_words = 4 + (per_wg < kHist0Bins ? per_wg : kHist0Bins);
   }
-  const size_t smem = (size_t)kIdxRing * kIdxStepBytes;
+  const size_t smem = (size_t)kIdxRing * kIdxStepBytes + (kIdxStageScores ? (size_t)per_wg * 4 : 0);
   if (sel)
     hipLaunchKernelGGL((k_index_fp8<true, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, steps,
                        q_idx, w, k_idx, scores, stride, *sel);
