@@ -50,9 +50,10 @@ __device__ __forceinline__ v8i load_key_operand(const unsigned char *tb, int kt,
 // (lane l) is the sum, over the 16 heads this lane's accumulator rows cover,
 // of w[h] * max(0, qI[h] . k) for query j and key 16 kt + l % 16.
 //
-// On gfx950 MFMA and VALU time add up on a SIMD (measured: they do not
-// overlap), so the epilogue (a max and an FMA per accumulator element) is
-// kept as short as it can be; each sum is split over two accumulators so
+// On gfx950 the epilogue (a max and an FMA per accumulator element) costs
+// about as many cycles as the MFMA itself and overlaps with MFMA work only in
+// part (counters: a VALU issue in about half of the MFMA-busy cycles), so it
+// is kept as short as it can be; each sum is split over two accumulators so
 // that consecutive FMAs do not wait on each other. The B operand is read
 // per 16-key tile, which also bounds how many MFMA results are live at once.
 // load_b(kt) returns the B operand of key tile kt.

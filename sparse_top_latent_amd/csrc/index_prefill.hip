@@ -41,9 +41,10 @@ constexpr int kPfChunk = 8192;  // keys per workgroup
 constexpr int kPfQpw = 1;       // queries per wave
 constexpr int kPfBufs = 3;
 
-// kQpw queries per wave, kPfGroup / kQpw waves per workgroup. MFMA and VALU
-// time add up on a SIMD, so latency is hidden by wave count: the register
-// budget is held to 6 waves per SIMD (3 workgroups per CU).
+// kQpw queries per wave, kPfGroup / kQpw waves per workgroup. The
+// weighted-ReLU epilogue brings about as much VALU work as there is MFMA work
+// and the two overlap only in part on a SIMD, so latency is hidden by wave
+// count: the register budget is held to 6 waves per SIMD (3 workgroups per CU).
 template <int kQpw>
 __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta m, int T,
                                                                 const uint8_t *__restrict__ q_idx,

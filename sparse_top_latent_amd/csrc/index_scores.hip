@@ -173,10 +173,6 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
           kKeyLoadPolicy);
     }
   };
-  // the key stream starts first; the query's index matrix and weights load
-  // while the first steps are in flight
-  for (int i = 0; i < kR - 1; ++i)
-    if (i < nsteps) issue(i);
   // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row;
   // accumulator row r of this lane is head ht*16 + 4 kg + r
   v8i a[4];
@@ -189,10 +185,17 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
   }
+  // The first steps are requested after the query's index matrix and weights,
+  // so that only those loads are waited for before the loop (step 0 then
+  // lands while the waves finish setting up). The requests are unconditional,
+  // so that the compiler can count them in its own wait for the query
+  // registers; steps past nsteps read the clamped last key into ring buffers
+  // that are never read, and the loop's last wait covers them.
+  for (int i = 0; i < kR - 1; ++i) issue(i);
   // (cleared before the first barrier of the loop; no wave adds to it earlier)
   if (kHist)
     for (int i = tid; i < kHist0Bins; i += kThreads) hist[i] = 0u;
-  wait_vmcnt<0>();  // query loads and the first steps have landed; from here vmcnt counts copies and stores
+  wait_vmcnt<kIdxPieces * (kR - 1)>();  // the query loads have landed; from here vmcnt counts copies and stores
   float *srow = scores + t * stride;
   for (int i = 0; i < nsteps; ++i) {
     // step i has landed once at most the copies of the steps issued after it
