@@ -99,6 +99,48 @@ __device__ __forceinline__ int wave_find_threshold_bin(const uint32_t *hist, uin
   return top - J;
 }
 
+// Level-0 threshold search of one wave over list heads held in registers:
+// lane l < nl holds a head e[0..15] (entry count, then up to 15 entries
+// bin << 20 | count in descending bin order). Same result as adding the heads
+// into a 4096-bin histogram and calling wave_find_threshold_bin, in two
+// passes over 64 bins each: first the 64 buckets of 64 bins (bin >> 6), then
+// the 64 bins of the bucket that holds the `want`-th element. `h` is 128
+// words of LDS used by this wave alone (its LDS operations take effect in
+// order). Returns the same result for every lane.
+__device__ __forceinline__ int wave_heads_threshold_bin(uint32_t *h, const uint32_t (&e)[16], int nl,
+                                                        uint32_t want, uint32_t *above) {
+  const int lane = threadIdx.x & 63;
+  h[lane] = 0u;
+  h[64 + lane] = 0u;
+  if (lane < nl) {
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+      if ((uint32_t)i <= e[0]) atomicAdd(&h[e[i] >> 26], e[i] & 0xFFFFFu);
+  }
+  // lane l takes bucket 63 - l: an inclusive scan over lanes is a suffix
+  // scan over buckets
+  const uint32_t cc = h[63 - lane];
+  const uint32_t inc = wave_inclusive_scan(cc);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  if (total < want) {
+    *above = total;
+    return -1;
+  }
+  const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(inc >= want)) - 1);
+  const uint32_t above_c = (uint32_t)__builtin_amdgcn_readlane((int)(inc - cc), L);
+  const uint32_t bucket = 63u - (uint32_t)L;
+  if (lane < nl) {
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+      if ((uint32_t)i <= e[0] && (e[i] >> 26) == bucket) atomicAdd(&h[64 + ((e[i] >> 20) & 63u)], e[i] & 0xFFFFFu);
+  }
+  const uint32_t fc = h[64 + 63 - lane];
+  const uint32_t finc = above_c + wave_inclusive_scan(fc);
+  const int J = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(finc >= want)) - 1);
+  *above = (uint32_t)__builtin_amdgcn_readlane((int)(finc - fc), J);
+  return (int)(bucket << 6) + 63 - J;
+}
+
 // Writes the nonzero bins of a 4096-bin LDS level-0 histogram as the list of
 // slot `slot` of query t: the entry count, then entries (bin << 20 | count)
 // in descending bin order. kBlock threads (blockDim.x) scan 4096 / kBlock

@@ -167,16 +167,8 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_select(SeqMeta m, int k,
   bool done = false;
   if (nslots <= 64) {
     if (wave == 0) {
-#pragma unroll
-      for (int q = 0; q < kHist0Bins / 256; ++q) *(uint4 *)(hist + 4 * (lane * (kHist0Bins / 256) + q)) = make_uint4(0u, 0u, 0u, 0u);
-      // (the LDS operations of one wave take effect in order)
-      if (lane < nslots) {
-#pragma unroll
-        for (int i = 1; i < 16; ++i)
-          if ((uint32_t)i <= wd[0]) atomicAdd(&hist[wd[i] >> 20], wd[i] & 0xFFFFFu);
-      }
       uint32_t ab;
-      const int b = wave_find_threshold_bin<kHist0Bins>(hist, (uint32_t)k, &ab);
+      const int b = wave_heads_threshold_bin(hist, wd, nslots, (uint32_t)k, &ab);
       // the heads are exact down to the lowest bin read from every cut list
       const bool cut = __ballot(lane < nslots && wd[0] > 15u && (int)(wd[15] >> 20) > b) != 0;
       const uint32_t cnt = lane < nslots ? head_count_ge(wd, (uint32_t)b) : 0u;
