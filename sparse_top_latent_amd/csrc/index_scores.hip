@@ -273,12 +273,15 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
 
 int index_fp8_iters(int T, int max_kv_len) {
   // a workgroup scores 4 * iters tiles of 64 keys; aim for about two
-  // workgroups per CU over the whole batch (4096 keys each for 16 x 128K)
+  // workgroups per CU over the whole batch (4096 keys each for 16 x 128K).
+  // At most 4096 keys per workgroup: the grid is sized by max_kv_len, and
+  // with sequences of mixed length most of a long grid row has work only for
+  // the longest sequences, so larger workgroups would leave CUs idle.
   const int64_t keys = (int64_t)T * max_kv_len;
   const int64_t per_iter = 2048LL * kIdxTileKeys;
   int64_t it = (keys + per_iter - 1) / per_iter;
   if (it < 2) it = 2;
-  if (it > 32) it = 32;
+  if (it > 16) it = 16;
   return (int)it;
 }
 
@@ -311,8 +314,8 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
   static bool attr = false;
   if (!attr) {
-    // ring plus the largest score stage (128 tiles)
-    const int max_smem = kIdxRing * kIdxStepBytes + (kIdxStageScores ? 128 * kIdxTileKeys * 4 : 0);
+    // ring plus the largest score stage (64 tiles)
+    const int max_smem = kIdxRing * kIdxStepBytes + (kIdxStageScores ? 64 * kIdxTileKeys * 4 : 0);
     (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
     (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing>,
