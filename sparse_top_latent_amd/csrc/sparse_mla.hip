@@ -142,6 +142,10 @@ constexpr bool kMlaEightWaves = true;         // bf16: two waves per SIMD (k_mla
 
 constexpr size_t kBfSmem = (size_t)kMaxTiles * kTileBytes;
 constexpr size_t kMxSmem = (size_t)kMaxTiles * kMxRawBytes + kTileBytes + kMlaRowsPerSplit * kScales;
+// k_mla_split8<MXFP8>: the raw tiles, one expanded bf16 tile per wave set, the scales
+constexpr size_t kMx8Smem = (size_t)kMaxTiles * kMxRawBytes + 2 * kTileBytes + kMlaRowsPerSplit * kScales;
+static_assert(kMx8Smem + kMlaRowsPerSplit * 8 <= 160 * 1024, "LDS of k_mla_split8<MXFP8>");
+static_assert(4 * kCt * 64 * 16 + 2 * 4 * 64 * 8 <= kMx8Smem, "the set merge reuses the tile area");
 
 // 16 zero bytes: the DMA source of rows that are not selected
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
@@ -426,6 +430,7 @@ __device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int 
   }
 }
 
+template <bool kMx>
 __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
                                                     float2 *__restrict__ ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -454,28 +459,74 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
 #pragma unroll
   for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
 
+  // MXFP8: raw tiles at smem, the set's expanded bf16 tile after them, then
+  // the scales of the 128 rows
+  unsigned char *cvt = smem + kMaxTiles * kMxRawBytes + set * kTileBytes;
+  uint8_t *scl = (uint8_t *)(smem + kMaxTiles * kMxRawBytes + 2 * kTileBytes);
+  constexpr int kSclPer = (kMlaRowsPerSplit * 9 + 511) / 512;  // two-byte scale words per thread
+  uint32_t sreg[kSclPer];
+  if (kMx) {
+    // scales as 9 two-byte words per row, loaded without branches (unselected
+    // rows and padding read the zero block) and replaced by 2^0 afterwards
+#pragma unroll
+    for (int j = 0; j < kSclPer; ++j) {
+      const int i = tid + 512 * j;
+      const int64_t gr = i < kMlaRowsPerSplit * 9 ? rows[i / 9] : -1;
+      const uint16_t *src = gr >= 0 ? (const uint16_t *)(a.kv_scale + gr * kScales + 2 * (i % 9))
+                                    : (const uint16_t *)g_zero16;
+      sreg[j] = *src;
+      if (gr < 0) sreg[j] = 0x7F7Fu;
+    }
+  }
   // gather: the set's 256 threads copy its tiles set and set + 2 (tiles past
-  // ntiles read the zero block, so every thread issues kBfDma copies a tile)
+  // ntiles read the zero block, so every thread issues the same number of
+  // copies a tile). bf16: rows land swizzled in their tile; MXFP8: the raw
+  // 576-byte rows land in order (36 chunks each) and are expanded below.
   auto issue_tile = [&](int tt) {
-    unsigned char *tbase = smem + tt * kTileBytes;
-    int64_t gr[kBfDma];
+    if (!kMx) {
+      unsigned char *tbase = smem + tt * kTileBytes;
+      int64_t gr[kBfDma];
 #pragma unroll
-    for (int j = 0; j < kBfDma; ++j)
-      gr[j] = tt < ntiles ? rows[tt * kTile + (j * 256 + st) / kRowChunks] : -1;
+      for (int j = 0; j < kBfDma; ++j)
+        gr[j] = tt < ntiles ? rows[tt * kTile + (j * 256 + st) / kRowChunks] : -1;
 #pragma unroll
-    for (int j = 0; j < kBfDma; ++j) {
-      const int c = j * 256 + st;
-      const int r = c / kRowChunks;
-      const int col = (c - r * kRowChunks) ^ row_swz(r);
-      const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
-                                   : (const void *)g_zero16;
-      dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
+      for (int j = 0; j < kBfDma; ++j) {
+        const int c = j * 256 + st;
+        const int r = c / kRowChunks;
+        const int col = (c - r * kRowChunks) ^ row_swz(r);
+        const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
+                                     : (const void *)g_zero16;
+        dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
+      }
+    } else {
+      unsigned char *tbase = smem + tt * kMxRawBytes;
+      int64_t gr[kMxDma];
+#pragma unroll
+      for (int j = 0; j < kMxDma; ++j) {
+        const int c = j * 256 + st;  // raw chunk slot: row c / 36, 16 values
+        gr[j] = (c < kMxChunks && tt < ntiles) ? rows[tt * kTile + c / 36] : -1;
+      }
+#pragma unroll
+      for (int j = 0; j < kMxDma; ++j) {
+        const int c = j * 256 + st;
+        const int r = c / 36;
+        const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + gr[j] * kD + (c - r * 36) * 16)
+                                     : (const void *)g_zero16;
+        dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
+      }
     }
   };
   // both tiles of the set at once: with 8 waves issuing, the gather runs near
   // the random-row rate of the memory system
   issue_tile(set);
   issue_tile(set + 2);
+  if (kMx) {
+#pragma unroll
+    for (int j = 0; j < kSclPer; ++j) {
+      const int i = tid + 512 * j;
+      if (i < kMlaRowsPerSplit * 9) *(uint16_t *)(scl + (i / 9) * kScales + 2 * (i % 9)) = (uint16_t)sreg[j];
+    }
+  }
 
   v4f acc[kCt];
 #pragma unroll
@@ -489,11 +540,34 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
 
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    if (u == 0) wait_vmcnt<kBfDma>(); else wait_vmcnt<0>();
-    barrier_lds();  // tiles 2u and 2u + 1 have landed
+    if (u == 0) wait_vmcnt<kMx ? kMxDma : kBfDma>(); else wait_vmcnt<0>();
+    barrier_lds();  // tiles 2u and 2u + 1 have landed (MXFP8: and the scales; u = 1: the set's expanded tile is free)
     const int tt = set + 2 * u;
-    if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
     const unsigned char *tile = smem + tt * kTileBytes;
+    if (kMx) {
+      // the set's 256 threads expand raw tile tt into the set's bf16 tile,
+      // each 16-value chunk with the E8M0 scale of its 32-channel block
+      if (tt < ntiles) {
+        const unsigned char *raw = smem + tt * kMxRawBytes;
+        for (int c = st; c < kMxChunks; c += 256) {
+          const int r = c / 36, blk = c - r * 36;  // 16 values = channels blk*16 ..
+          const v4i v = *(const v4i *)(raw + c * 16);
+          const float sc = e8m0_to_f32(scl[(tt * kTile + r) * kScales + (blk >> 1)]);
+          const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+          uint32_t o[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, false));
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, true));
+          }
+          *(v4i *)(cvt + swz(r, 2 * blk) * 16) = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+          *(v4i *)(cvt + swz(r, 2 * blk + 1) * 16) = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+        }
+      }
+      barrier_lds();  // the set's expanded tile is complete
+      tile = cvt;
+    }
+    if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
     const uint32_t tvalid = (uint32_t)((tt < 2 ? valid01 : valid23) >> (32 * (tt & 1)));
     if (tvalid == 0u) continue;  // no selected row in this tile (uniform)
     // the two 16-row halves are independent accumulation chains, interleaved
@@ -725,15 +799,19 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
     (void)hipFuncSetAttribute((const void *)k_mla_split<true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8,
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
     (void)hipGetLastError();
     attr = true;
   }
-  if (a.kv_dtype == SGA_MXFP8_E4M3FN)
+  if (a.kv_dtype == SGA_MXFP8_E4M3FN && kMlaEightWaves)
+    hipLaunchKernelGGL(k_mla_split8<true>, dim3(S, a.T), dim3(512), kMx8Smem, s, a, opart, ml);
+  else if (a.kv_dtype == SGA_MXFP8_E4M3FN)
     hipLaunchKernelGGL(k_mla_split<true>, dim3(S, a.T), dim3(256), kMxSmem, s, a, opart, ml);
   else if (kMlaEightWaves)
-    hipLaunchKernelGGL(k_mla_split8, dim3(S, a.T), dim3(512), kBfSmem, s, a, opart, ml);
+    hipLaunchKernelGGL(k_mla_split8<false>, dim3(S, a.T), dim3(512), kBfSmem, s, a, opart, ml);
   else
     hipLaunchKernelGGL(k_mla_split<false>, dim3(S, a.T), dim3(256), kBfSmem, s, a, opart, ml);
   return hipGetLastError();
