@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kF32Block) void k_mla_f32(MlaArgs a) {
 constexpr int kH = 64, kDc = 512, kD = 576;  // d_rope = 64
 constexpr int kTile = 32;                     // rows per LDS tile
 constexpr int kMaxTiles = kMlaRowsPerSplit / kTile;
+constexpr int kMaxRounds = 4;                 // rounds of 128 rows one split kernel workgroup may take
 constexpr int kRowChunks = kD * 2 / 16;       // 72 16-byte chunks per bf16 row
 constexpr int kTileBytes = kTile * kD * 2;    // 36,864
 constexpr int kBfDma = kTile * kRowChunks / 256;  // 9 DMA issues per thread per tile
@@ -144,7 +145,7 @@ constexpr size_t kBfSmem = (size_t)kMaxTiles * kTileBytes;
 constexpr size_t kMxSmem = (size_t)kMaxTiles * kMxRawBytes + kTileBytes + kMlaRowsPerSplit * kScales;
 // k_mla_split8<MXFP8>: the raw tiles, one expanded bf16 tile per wave set, the scales
 constexpr size_t kMx8Smem = (size_t)kMaxTiles * kMxRawBytes + 2 * kTileBytes + kMlaRowsPerSplit * kScales;
-static_assert(kMx8Smem + kMlaRowsPerSplit * 8 <= 160 * 1024, "LDS of k_mla_split8<MXFP8>");
+static_assert(kMx8Smem + kMaxRounds * kMlaRowsPerSplit * 4 <= 160 * 1024, "LDS of k_mla_split8<MXFP8>");
 static_assert(4 * kCt * 64 * 16 + 2 * 4 * 64 * 8 <= kMx8Smem, "the set merge reuses the tile area");
 
 // 16 zero bytes: the DMA source of rows that are not selected
@@ -430,29 +431,30 @@ __device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int 
   }
 }
 
-template <bool kMx>
+template <bool kMx, int R>
 __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
                                                     float2 *__restrict__ ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int64_t rows[kMlaRowsPerSplit];
+  // cache row of each selected row of the split (-1: none); int32 row ids
+  // keep the gather's address batches small in registers
+  __shared__ int32_t rows[R * kMlaRowsPerSplit];
   const int split = blockIdx.x, t = blockIdx.y, S = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave & 3, set = wave >> 2, st = tid & 255;
   const int g = lane >> 4, c16 = lane & 15;
-  const int r0 = split * kMlaRowsPerSplit;
-  const int nrows = min(kMlaRowsPerSplit, a.k - r0);  // >= 1: one split per 128 selected rows
-  const int ntiles = (nrows + kTile - 1) / kTile;
+  // this split: R rounds of 128 selected rows
+  const int r0 = split * R * kMlaRowsPerSplit;
+  const int nrows = min(R * kMlaRowsPerSplit, a.k - r0);  // >= 1
+  const int rounds = (nrows + kMlaRowsPerSplit - 1) / kMlaRowsPerSplit;
   // the selected positions are requested first (clamped, unconditional) so
-  // that their latency overlaps the sequence lookup
-  int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(tid & (kMlaRowsPerSplit - 1), nrows - 1)];
+  // that their latency overlaps the sequence lookup; thread i takes row i
+  const int my_row = min(tid, R * kMlaRowsPerSplit - 1);
+  int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(my_row, nrows - 1)];
   int64_t start;
   const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
-  if (tid < kMlaRowsPerSplit) rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? start + pos : -1;
+  if (tid < R * kMlaRowsPerSplit) rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? (int32_t)(start + pos) : -1;
   __syncthreads();  // rows[] ready
-  // validity of the 128 rows as two wave-wide bit masks (rows past nrows are -1)
-  const uint64_t valid01 = __ballot(rows[lane] >= 0);
-  const uint64_t valid23 = __ballot(rows[64 + lane] >= 0);
   const int head = hg * 16 + c16;
   const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
   v8bf qreg[kKsteps];
@@ -460,73 +462,10 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
 
   // MXFP8: raw tiles at smem, the set's expanded bf16 tile after them, then
-  // the scales of the 128 rows
+  // the scales of the round's 128 rows
   unsigned char *cvt = smem + kMaxTiles * kMxRawBytes + set * kTileBytes;
   uint8_t *scl = (uint8_t *)(smem + kMaxTiles * kMxRawBytes + 2 * kTileBytes);
   constexpr int kSclPer = (kMlaRowsPerSplit * 9 + 511) / 512;  // two-byte scale words per thread
-  uint32_t sreg[kSclPer];
-  if (kMx) {
-    // scales as 9 two-byte words per row, loaded without branches (unselected
-    // rows and padding read the zero block) and replaced by 2^0 afterwards
-#pragma unroll
-    for (int j = 0; j < kSclPer; ++j) {
-      const int i = tid + 512 * j;
-      const int64_t gr = i < kMlaRowsPerSplit * 9 ? rows[i / 9] : -1;
-      const uint16_t *src = gr >= 0 ? (const uint16_t *)(a.kv_scale + gr * kScales + 2 * (i % 9))
-                                    : (const uint16_t *)g_zero16;
-      sreg[j] = *src;
-      if (gr < 0) sreg[j] = 0x7F7Fu;
-    }
-  }
-  // gather: the set's 256 threads copy its tiles set and set + 2 (tiles past
-  // ntiles read the zero block, so every thread issues the same number of
-  // copies a tile). bf16: rows land swizzled in their tile; MXFP8: the raw
-  // 576-byte rows land in order (36 chunks each) and are expanded below.
-  auto issue_tile = [&](int tt) {
-    if (!kMx) {
-      unsigned char *tbase = smem + tt * kTileBytes;
-      int64_t gr[kBfDma];
-#pragma unroll
-      for (int j = 0; j < kBfDma; ++j)
-        gr[j] = tt < ntiles ? rows[tt * kTile + (j * 256 + st) / kRowChunks] : -1;
-#pragma unroll
-      for (int j = 0; j < kBfDma; ++j) {
-        const int c = j * 256 + st;
-        const int r = c / kRowChunks;
-        const int col = (c - r * kRowChunks) ^ row_swz(r);
-        const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
-                                     : (const void *)g_zero16;
-        dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
-      }
-    } else {
-      unsigned char *tbase = smem + tt * kMxRawBytes;
-      int64_t gr[kMxDma];
-#pragma unroll
-      for (int j = 0; j < kMxDma; ++j) {
-        const int c = j * 256 + st;  // raw chunk slot: row c / 36, 16 values
-        gr[j] = (c < kMxChunks && tt < ntiles) ? rows[tt * kTile + c / 36] : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < kMxDma; ++j) {
-        const int c = j * 256 + st;
-        const int r = c / 36;
-        const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + gr[j] * kD + (c - r * 36) * 16)
-                                     : (const void *)g_zero16;
-        dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
-      }
-    }
-  };
-  // both tiles of the set at once: with 8 waves issuing, the gather runs near
-  // the random-row rate of the memory system
-  issue_tile(set);
-  issue_tile(set + 2);
-  if (kMx) {
-#pragma unroll
-    for (int j = 0; j < kSclPer; ++j) {
-      const int i = tid + 512 * j;
-      if (i < kMlaRowsPerSplit * 9) *(uint16_t *)(scl + (i / 9) * kScales + 2 * (i % 9)) = (uint16_t)sreg[j];
-    }
-  }
 
   v4f acc[kCt];
 #pragma unroll
@@ -539,90 +478,166 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   const int q = (c16 & 3) >> 1, vsub = (c16 & 1) * 8;
 
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if (u == 0) wait_vmcnt<kMx ? kMxDma : kBfDma>(); else wait_vmcnt<0>();
-    barrier_lds();  // tiles 2u and 2u + 1 have landed (MXFP8: and the scales; u = 1: the set's expanded tile is free)
-    const int tt = set + 2 * u;
-    const unsigned char *tile = smem + tt * kTileBytes;
+  for (int rd = 0; rd < R; ++rd) {
+    if (rd >= rounds) break;  // uniform over the workgroup
+    if (rd > 0) barrier_lds();  // every wave is done with the previous round's tiles
+    const int32_t *rrows = rows + rd * kMlaRowsPerSplit;
+    const int ntiles = (min(kMlaRowsPerSplit, nrows - rd * kMlaRowsPerSplit) + kTile - 1) / kTile;
+    // validity of the round's 128 rows as two wave-wide bit masks (rows past
+    // nrows are -1)
+    const uint64_t valid01 = __ballot(rrows[lane] >= 0);
+    const uint64_t valid23 = __ballot(rrows[64 + lane] >= 0);
+    uint32_t sreg[kSclPer];
     if (kMx) {
-      // the set's 256 threads expand raw tile tt into the set's bf16 tile,
-      // each 16-value chunk with the E8M0 scale of its 32-channel block
-      if (tt < ntiles) {
-        const unsigned char *raw = smem + tt * kMxRawBytes;
-        for (int c = st; c < kMxChunks; c += 256) {
-          const int r = c / 36, blk = c - r * 36;  // 16 values = channels blk*16 ..
-          const v4i v = *(const v4i *)(raw + c * 16);
-          const float sc = e8m0_to_f32(scl[(tt * kTile + r) * kScales + (blk >> 1)]);
-          const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-          uint32_t o[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, false));
-            o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, true));
-          }
-          *(v4i *)(cvt + swz(r, 2 * blk) * 16) = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-          *(v4i *)(cvt + swz(r, 2 * blk + 1) * 16) = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      // scales as 9 two-byte words per row, loaded without branches (unselected
+      // rows and padding read the zero block) and replaced by 2^0 afterwards
+  #pragma unroll
+      for (int j = 0; j < kSclPer; ++j) {
+        const int i = tid + 512 * j;
+        const int64_t gr = i < kMlaRowsPerSplit * 9 ? (int64_t)rrows[i / 9] : -1;
+        const uint16_t *src = gr >= 0 ? (const uint16_t *)(a.kv_scale + gr * kScales + 2 * (i % 9))
+                                      : (const uint16_t *)g_zero16;
+        sreg[j] = *src;
+        if (gr < 0) sreg[j] = 0x7F7Fu;
+      }
+    }
+    // gather: the set's 256 threads copy its tiles set and set + 2 (tiles past
+    // ntiles read the zero block, so every thread issues the same number of
+    // copies a tile). bf16: rows land swizzled in their tile; MXFP8: the raw
+    // 576-byte rows land in order (36 chunks each) and are expanded below.
+    auto issue_tile = [&](int tt) {
+      if (!kMx) {
+        unsigned char *tbase = smem + tt * kTileBytes;
+        int64_t gr[kBfDma];
+  #pragma unroll
+        for (int j = 0; j < kBfDma; ++j)
+          gr[j] = tt < ntiles ? rrows[tt * kTile + (j * 256 + st) / kRowChunks] : -1;
+  #pragma unroll
+        for (int j = 0; j < kBfDma; ++j) {
+          const int c = j * 256 + st;
+          const int r = c / kRowChunks;
+          const int col = (c - r * kRowChunks) ^ row_swz(r);
+          const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + (int64_t)gr[j] * (kD * 2) + col * 16)
+                                       : (const void *)g_zero16;
+          dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
+        }
+      } else {
+        unsigned char *tbase = smem + tt * kMxRawBytes;
+        int64_t gr[kMxDma];
+  #pragma unroll
+        for (int j = 0; j < kMxDma; ++j) {
+          const int c = j * 256 + st;  // raw chunk slot: row c / 36, 16 values
+          gr[j] = (c < kMxChunks && tt < ntiles) ? rrows[tt * kTile + c / 36] : -1;
+        }
+  #pragma unroll
+        for (int j = 0; j < kMxDma; ++j) {
+          const int c = j * 256 + st;
+          const int r = c / 36;
+          const void *src = gr[j] >= 0 ? (const void *)((const uint8_t *)a.kv + (int64_t)gr[j] * kD + (c - r * 36) * 16)
+                                       : (const void *)g_zero16;
+          dma16(src, tbase + (j * 256 + (wave & 3) * 64) * 16);
         }
       }
-      barrier_lds();  // the set's expanded tile is complete
-      tile = cvt;
+    };
+    // both tiles of the set at once: with 8 waves issuing, the gather runs near
+    // the random-row rate of the memory system
+    issue_tile(set);
+    issue_tile(set + 2);
+    if (kMx) {
+  #pragma unroll
+      for (int j = 0; j < kSclPer; ++j) {
+        const int i = tid + 512 * j;
+        if (i < kMlaRowsPerSplit * 9) *(uint16_t *)(scl + (i / 9) * kScales + 2 * (i % 9)) = (uint16_t)sreg[j];
+      }
     }
-    if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
-    const uint32_t tvalid = (uint32_t)((tt < 2 ? valid01 : valid23) >> (32 * (tt & 1)));
-    if (tvalid == 0u) continue;  // no selected row in this tile (uniform)
-    // the two 16-row halves are independent accumulation chains, interleaved
-    // so that consecutive MFMAs do not wait on each other
-    v4f sv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        sv[rt] = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(rt * 16 + c16, 4 * ks + g) * 16)), qreg[ks], sv[rt]);
-    float lg[8];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = (tvalid >> ((j >> 2) * 16 + 4 * g + (j & 3))) & 1u;
-      lg[j] = ok ? sv[j >> 2][j & 3] * scale2 : -INFINITY;
-      mt = fmaxf(mt, lg[j]);
+
+  #pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 0) wait_vmcnt<kMx ? kMxDma : kBfDma>(); else wait_vmcnt<0>();
+      barrier_lds();  // tiles 2u and 2u + 1 have landed (MXFP8: and the scales; u = 1: the set's expanded tile is free)
+      const int tt = set + 2 * u;
+      const unsigned char *tile = smem + tt * kTileBytes;
+      if (kMx) {
+        // the set's 256 threads expand raw tile tt into the set's bf16 tile,
+        // each 16-value chunk with the E8M0 scale of its 32-channel block
+        if (tt < ntiles) {
+          const unsigned char *raw = smem + tt * kMxRawBytes;
+          for (int c = st; c < kMxChunks; c += 256) {
+            const int r = c / 36, blk = c - r * 36;  // 16 values = channels blk*16 ..
+            const v4i v = *(const v4i *)(raw + c * 16);
+            const float sc = e8m0_to_f32(scl[(tt * kTile + r) * kScales + (blk >> 1)]);
+            const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+            uint32_t o[8];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, false));
+              o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, true));
+            }
+            *(v4i *)(cvt + swz(r, 2 * blk) * 16) = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+            *(v4i *)(cvt + swz(r, 2 * blk + 1) * 16) = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+          }
+        }
+        barrier_lds();  // the set's expanded tile is complete
+        tile = cvt;
+      }
+      if (tt >= ntiles) continue;  // uniform over the wave; no barrier skipped
+      const uint32_t tvalid = (uint32_t)((tt < 2 ? valid01 : valid23) >> (32 * (tt & 1)));
+      if (tvalid == 0u) continue;  // no selected row in this tile (uniform)
+      // the two 16-row halves are independent accumulation chains, interleaved
+      // so that consecutive MFMAs do not wait on each other
+      v4f sv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  #pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks)
+  #pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          sv[rt] = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(rt * 16 + c16, 4 * ks + g) * 16)), qreg[ks], sv[rt]);
+      float lg[8];
+      float mt = -INFINITY;
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = (tvalid >> ((j >> 2) * 16 + 4 * g + (j & 3))) & 1u;
+        lg[j] = ok ? sv[j >> 2][j & 3] * scale2 : -INFINITY;
+        mt = fmaxf(mt, lg[j]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      if (!(mt > -INFINITY)) continue;  // no selected row in this tile (uniform over heads)
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+  #pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) acc[ct] *= alpha;
+        m_run = m_new;
+      }
+      float p[8], ps = 0.0f;
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = exp2f(lg[j] - m_run);
+        ps += p[j];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run += ps;
+      v8bf pb;
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
+      int voff[4];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) voff[i] = (vr * kRowChunks + ((2 * i + q) ^ row_swz(vr))) * 16 + vsub;
+      {
+        pv_block_b<0>(tile, voff, pb, acc);
+        pv_block_b<1>(tile, voff, pb, acc);
+        pv_block_b<2>(tile, voff, pb, acc);
+        pv_block_b<3>(tile, voff, pb, acc);
+        pv_block_b<4>(tile, voff, pb, acc);
+        pv_block_b<5>(tile, voff, pb, acc);
+        pv_block_b<6>(tile, voff, pb, acc);
+        pv_block_b<7>(tile, voff, pb, acc);
+      }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    if (!(mt > -INFINITY)) continue;  // no selected row in this tile (uniform over heads)
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) acc[ct] *= alpha;
-      m_run = m_new;
-    }
-    float p[8], ps = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(lg[j] - m_run);
-      ps += p[j];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run += ps;
-    v8bf pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-    int voff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) voff[i] = (vr * kRowChunks + ((2 * i + q) ^ row_swz(vr))) * 16 + vsub;
-    {
-      pv_block_b<0>(tile, voff, pb, acc);
-      pv_block_b<1>(tile, voff, pb, acc);
-      pv_block_b<2>(tile, voff, pb, acc);
-      pv_block_b<3>(tile, voff, pb, acc);
-      pv_block_b<4>(tile, voff, pb, acc);
-      pv_block_b<5>(tile, voff, pb, acc);
-      pv_block_b<6>(tile, voff, pb, acc);
-      pv_block_b<7>(tile, voff, pb, acc);
-    }
-  }
+
+  }  // rounds
 
   // merge the two sets through LDS (the tile area is free now): set 0 finishes
   // channel tiles 0..15 and set 1 channel tiles 16..31, each with the other
@@ -783,6 +798,26 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static int mla_splits(int k) { return (k + kMlaRowsPerSplit - 1) / kMlaRowsPerSplit; }
 
+// Rounds of 128 rows per split workgroup (R) and splits per query (S) of the
+// 8-wave split kernel: the fewest rounds that fit all workgroups on the
+// chip's CUs at once (one per CU: the tiles fill its LDS): 1, 2 or 4.
+// More rounds mean fewer partials to write and combine, and no second wave of
+// workgroups waiting for a CU.
+static void mla_plan(int T, int k, int *R, int *S) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    (void)hipGetLastError();
+  }
+  int r = 1;
+  while (r < kMaxRounds && (int64_t)T * ((k + r * kMlaRowsPerSplit - 1) / (r * kMlaRowsPerSplit)) > cus) r *= 2;
+  *R = kMlaEightWaves ? r : 1;
+  *S = (k + *R * kMlaRowsPerSplit - 1) / (*R * kMlaRowsPerSplit);
+}
+
 size_t mla_split_ws_bytes(int T, int k) {
   size_t S = (size_t)mla_splits(k);
   return align256((size_t)T * S * kH * kDc * 2) + align256((size_t)T * S * kH * sizeof(float2));
@@ -790,7 +825,8 @@ size_t mla_split_ws_bytes(int T, int k) {
 
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int S = mla_splits(a.k);
+  int R, S;
+  mla_plan(a.T, a.k, &R, &S);
   uint16_t *opart = (uint16_t *)ws;
   float2 *ml = (float2 *)((char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
   static bool attr = false;
@@ -799,19 +835,39 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
     (void)hipFuncSetAttribute((const void *)k_mla_split<true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<false>,
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 1>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<true>,
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 2>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 4>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<true, 1>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<true, 2>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<true, 4>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
     (void)hipGetLastError();
     attr = true;
   }
-  if (a.kv_dtype == SGA_MXFP8_E4M3FN && kMlaEightWaves)
-    hipLaunchKernelGGL(k_mla_split8<true>, dim3(S, a.T), dim3(512), kMx8Smem, s, a, opart, ml);
-  else if (a.kv_dtype == SGA_MXFP8_E4M3FN)
+  const dim3 grid(S, a.T);
+  const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
+  if (kMlaEightWaves && mx) {
+    if (R == 4)
+      hipLaunchKernelGGL((k_mla_split8<true, 4>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
+    else if (R == 2)
+      hipLaunchKernelGGL((k_mla_split8<true, 2>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
+    else
+      hipLaunchKernelGGL((k_mla_split8<true, 1>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
+  } else if (kMlaEightWaves) {
+    if (R == 4)
+      hipLaunchKernelGGL((k_mla_split8<false, 4>), grid, dim3(512), kBfSmem, s, a, opart, ml);
+    else if (R == 2)
+      hipLaunchKernelGGL((k_mla_split8<false, 2>), grid, dim3(512), kBfSmem, s, a, opart, ml);
+    else
+      hipLaunchKernelGGL((k_mla_split8<false, 1>), grid, dim3(512), kBfSmem, s, a, opart, ml);
+  } else if (mx)
     hipLaunchKernelGGL(k_mla_split<true>, dim3(S, a.T), dim3(256), kMxSmem, s, a, opart, ml);
-  else if (kMlaEightWaves)
-    hipLaunchKernelGGL(k_mla_split8<false>, dim3(S, a.T), dim3(512), kBfSmem, s, a, opart, ml);
   else
     hipLaunchKernelGGL(k_mla_split<false>, dim3(S, a.T), dim3(256), kBfSmem, s, a, opart, ml);
   return hipGetLastError();
@@ -819,12 +875,17 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
 
 hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int S = mla_splits(a.k);
+  int R, S;
+  mla_plan(a.T, a.k, &R, &S);
   const uint16_t *opart = (const uint16_t *)ws;
   const float2 *ml = (const float2 *)((const char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
   const dim3 grid(kCt / kCombCt, 4, a.T), block(64 * kCombCt);
   if (S == kMaxSplits)
     hipLaunchKernelGGL(k_mla_combine<kMaxSplits>, grid, block, 0, s, a, opart, ml, S);
+  else if (S == kMaxSplits / 2)
+    hipLaunchKernelGGL(k_mla_combine<kMaxSplits / 2>, grid, block, 0, s, a, opart, ml, S);
+  else if (S == kMaxSplits / 4)
+    hipLaunchKernelGGL(k_mla_combine<kMaxSplits / 4>, grid, block, 0, s, a, opart, ml, S);
   else
     hipLaunchKernelGGL(k_mla_combine<0>, grid, block, 0, s, a, opart, ml, S);
   return hipGetLastError();

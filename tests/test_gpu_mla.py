@@ -68,6 +68,26 @@ def test_mla_full_dims_small(precision, out_dtype):
     _compare(case, out, lse, ref, f"{precision}/{out_dtype}")
 
 
+# Enough queries that one split workgroup takes several rounds of 128 rows
+# (40 x 16 groups of 128 exceed the CU count, so 4 rounds of 4 splits), with
+# queries short of k (padded lists) among them.
+ROUND_LENS = [2600, 3100, 2300, 4000]
+ROUND_Q = [(b, p) for b, (L, ps) in enumerate(zip(ROUND_LENS, [(0.3, 0.8, 0.99), (0.5, 0.7, 0.9, 0.999),
+                                                              (0.2, 0.6, 0.95), (0.1, 0.4, 0.55, 0.999)]))
+           for p in [int(L * f) for f in ps]]
+ROUND_Q = (ROUND_Q * 3)[:40]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_mla_split_rounds(precision):
+    case = make_custom(ROUND_LENS, ROUND_Q, dims=FULL_DIMS, precision=precision, seed=9,
+                       device="cuda", softmax_scale=1 / 24)
+    ref, idx = _oracle(case)
+    say(f"case mla rounds {precision}, {case.num_q} queries")
+    out, lse = _run_mla(case, idx)
+    _compare(case, out, lse, ref, f"rounds/{precision}")
+
+
 def test_mla_order_invariance_and_invalid_entries():
     case = make_custom(SMALL_LENS, SMALL_Q, dims=FULL_DIMS, precision="bf16", seed=6,
                        device="cuda", softmax_scale=1 / 24)
