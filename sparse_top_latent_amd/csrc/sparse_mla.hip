@@ -14,12 +14,11 @@
 //
 // Kernels:
 //  * k_mla_f32: generic fp32 path, one workgroup per (query, head).
-//  * k_mla_split8 / k_mla_split (MI355X path, H = 64, Dc = 512, Dr = 64): the
-//    selected rows of a query are cut into splits of 128; one workgroup per
-//    (split, query) gathers 32-row tiles into LDS (bf16, or MXFP8 expanded
-//    exactly to bf16). In k_mla_split (MXFP8) each of 4 waves owns 16 heads;
-//    k_mla_split8 (bf16) has 8 waves, two sets of 4 that take alternate tiles
-//    and merge at the end. Per wave:
+//  * k_mla_split8 (MI355X path, H = 64, Dc = 512, Dr = 64): the selected rows
+//    of a query are cut into splits of 128, 256 or 512 (one, two or four
+//    rounds of 128); one workgroup per (split, query) gathers 32-row tiles
+//    into LDS (bf16, or MXFP8 expanded exactly to bf16). Its 8 waves form two
+//    sets of 4 that take alternate tiles and merge at the end. Per wave:
 //      S^T = rows . Q^T  with bf16 16x16x32 MFMA (the query slice stays in VGPRs),
 //      online softmax per head in fp32 (exp2 domain),
 //      O^T += V^T . P^T  with bf16 MFMA; P^T comes straight from the S^T
@@ -139,10 +138,8 @@ constexpr int kScales = kD / 32;              // 18 E8M0 scales per row
 constexpr int kKsteps = kD / 32;              // 18 MFMA k-steps for q . row
 constexpr int kCt = kDc / 16;                 // 32 channel tiles of the value
 constexpr float kRescaleSlack = 8.0f;         // log2 headroom before the running max moves
-constexpr bool kMlaEightWaves = true;         // bf16: two waves per SIMD (k_mla_split8)
 
 constexpr size_t kBfSmem = (size_t)kMaxTiles * kTileBytes;
-constexpr size_t kMxSmem = (size_t)kMaxTiles * kMxRawBytes + kTileBytes + kMlaRowsPerSplit * kScales;
 // k_mla_split8<MXFP8>: the raw tiles, one expanded bf16 tile per wave set, the scales
 constexpr size_t kMx8Smem = (size_t)kMaxTiles * kMxRawBytes + 2 * kTileBytes + kMlaRowsPerSplit * kScales;
 static_assert(kMx8Smem + kMaxRounds * kMlaRowsPerSplit * 4 <= 160 * 1024, "LDS of k_mla_split8<MXFP8>");
@@ -175,18 +172,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until this thread's DMAs of tile `tt` have landed: kPer DMA issues per
-// tile were made for all kMaxTiles tiles, in order.
-template <int kPer>
-__device__ __forceinline__ void wait_tile(int tt) {
-  switch (tt) {
-    case 0: wait_vmcnt<3 * kPer>(); break;
-    case 1: wait_vmcnt<2 * kPer>(); break;
-    case 2: wait_vmcnt<kPer>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
 // Workgroup barrier that waits for this wave's LDS operations but not for its
 // outstanding global->LDS DMAs (a __syncthreads() would drain those too).
 __device__ __forceinline__ void barrier_lds() {
@@ -200,207 +185,8 @@ __device__ __forceinline__ void dma16(const void *src, unsigned char *lds_wave_b
   __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
 }
 
-template <bool kMx>
-__global__ __launch_bounds__(256) void k_mla_split(MlaArgs a, uint16_t *__restrict__ opart,
-                                                   float2 *__restrict__ ml) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int64_t rows[kMlaRowsPerSplit];
-  const int split = blockIdx.x, t = blockIdx.y, S = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  int64_t start;
-  const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
-  const int r0 = split * kMlaRowsPerSplit;
-  const int nrows = min(kMlaRowsPerSplit, a.k - r0);
-  const int ntiles = (nrows + kTile - 1) / kTile;
-  if (tid < kMlaRowsPerSplit) {
-    int32_t pos = tid < nrows ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
-    rows[tid] = (pos >= 0 && pos < L) ? start + pos : -1;
-  }
-  __syncthreads();  // rows[] ready
-  // this wave's 16 heads: B operand of S^T = rows . Q^T, kept in VGPRs
-  const int head = wave * 16 + c16;
-  const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
-  v8bf qreg[kKsteps];
-#pragma unroll
-  for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
-
-  unsigned char *tiles = smem;                                  // bf16: kMaxTiles x 36 KB
-  unsigned char *cvt = smem + kMaxTiles * kMxRawBytes;          // MXFP8: expanded tile
-  uint8_t *scl = (uint8_t *)(cvt + kTileBytes);                 // MXFP8: [128][18] scales
-  uint32_t sreg[5];
-  if (kMx) {
-    // scales as 9 two-byte words per row, loaded without branches (unselected
-    // rows and padding read the zero block) and replaced by 2^0 afterwards
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      const int i = tid + 256 * j;
-      const int64_t gr = i < kMlaRowsPerSplit * 9 ? rows[i / 9] : -1;
-      const uint16_t *src = gr >= 0 ? (const uint16_t *)(a.kv_scale + gr * kScales + 2 * (i % 9))
-                                    : (const uint16_t *)g_zero16;
-      sreg[j] = *src;
-      if (gr < 0) sreg[j] = 0x7F7Fu;
-    }
-  }
-  // issue every tile's gather now; tiles are consumed in order below. The
-  // row ids of a tile are read from LDS in one batch before its DMAs.
-#pragma unroll
-  for (int tt = 0; tt < kMaxTiles; ++tt) {
-    // tiles past ntiles are filled from the zero block so that every thread
-    // issues the same, static number of DMAs (exact vmcnt bookkeeping)
-    if (!kMx) {
-      unsigned char *tbase = tiles + tt * kTileBytes;
-      int64_t gr[kBfDma];
-#pragma unroll
-      for (int j = 0; j < kBfDma; ++j)
-        gr[j] = tt < ntiles ? rows[tt * kTile + (j * 256 + tid) / kRowChunks] : -1;
-#pragma unroll
-      for (int j = 0; j < kBfDma; ++j) {
-        const int c = j * 256 + tid;                 // chunk slot in the tile
-        const int r = c / kRowChunks;
-        const int col = (c - r * kRowChunks) ^ row_swz(r);
-        const void *src = gr[j] >= 0
-                              ? (const void *)((const uint8_t *)a.kv + gr[j] * (kD * 2) + col * 16)
-                              : (const void *)g_zero16;
-        dma16(src, tbase + (j * 256 + wave * 64) * 16);
-      }
-    } else {
-      unsigned char *tbase = tiles + tt * kMxRawBytes;
-      int64_t gr[kMxDma];
-#pragma unroll
-      for (int j = 0; j < kMxDma; ++j) {
-        const int c = j * 256 + tid;                 // raw chunk slot: row c/36, 16 values
-        gr[j] = (c < kMxChunks && tt < ntiles) ? rows[tt * kTile + c / 36] : -1;
-      }
-#pragma unroll
-      for (int j = 0; j < kMxDma; ++j) {
-        const int c = j * 256 + tid;
-        const int r = c / 36;
-        const void *src = gr[j] >= 0
-                              ? (const void *)((const uint8_t *)a.kv + gr[j] * kD + (c - r * 36) * 16)
-                              : (const void *)g_zero16;
-        dma16(src, tbase + (j * 256 + wave * 64) * 16);
-      }
-    }
-  }
-  if (kMx) {
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      int i = tid + 256 * j;
-      if (i < kMlaRowsPerSplit * 9) *(uint16_t *)(scl + (i / 9) * kScales + 2 * (i % 9)) = (uint16_t)sreg[j];
-    }
-  }
-
-  v4f acc[kCt];
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-  const float scale2 = a.tau * kLog2e;  // logits kept in the exp2 domain
-
-#pragma unroll
-  for (int tt = 0; tt < kMaxTiles; ++tt) {
-    if (tt >= ntiles) break;
-    const unsigned char *tile;
-    if (!kMx) {
-      wait_tile<kBfDma>(tt);
-      barrier_lds();  // every wave's DMAs of tile tt have landed
-      tile = tiles + tt * kTileBytes;
-    } else {
-      wait_tile<kMxDma>(tt);
-      barrier_lds();  // raw tile tt and the scales are in LDS; the previous tile is consumed
-      const unsigned char *raw = tiles + tt * kMxRawBytes;
-      for (int c = tid; c < kMxChunks; c += 256) {
-        const int r = c / 36, blk = c - r * 36;      // 16 values = channels blk*16 ..
-        const v4i v = *(const v4i *)(raw + c * 16);
-        const float sc = e8m0_to_f32(scl[(tt * kTile + r) * kScales + (blk >> 1)]);
-        const uint32_t w4[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-        uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, false));
-          o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], sc, true));
-        }
-        *(v4i *)(cvt + swz(r, 2 * blk) * 16) = (v4i){(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-        *(v4i *)(cvt + swz(r, 2 * blk + 1) * 16) = (v4i){(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
-      }
-      barrier_lds();
-      tile = cvt;
-    }
-    // S^T[row][head] for the two 16-row halves of the tile
-    v4f s[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      v4f sacc = {0.f, 0.f, 0.f, 0.f};
-      const int row = rt * 16 + c16;
-#pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks)
-        sacc = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(row, 4 * ks + g) * 16)), qreg[ks], sacc);
-      s[rt] = sacc;
-    }
-    float lg[8];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int ri = tt * kTile + (j >> 2) * 16 + 4 * g + (j & 3);
-      bool ok = ri < nrows && rows[ri] >= 0;
-      lg[j] = ok ? s[j >> 2][j & 3] * scale2 : -INFINITY;
-      mt = fmaxf(mt, lg[j]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    if (!(mt > -INFINITY)) continue;  // no selected row in this tile (uniform over heads)
-    // move the running max only when a logit would exceed it by 2^8 (exact either way)
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) acc[ct] *= alpha;
-      m_run = m_new;
-    }
-    float p[8], ps = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = exp2f(lg[j] - m_run);
-      ps += p[j];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run += ps;
-    v8bf pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-    // V^T operand by transposed LDS reads: lane (g, c16) receives channel ct*16 + c16
-    // of rows 4g..4g+3 (first read) and 16+4g..16+4g+3 (second read)
-    const int vr = 4 * g + (c16 >> 2);
-    const int vsub = (c16 & 1) * 8;
-#pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) {
-      const int chunk = 2 * ct + ((c16 & 3) >> 1);
-      const v4bf lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) v4bf *)(tile + swz(vr, chunk) * 16 + vsub));
-      const v4bf hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) v4bf *)(tile + swz(vr + 16, chunk) * 16 + vsub));
-      const v8bf va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      acc[ct] = mfma_bf16(va, pb, acc[ct]);
-    }
-  }
-  // partial O^T in bf16 (the softmax weights are still unnormalised, so only
-  // relative precision matters), stored in register order: [t][split][wave]
-  // [ct][lane] x 4 channels, so that each store of a wave is 512 contiguous
-  // bytes. Lane (g, c16) holds channels ct*16 + 4g + i of head wave*16 + c16.
-  uint2 *pdst = (uint2 *)opart + ((((size_t)t * S + split) * 4 + wave) * kCt) * 64 + lane;
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-    const uint32_t lo = f32_to_bf16_bits(acc[ct][0]) | (f32_to_bf16_bits(acc[ct][1]) << 16);
-    const uint32_t hi = f32_to_bf16_bits(acc[ct][2]) | (f32_to_bf16_bits(acc[ct][3]) << 16);
-    pdst[ct * 64] = make_uint2(lo, hi);
-  }
-  if (g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m_run, l_run);
-}
-
 // --------------------------------------------------------------------------
-// bf16 split kernel with two waves per SIMD.
+// Split kernel (bf16 or MXFP8 latent cache), two waves per SIMD.
 //
 // 8 waves: wave w serves heads 16 (w % 4) .. 16 (w % 4) + 15 for the tiles of
 // its set (w / 4): set 0 takes tiles 0 and 2, set 1 tiles 1 and 3, each with
@@ -814,7 +600,7 @@ static void mla_plan(int T, int k, int *R, int *S) {
   }
   int r = 1;
   while (r < kMaxRounds && (int64_t)T * ((k + r * kMlaRowsPerSplit - 1) / (r * kMlaRowsPerSplit)) > cus) r *= 2;
-  *R = kMlaEightWaves ? r : 1;
+  *R = r;
   *S = (k + *R * kMlaRowsPerSplit - 1) / (*R * kMlaRowsPerSplit);
 }
 
@@ -831,10 +617,6 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   float2 *ml = (float2 *)((char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void *)k_mla_split<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxSmem);
     (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 1>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
     (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 2>,
@@ -852,24 +634,21 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   }
   const dim3 grid(S, a.T);
   const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
-  if (kMlaEightWaves && mx) {
+  if (mx) {
     if (R == 4)
       hipLaunchKernelGGL((k_mla_split8<true, 4>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
     else if (R == 2)
       hipLaunchKernelGGL((k_mla_split8<true, 2>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
     else
       hipLaunchKernelGGL((k_mla_split8<true, 1>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
-  } else if (kMlaEightWaves) {
+  } else {
     if (R == 4)
       hipLaunchKernelGGL((k_mla_split8<false, 4>), grid, dim3(512), kBfSmem, s, a, opart, ml);
     else if (R == 2)
       hipLaunchKernelGGL((k_mla_split8<false, 2>), grid, dim3(512), kBfSmem, s, a, opart, ml);
     else
       hipLaunchKernelGGL((k_mla_split8<false, 1>), grid, dim3(512), kBfSmem, s, a, opart, ml);
-  } else if (mx)
-    hipLaunchKernelGGL(k_mla_split<true>, dim3(S, a.T), dim3(256), kMxSmem, s, a, opart, ml);
-  else
-    hipLaunchKernelGGL(k_mla_split<false>, dim3(S, a.T), dim3(256), kBfSmem, s, a, opart, ml);
+  }
   return hipGetLastError();
 }
 
