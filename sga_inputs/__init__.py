@@ -14,6 +14,7 @@ milliseconds while the tests rebuild the very same bytes on the host.
 
 from .gen import (  # noqa: F401
     CONFIG_NAMES,
+    EXTRA_NAMES,
     SgaCase,
     config_dims,
     make_case,

@@ -344,6 +344,12 @@ CONFIG_NAMES = (
     "prefill_q4096_n128k",   # 1 seq, 4,096 queries at positions 126,976..131,071
     "varlen_mxfp8_b64",      # 64 seqs, log-uniform lengths in [4,096, 262,144], MXFP8 latent
 )
+# Further workloads: several queries per sequence in decode (the verification
+# step of speculative decoding: the last 4 cached positions of each sequence
+# are queries, so the 4 share one scan of the sequence's index keys).
+EXTRA_NAMES = (
+    "decode_b16_n128k_mq4",  # 16 seqs x 131,072 cached, 4 queries each at n-4 .. n-1, k=2048
+)
 
 
 def varlen_lengths(seed: int, n: int = 64, lo: int = 4096, hi: int = 262144) -> List[int]:
@@ -357,7 +363,7 @@ def config_dims(name: str) -> Dict[str, int]:
 
 
 def make_case(name: str, *, seed: int = 0, device="cpu", out_dtype: Optional[str] = None) -> SgaCase:
-    """One of the five named workloads, drawn with `seed`."""
+    """One of the named workloads (CONFIG_NAMES, EXTRA_NAMES), drawn with `seed`."""
     if name == "tiny_fp32_L512":
         L = 512
         return make_custom([L], [(0, p) for p in range(L)], dims=TINY_DIMS, precision="f32",
@@ -370,6 +376,11 @@ def make_case(name: str, *, seed: int = 0, device="cpu", out_dtype: Optional[str
     if name == "decode_b16_n128k":
         B, n = 16, 131072
         return make_custom([n] * B, [(b, n - 1) for b in range(B)], dims=FULL_DIMS,
+                           precision="bf16", seed=seed, device=device, name=name,
+                           out_dtype=out_dtype, softmax_scale=1.0 / 24.0)
+    if name == "decode_b16_n128k_mq4":
+        B, n, Q = 16, 131072, 4
+        return make_custom([n] * B, [(b, n - Q + j) for b in range(B) for j in range(Q)], dims=FULL_DIMS,
                            precision="bf16", seed=seed, device=device, name=name,
                            out_dtype=out_dtype, softmax_scale=1.0 / 24.0)
     if name == "prefill_q4096_n128k":

@@ -28,31 +28,36 @@ namespace {
 // workgroup, one row per wave, without sharing.
 // --------------------------------------------------------------------------
 // A group is "shared" when all of its rows name the same sequence.
+template <int kGroup>
 __device__ __forceinline__ bool group_is_shared(const SeqMeta &m, int T, int g) {
-  const int t0 = g * kPfGroup;
-  const int t1 = min(T, t0 + kPfGroup);
+  const int t0 = g * kGroup;
+  const int t1 = min(T, t0 + kGroup);
   const int32_t b = m.q_seq[t0];
   bool same = true;
   for (int t = t0 + 1; t < t1; ++t) same = same && (m.q_seq[t] == b);
   return same;
 }
 
-constexpr int kPfChunk = 8192;  // keys per workgroup
+// Two shapes of the kernel (query rows per workgroup, keys per workgroup,
+// tile buffers): prefill, 8 rows x 8,192 keys with 3 buffers, bound by the
+// MFMAs; multi-query decode (a few queries per sequence, e.g. the draft
+// tokens of speculative decoding), 4 rows x 4,096 keys with 4 buffers, so that
+// two workgroups per CU keep 6 tiles in flight as the single-query kernel does.
 constexpr int kPfQpw = 1;       // queries per wave
-constexpr int kPfBufs = 3;
 
 // kQpw queries per wave, kPfGroup / kQpw waves per workgroup. The
 // weighted-ReLU epilogue brings about as much VALU work as there is MFMA work
 // and the two overlap only in part on a SIMD, so latency is hidden by wave
 // count: the register budget is held to 6 waves per SIMD (3 workgroups per CU).
-template <int kQpw>
-__global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta m, int T,
+template <int kQpw, int kGroup, int kChunk, int kBufs>
+__global__ __launch_bounds__(kGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta m, int T,
                                                                 const uint8_t *__restrict__ q_idx,
                                                                 const float *__restrict__ w,
                                                                 const uint8_t *__restrict__ k_idx,
                                                                 float *__restrict__ scores,
                                                                 int64_t stride) {
-  constexpr int kThreads = kPfGroup / kQpw * 64;
+  constexpr int kThreads = kGroup / kQpw * 64;
+  static_assert(kBufs == 3 || kBufs == 4, "tile buffers");
   static_assert(512 % kThreads == 0 || kThreads % 512 == 0, "a tile is 512 16-byte pieces");
   constexpr int kDmaPer = kThreads >= 512 ? 1 : 512 / kThreads;  // DMA issues per thread per tile
   // dynamic LDS: the compiler then leaves the DMA/LDS-read ordering to the
@@ -60,22 +65,22 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
   extern __shared__ __attribute__((aligned(16))) unsigned char tiles[];
   __shared__ int s_nmax;
   const int g = blockIdx.y;
-  const bool shared = group_is_shared(m, T, g);  // uniform over the workgroup
-  const int t0 = g * kPfGroup;
+  const bool shared = group_is_shared<kGroup>(m, T, g);  // uniform over the workgroup
+  const int t0 = g * kGroup;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kg = lane >> 4, c16 = lane & 15;
   int64_t start = 0;
   if (tid == 0) {
     int mx = 0;
-    for (int t = t0; t < min(T, t0 + kPfGroup); ++t) mx = max(mx, query_candidates(m, t, &start));
+    for (int t = t0; t < min(T, t0 + kGroup); ++t) mx = max(mx, query_candidates(m, t, &start));
     s_nmax = mx;
   }
   __syncthreads();
   const int nmax = s_nmax;
-  const int c0 = blockIdx.x * kPfChunk;
+  const int c0 = blockIdx.x * kChunk;
   if (c0 >= nmax) return;
-  const int ntiles = (min(nmax, c0 + kPfChunk) - c0 + kIdxTileKeys - 1) / kIdxTileKeys;
+  const int ntiles = (min(nmax, c0 + kChunk) - c0 + kIdxTileKeys - 1) / kIdxTileKeys;
 
   // the wave's queries (rows past T get n = 0)
   int nq[kQpw];
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
       const int t = t0 + kQpw * wave + j;
       int64_t st = 0;
       const int n = t < T ? query_candidates(m, t, &st) : 0;
-      const int cend = min(n, c0 + kPfChunk);
+      const int cend = min(n, c0 + kChunk);
       for (int kbase = c0; kbase < cend; kbase += kIdxTileKeys) {
         float part[1][4];
         const v8i(&aj)[1][4] = *reinterpret_cast<const v8i(*)[1][4]>(&a[j]);
@@ -140,26 +145,32 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
       key = key < nmax ? key : nmax - 1;
       const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
       __builtin_amdgcn_global_load_lds(
-          src, (lds_void *)(tiles + (i % kPfBufs) * kIdxTileBytes + (u * kThreads + wave * 64) * 16),
+          src, (lds_void *)(tiles + (i % kBufs) * kIdxTileBytes + (u * kThreads + wave * 64) * 16),
           16, 0, 0);
     }
   };
   wait_vmcnt<0>();
-  issue(0);
-  if (ntiles > 1) issue(1);
+  for (int i = 0; i < kBufs - 1; ++i)
+    if (i < ntiles) issue(i);
   for (int i = 0; i < ntiles; ++i) {
-    // Tile i has landed once at most the kDmaPer copies of tile i + 1 (issued
-    // after it) are outstanding; score stores issued later only make this
-    // wait longer. The barrier then publishes every wave's part of tile i and
+    // Tile i has landed once at most the kDmaPer copies of each tile issued
+    // after it are outstanding; score stores issued later only make this wait
+    // longer. The barrier then publishes every wave's part of tile i and
     // certifies that all LDS reads of tile i - 1 are done, so the copy of
-    // tile i + 2 may overwrite that buffer.
-    if (i + 1 < ntiles) wait_vmcnt<kDmaPer>(); else wait_vmcnt<0>();
+    // tile i + kBufs - 1 may overwrite that buffer.
+    const int after = min(ntiles - 1, i + kBufs - 2) - i;  // tiles issued after tile i
+    if (after >= 2)
+      wait_vmcnt<2 * kDmaPer>();
+    else if (after == 1)
+      wait_vmcnt<kDmaPer>();
+    else
+      wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (i + 2 < ntiles) issue(i + 2);
-    const unsigned char *tb = tiles + (i % kPfBufs) * kIdxTileBytes;
+    if (i + kBufs - 1 < ntiles) issue(i + kBufs - 1);
+    const unsigned char *tb = tiles + (i % kBufs) * kIdxTileBytes;
     const int kbase = c0 + i * kIdxTileKeys;
     float part[kQpw][4];
     score_tiles<kQpw>(a, [&](int kt) { return load_key_operand(tb, kt, kg, c16); }, wv, part);
@@ -177,9 +188,16 @@ __global__ __launch_bounds__(kPfGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMet
 hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
                                     const uint8_t *k_idx, float *scores, int64_t stride,
                                     hipStream_t s) {
-  dim3 grid((m.max_kv_len + kPfChunk - 1) / kPfChunk, (T + kPfGroup - 1) / kPfGroup);
-  hipLaunchKernelGGL(k_index_fp8_pf<kPfQpw>, grid, dim3(kPfGroup / kPfQpw * 64),
-                     kPfBufs * kIdxTileBytes, s, m, T, q_idx, w, k_idx, scores, stride);
+  if (T < 8 * m.num_seqs) {
+    // a few queries per sequence (multi-query decode): groups of 4 rows
+    dim3 grid((m.max_kv_len + 4095) / 4096, (T + 3) / 4);
+    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, 4, 4096, 4>), grid, dim3(4 / kPfQpw * 64), 4 * kIdxTileBytes, s,
+                       m, T, q_idx, w, k_idx, scores, stride);
+  } else {
+    dim3 grid((m.max_kv_len + 8191) / 8192, (T + kPfGroup - 1) / kPfGroup);
+    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, kPfGroup, 8192, 3>), grid, dim3(kPfGroup / kPfQpw * 64),
+                       3 * kIdxTileBytes, s, m, T, q_idx, w, k_idx, scores, stride);
+  }
   return hipGetLastError();
 }
 

@@ -145,6 +145,21 @@ def test_index_scores_prefill_single_sequence_chunk():
     _check_scores(case, [0, 1, 17, 100, 150, 199])
 
 
+def test_index_scores_multi_query_groups_of_four():
+    # a few queries per sequence (speculative verification): 4-row groups
+    # share each key tile. Sequence 5 holds 5 queries, so every later group
+    # straddles a sequence boundary and takes the per-query path; ragged
+    # lengths give ragged last chunks and a 64-key sequence.
+    lens = [9000, 20000, 3000, 4097, 12000, 5000, 64, 8191, 16385, 2048, 7000, 30000]
+    qs = []
+    for b, n in enumerate(lens):
+        q = 5 if b == 5 else 4
+        qs += [(b, n - q + j) for j in range(q)]
+    case = make_custom(lens, qs, dims=FULL_DIMS, precision="bf16", seed=43, device="cuda")
+    say(f"case multi-query index scores, {len(qs)} queries over {len(lens)} sequences")
+    _check_scores(case)
+
+
 def test_topk_threshold_deep_in_wide_histograms():
     # scores spread over hundreds of level-0 bins per 4096-position chunk and
     # k near n / 2: the threshold lies far below the 15 highest bins of every

@@ -87,6 +87,13 @@ def test_layer_decode_b16_n128k_sampled_and_deterministic():
     compare_layer(case, [0, 5, 10, 15], out=out1, idx=idx1, lse=lse1, label="decode_b16_n128k")
 
 
+def test_layer_decode_b16_n128k_mq4_sampled():
+    # 4 queries per sequence at its last 4 positions share one index scan
+    case = make_case("decode_b16_n128k_mq4", device="cuda")
+    say("case layer decode_b16_n128k_mq4")
+    compare_layer(case, [0, 1, 2, 3, 22, 63], label="decode_b16_n128k_mq4")
+
+
 def test_layer_varlen_mxfp8_b64_sampled():
     case = make_case("varlen_mxfp8_b64", device="cuda")
     lens = np.array(case.lens)
