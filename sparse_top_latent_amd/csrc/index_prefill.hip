@@ -41,8 +41,8 @@ __device__ __forceinline__ bool group_is_shared(const SeqMeta &m, int T, int g) 
 // Two shapes of the kernel (query rows per workgroup, keys per workgroup,
 // tile buffers): prefill, 8 rows x 8,192 keys with 3 buffers, bound by the
 // MFMAs; multi-query decode (a few queries per sequence, e.g. the draft
-// tokens of speculative decoding), 4 rows x 4,096 keys with 4 buffers, so that
-// two workgroups per CU keep 6 tiles in flight as the single-query kernel does.
+// tokens of speculative decoding), 4 rows x 2,048 keys with 4 buffers: four
+// workgroups per CU for 16 x 128K (4,096 keys per workgroup: 10 % slower).
 constexpr int kPfQpw = 1;       // queries per wave
 
 // kQpw queries per wave, kPfGroup / kQpw waves per workgroup. The
@@ -190,8 +190,8 @@ hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_id
                                     hipStream_t s) {
   if (T < 8 * m.num_seqs) {
     // a few queries per sequence (multi-query decode): groups of 4 rows
-    dim3 grid((m.max_kv_len + 4095) / 4096, (T + 3) / 4);
-    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, 4, 4096, 4>), grid, dim3(4 / kPfQpw * 64), 4 * kIdxTileBytes, s,
+    dim3 grid((m.max_kv_len + 2047) / 2048, (T + 3) / 4);
+    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, 4, 2048, 4>), grid, dim3(4 / kPfQpw * 64), 4 * kIdxTileBytes, s,
                        m, T, q_idx, w, k_idx, scores, stride);
   } else {
     dim3 grid((m.max_kv_len + 8191) / 8192, (T + kPfGroup - 1) / kPfGroup);

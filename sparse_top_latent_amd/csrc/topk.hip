@@ -54,13 +54,19 @@ __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__re
   if (blockIdx.x == 0 && threadIdx.x == 0) ws.ncand[t] = n;
   const int c0 = blockIdx.x * kTopkChunk;
   if (c0 >= n) return;
+  // all of this thread's scores are requested before the histogram is
+  // cleared (clamped into the row; positions past n are not counted), so the
+  // loads overlap each other and the clearing instead of waiting one by one
+  constexpr int kPer = kTopkChunk / 256;
+  const float *row = scores + t * stride;
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = row[min(c0 + j * 256 + (int)threadIdx.x, n - 1)];
   for (int i = threadIdx.x; i < kHist0Bins; i += 256) hist[i] = 0u;
   __syncthreads();
-  const float *row = scores + t * stride;
-  for (int j = 0; j < kTopkChunk / 256; ++j) {
-    int s = c0 + j * 256 + threadIdx.x;
-    if (s < n) atomicAdd(&hist[score_key(row[s]) >> kHist0Shift], 1u);
-  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (c0 + j * 256 + (int)threadIdx.x < n) atomicAdd(&hist[score_key(v[j]) >> kHist0Shift], 1u);
   __syncthreads();
   write_hist0_list<false, 256>(hist, ws, t, blockIdx.x, scratch);
 }
