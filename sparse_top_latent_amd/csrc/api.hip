@@ -201,6 +201,9 @@ MlaArgs mla_args(const sga_problem *p, const void *q, const void *kv, const uint
   a.kv_dtype = p->kv_dtype;
   a.kv_scale = kv_scale;
   a.topk_idx = topk_idx;
+  a.fuse = false;
+  a.sel = TopkWs{};
+  a.topk_out = nullptr;
   a.gate = gate;
   a.gate_dtype = p->gate_dtype;
   a.out = out;
@@ -360,9 +363,19 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
     if (prof) prof_mark(s, 0);
     SGA_TRY(run_index(p, plan, q_idx, w, k_idx, scores, stride, &tw, s));
     if (prof) prof_mark(s, 1);
-    SGA_TRY(launched(launch_topk_select(m, T, p->topk, scores, stride, tw, idx, s), "topk select"));
+    // The MI355X MLA path can do the top-k's last step itself (MlaArgs::fuse)
+    // when its grid fits the CUs at once: only the select kernel runs here,
+    // and the split kernel derives its rows from the select's candidates and
+    // writes topk_idx_out.
+    const bool fuse = plan.mla != MlaPath::kF32 && p->max_kv_len > p->topk && mla_fuse_finish(T, p->topk);
+    SGA_TRY(launched(launch_topk_select(m, T, p->topk, scores, stride, tw, idx, s, !fuse), "topk select"));
     if (prof) prof_mark(s, 2);
     MlaArgs a = mla_args(p, q, kv, kv_scale, idx, gate, out, lse);
+    if (fuse) {
+      a.fuse = true;
+      a.sel = tw;
+      a.topk_out = topk_idx_out;
+    }
     SGA_TRY(run_mla(a, plan, mws, s, prof));
     if (prof) {
       prof_mark(s, 4);

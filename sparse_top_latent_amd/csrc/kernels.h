@@ -47,8 +47,10 @@ hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64
                              TopkWs *w, hipStream_t s);
 // Select (one workgroup per (slot, query)) and finish (one per query); needs
 // the lists and ncand from a producer launched earlier on the same stream.
+// With finish false only the select kernel runs; the last step is then left
+// to the consumer (the fused MLA split kernel, see MlaArgs::sel).
 hipError_t launch_topk_select(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
-                              const TopkWs &w, int32_t *topk_idx, hipStream_t s);
+                              const TopkWs &w, int32_t *topk_idx, hipStream_t s, bool finish = true);
 
 // --- sparse MLA + gate ---------------------------------------------------------
 struct MlaArgs {
@@ -66,6 +68,12 @@ struct MlaArgs {
   void *out;
   int out_dtype;
   float *lse;
+  // fused top-k finish (split kernel only): with fuse set, the split kernel
+  // takes its rows from the select kernel's candidates in `sel` instead of
+  // topk_idx, and writes the selected positions to topk_out when it is set
+  bool fuse;
+  TopkWs sel;
+  int32_t *topk_out;
 };
 // generic fp32 path (one workgroup per (query, head))
 hipError_t launch_mla_f32(const MlaArgs &a, hipStream_t s);
@@ -73,6 +81,8 @@ hipError_t launch_mla_f32(const MlaArgs &a, hipStream_t s);
 constexpr int kMlaRowsPerSplit = 128;
 size_t mla_split_ws_bytes(int T, int k);
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s);
+// whether the split kernel should do the top-k's last step itself (fuse)
+bool mla_fuse_finish(int T, int k);
 hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s);
 
 }  // namespace sga

@@ -178,4 +178,148 @@ __device__ __forceinline__ void write_hist0_list(const uint32_t *hist, const Top
   if (tid == 0) list[0] = total;
 }
 
+// The last step of the top-k select for query t, done by one workgroup of
+// kBlock threads: from the candidates k_topk_select wrote (position order) and
+// its totals (b0, keys above bin b0, candidates), the level-1 and level-2
+// histograms give the exact k-th key K* and the number of ties at K* to take;
+// then, round by round in position order, one packed scan gives every
+// selected candidate its output index. `out(o, pos)` is called once for each
+// o in [0, k) (in no particular order across threads). LDS: `hist` holds
+// 2 * 1024 words, `scratch` kBlock / 64, `res` 2. Every thread of the
+// workgroup must call it (it has barriers). Only for queries with n_t > k.
+template <int kBlock, class Out>
+__device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, uint32_t *hist,
+                                             uint32_t *scratch, int *res, Out out) {
+  constexpr int kPer = 4096 / kBlock;  // candidates per thread and round
+  constexpr int kRound = kBlock * kPer;
+  static_assert(kPer % 2 == 0, "candidate pairs");
+  const int tid = threadIdx.x;
+  const uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
+  const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;
+  // Round r holds candidates [r * kRound, r * kRound + kRound), thread tid the
+  // kPer consecutive ones from r * kRound + kPer tid; round 0 stays in
+  // registers and is requested before the query's totals arrive (reads past
+  // the end are clamped into the array and not used)
+  auto load_round = [&](int r, uint2 (&pr)[kPer]) {
+    const uint32_t f0 = (uint32_t)r * kRound + tid * kPer;
+#pragma unroll
+    for (int i = 0; i < kPer; i += 2) {
+      const uint32_t f = min(f0 + i, cap - 2);
+      const uint4 x = *(const uint4 *)(cand + f);
+      pr[i] = make_uint2(x.x, x.y);
+      pr[i + 1] = make_uint2(x.z, x.w);
+    }
+  };
+  uint2 p0r[kPer];
+  load_round(0, p0r);
+  const uint4 th = ws.thr[t];
+  const uint32_t ub0 = th.x, above0 = th.y;
+  const uint32_t total = min(th.z, cap);
+  for (int i = tid; i < 2 * kHist12Bins; i += kBlock) hist[i] = 0u;
+  __syncthreads();
+  const int rounds = (int)((total + kRound - 1) / kRound);
+  auto valid = [&](int r, int i) { return (uint32_t)r * kRound + tid * kPer + i < total; };
+  uint32_t *hist1 = hist, *hist2 = hist + kHist12Bins;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Keep the candidates in the registers they were loaded into: without this
+  // the compiler may load them again for each pass.
+  auto pin = [&](uint2 (&pr)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) asm volatile("" : "+v"(pr[i].x), "+v"(pr[i].y));
+  };
+  // threshold bin of a level histogram, found by wave 0 and shared
+  auto find_bin = [&](const uint32_t *h, uint32_t want, uint32_t *above) {
+    if (wave == 0) {
+      uint32_t a;
+      const int b = wave_find_threshold_bin<kHist12Bins>(h, want, &a);
+      if (lane == 0) {
+        res[0] = b;
+        res[1] = (int)a;
+      }
+    }
+    __syncthreads();
+    *above = (uint32_t)res[1];
+    return res[0];
+  };
+  pin(p0r);
+  // level 1: key bits 19..10 of the keys in bin b0
+  auto level1 = [&](int r, const uint2 (&pr)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (valid(r, i) && (pr[i].y >> kHist0Shift) == ub0) atomicAdd(&hist1[(pr[i].y >> 10) & 1023u], 1u);
+  };
+  level1(0, p0r);
+  for (int r = 1; r < rounds; ++r) {
+    uint2 pr[kPer];
+    load_round(r, pr);
+    pin(pr);
+    level1(r, pr);
+  }
+  __syncthreads();
+  uint32_t want = (uint32_t)k - above0;
+  uint32_t above1;
+  const int b1 = find_bin(hist1, want, &above1);
+  want -= above1;
+  const uint32_t prefix22 = (ub0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
+  // level 2: the last 10 bits among the keys that share the top 22 bits
+  auto level2 = [&](int r, const uint2 (&pr)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (valid(r, i) && (pr[i].y >> 10) == prefix22) atomicAdd(&hist2[pr[i].y & 1023u], 1u);
+  };
+  level2(0, p0r);
+  for (int r = 1; r < rounds; ++r) {
+    uint2 pr[kPer];
+    load_round(r, pr);
+    pin(pr);
+    level2(r, pr);
+  }
+  __syncthreads();
+  uint32_t above2;
+  const int b2 = find_bin(hist2, want, &above2);
+  want -= above2;
+  const uint32_t kstar = (prefix22 << 10) | (uint32_t)b2;  // the exact k-th largest key
+  const uint32_t take = want;                                 // ties at kstar to keep
+
+  // ordered emission, round by round: one scan gives, per thread, the keys
+  // above K* and the ties at K* in front of its run (16 bits each: a round
+  // holds at most 4096 candidates)
+  uint32_t gt_run = 0, tie_run = 0;
+  auto emit = [&](int r, const uint2 (&pr)[kPer]) {
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const bool ok = valid(r, i);
+      n_gt += ok && pr[i].y > kstar;
+      n_eq += ok && pr[i].y == kstar;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan((n_eq << 16) | n_gt, scratch, &tot);
+    uint32_t tr = tie_run + (pre >> 16);                      // ties in front of this run
+    uint32_t o2 = gt_run + (pre & 0xFFFFu) + min(tr, take);   // outputs in front of it
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (!valid(r, i)) continue;
+      bool sel = pr[i].y > kstar;
+      if (pr[i].y == kstar) {
+        sel = tr < take;
+        ++tr;
+      }
+      if (sel) {
+        if (o2 < (uint32_t)k) out(o2, (int32_t)pr[i].x);
+        ++o2;
+      }
+    }
+    gt_run += tot & 0xFFFFu;
+    tie_run += tot >> 16;
+  };
+  emit(0, p0r);
+  for (int r = 1; r < rounds; ++r) {
+    uint2 pr[kPer];
+    load_round(r, pr);
+    pin(pr);
+    emit(r, pr);
+  }
+}
+
 }  // namespace sga

@@ -29,6 +29,7 @@
 //    stored and read in the split kernel's register order (coalesced).
 
 #include "kernels.h"
+#include "select_common.h"
 
 namespace sga {
 
@@ -217,7 +218,7 @@ __device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int 
   }
 }
 
-template <bool kMx, int R>
+template <bool kMx, int R, bool kFuse>
 __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
                                                     float2 *__restrict__ ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -233,13 +234,40 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   const int r0 = split * R * kMlaRowsPerSplit;
   const int nrows = min(R * kMlaRowsPerSplit, a.k - r0);  // >= 1
   const int rounds = (nrows + kMlaRowsPerSplit - 1) / kMlaRowsPerSplit;
-  // the selected positions are requested first (clamped, unconditional) so
-  // that their latency overlaps the sequence lookup; thread i takes row i
-  const int my_row = min(tid, R * kMlaRowsPerSplit - 1);
-  int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(my_row, nrows - 1)];
   int64_t start;
-  const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
-  if (tid < R * kMlaRowsPerSplit) rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? (int32_t)(start + pos) : -1;
+  if (!kFuse) {
+    // the selected positions are requested first (clamped, unconditional) so
+    // that their latency overlaps the sequence lookup; thread i takes row i
+    const int my_row = min(tid, R * kMlaRowsPerSplit - 1);
+    int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(my_row, nrows - 1)];
+    const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
+    if (tid < R * kMlaRowsPerSplit) rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? (int32_t)(start + pos) : -1;
+  } else {
+    // The top-k's last step, done here for the workgroup's own output slots
+    // [r0, r0 + nrows) of the query (every split workgroup of the query
+    // repeats it; that costs no time, since it replaces a kernel boundary and
+    // the wait for the selected positions). n_t <= k: every candidate, in
+    // position order, then -1.
+    const int n = a.sel.ncand[t];
+    const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
+    if (tid < R * kMlaRowsPerSplit) {
+      const int32_t pos = (n <= a.k && tid < nrows && r0 + tid < n) ? r0 + tid : -1;
+      rows[tid] = (pos >= 0 && pos < L) ? (int32_t)(start + pos) : -1;
+      if (n <= a.k && a.topk_out && tid < nrows) a.topk_out[(size_t)t * a.k + r0 + tid] = pos;
+    }
+    if (n > a.k) {  // uniform over the workgroup
+      // (LDS for the histograms and scan at the start of the tile area; the
+      // copies into it start after the barrier below)
+      uint32_t *fh = (uint32_t *)smem;
+      finish_query<512>(a.k, a.sel, t, fh, fh + 2 * kHist12Bins, (int *)(fh + 2 * kHist12Bins + 8),
+                        [&](uint32_t o, int32_t p) {
+                          if (o >= (uint32_t)r0 && o < (uint32_t)(r0 + nrows)) {
+                            rows[o - r0] = (p >= 0 && p < L) ? (int32_t)(start + p) : -1;
+                            if (a.topk_out) a.topk_out[(size_t)t * a.k + o] = p;
+                          }
+                        });
+    }
+  }
   __syncthreads();  // rows[] ready
   const int head = hg * 16 + c16;
   const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
@@ -609,46 +637,57 @@ size_t mla_split_ws_bytes(int T, int k) {
   return align256((size_t)T * S * kH * kDc * 2) + align256((size_t)T * S * kH * sizeof(float2));
 }
 
+bool mla_fuse_finish(int T, int k) {
+  // With more split workgroups than CUs, the repeated top-k finish in every
+  // split workgroup of a query costs more than the finish kernel it replaces
+  // (prefill: 4,096 queries x 4 splits, 0.35 ms more).
+  int R, S;
+  mla_plan(T, k, &R, &S);
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  (void)hipGetLastError();
+  return (int64_t)T * S <= cus;
+}
+
+template <bool kMx, int R, bool kFuse>
+static void launch_split8(const MlaArgs &a, uint16_t *opart, float2 *ml, int S, hipStream_t s) {
+  static bool attr = false;
+  const size_t smem = kMx ? kMx8Smem : kBfSmem;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<kMx, R, kFuse>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse>), dim3(S, a.T), dim3(512), smem, s, a, opart, ml);
+}
+
+template <bool kMx, bool kFuse>
+static void launch_split8_r(const MlaArgs &a, uint16_t *opart, float2 *ml, int R, int S, hipStream_t s) {
+  if (R == 4)
+    launch_split8<kMx, 4, kFuse>(a, opart, ml, S, s);
+  else if (R == 2)
+    launch_split8<kMx, 2, kFuse>(a, opart, ml, S, s);
+  else
+    launch_split8<kMx, 1, kFuse>(a, opart, ml, S, s);
+}
+
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   int R, S;
   mla_plan(a.T, a.k, &R, &S);
   uint16_t *opart = (uint16_t *)ws;
   float2 *ml = (float2 *)((char *)ws + align256((size_t)a.T * S * kH * kDc * 2));
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 1>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 2>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<false, 4>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBfSmem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<true, 1>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<true, 2>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<true, 4>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMx8Smem);
-    (void)hipGetLastError();
-    attr = true;
-  }
-  const dim3 grid(S, a.T);
   const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
-  if (mx) {
-    if (R == 4)
-      hipLaunchKernelGGL((k_mla_split8<true, 4>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
-    else if (R == 2)
-      hipLaunchKernelGGL((k_mla_split8<true, 2>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
-    else
-      hipLaunchKernelGGL((k_mla_split8<true, 1>), grid, dim3(512), kMx8Smem, s, a, opart, ml);
-  } else {
-    if (R == 4)
-      hipLaunchKernelGGL((k_mla_split8<false, 4>), grid, dim3(512), kBfSmem, s, a, opart, ml);
-    else if (R == 2)
-      hipLaunchKernelGGL((k_mla_split8<false, 2>), grid, dim3(512), kBfSmem, s, a, opart, ml);
-    else
-      hipLaunchKernelGGL((k_mla_split8<false, 1>), grid, dim3(512), kBfSmem, s, a, opart, ml);
-  }
+  if (mx && a.fuse)
+    launch_split8_r<true, true>(a, opart, ml, R, S, s);
+  else if (mx)
+    launch_split8_r<true, false>(a, opart, ml, R, S, s);
+  else if (a.fuse)
+    launch_split8_r<false, true>(a, opart, ml, R, S, s);
+  else
+    launch_split8_r<false, false>(a, opart, ml, R, S, s);
   return hipGetLastError();
 }
 

@@ -41,8 +41,6 @@ constexpr int kSelWaves = kSelBlock / 64;
 constexpr int kSelPer = 4096 / kSelBlock;          // consecutive scores per thread and batch
 constexpr int kSelBatch = kSelBlock * kSelPer;     // 4096 positions
 constexpr int kFinBlock = 1024;                    // threads of the finishing workgroup
-constexpr int kFinPer = 4096 / kFinBlock;          // candidates per thread and round of the last pass
-constexpr int kFinRound = kFinBlock * kFinPer;     // 4096 candidates
 
 __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__restrict__ scores,
                                                     int64_t stride, TopkWs ws) {
@@ -288,135 +286,9 @@ __global__ __launch_bounds__(kFinBlock) void k_topk_finish(int k, TopkWs ws, int
   __shared__ __attribute__((aligned(16))) uint32_t hist[2 * kHist12Bins];  // levels 1 and 2
   __shared__ uint32_t scratch[kFinBlock / 64];
   __shared__ int res[2];
-  const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  const uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
-  const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;
-  // Round r holds candidates [r * 4096, r * 4096 + 4096), thread tid the
-  // kFinPer consecutive ones from r * 4096 + kFinPer tid; round 0 stays in registers and is
-  // requested before the query's totals arrive (reads past the end are
-  // clamped into the array and not used)
-  auto load_round = [&](int r, uint32_t lim, uint2 (&pr)[kFinPer]) {
-    const uint32_t f0 = (uint32_t)r * kFinRound + tid * kFinPer;
-#pragma unroll
-    for (int i = 0; i < kFinPer; i += 2) {
-      const uint32_t f = min(f0 + i, lim - 2);
-      const uint4 x = *(const uint4 *)(cand + f);
-      pr[i] = make_uint2(x.x, x.y);
-      pr[i + 1] = make_uint2(x.z, x.w);
-    }
-  };
-  uint2 p0r[kFinPer];
-  load_round(0, cap, p0r);
-  const uint4 th = ws.thr[t];  // no candidates for a query that keeps all of its n_t <= k
-  const uint32_t ub0 = th.x, above0 = th.y;
-  const uint32_t total = min(th.z, cap);
-  for (int i = tid; i < 2 * kHist12Bins; i += kFinBlock) hist[i] = 0u;
-  __syncthreads();
-  const int rounds = (int)((total + kFinRound - 1) / kFinRound);
-  auto valid = [&](int r, int i) { return (uint32_t)r * kFinRound + tid * kFinPer + i < total; };
-  uint32_t *hist1 = hist, *hist2 = hist + kHist12Bins;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  // Keep the candidates in the registers they were loaded into: without this
-  // the compiler may load them again for each pass.
-  auto pin = [&](uint2 (&pr)[kFinPer]) {
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i) asm volatile("" : "+v"(pr[i].x), "+v"(pr[i].y));
-  };
-  // threshold bin of a level histogram, found by wave 0 and shared
-  auto find_bin = [&](const uint32_t *h, uint32_t want, uint32_t *above) {
-    if (wave == 0) {
-      uint32_t a;
-      const int b = wave_find_threshold_bin<kHist12Bins>(h, want, &a);
-      if (lane == 0) {
-        res[0] = b;
-        res[1] = (int)a;
-      }
-    }
-    __syncthreads();
-    *above = (uint32_t)res[1];
-    return res[0];
-  };
-  pin(p0r);
-  // level 1: key bits 19..10 of the keys in bin b0
-  auto level1 = [&](int r, const uint2 (&pr)[kFinPer]) {
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i)
-      if (valid(r, i) && (pr[i].y >> kHist0Shift) == ub0) atomicAdd(&hist1[(pr[i].y >> 10) & 1023u], 1u);
-  };
-  level1(0, p0r);
-  for (int r = 1; r < rounds; ++r) {
-    uint2 pr[kFinPer];
-    load_round(r, cap, pr);
-    pin(pr);
-    level1(r, pr);
-  }
-  __syncthreads();
-  uint32_t want = (uint32_t)k - above0;
-  uint32_t above1;
-  const int b1 = find_bin(hist1, want, &above1);
-  want -= above1;
-  const uint32_t prefix22 = (ub0 << 10) | (uint32_t)b1;  // key bits 31..10 of K*
-  // level 2: the last 10 bits among the keys that share the top 22 bits
-  auto level2 = [&](int r, const uint2 (&pr)[kFinPer]) {
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i)
-      if (valid(r, i) && (pr[i].y >> 10) == prefix22) atomicAdd(&hist2[pr[i].y & 1023u], 1u);
-  };
-  level2(0, p0r);
-  for (int r = 1; r < rounds; ++r) {
-    uint2 pr[kFinPer];
-    load_round(r, cap, pr);
-    pin(pr);
-    level2(r, pr);
-  }
-  __syncthreads();
-  uint32_t above2;
-  const int b2 = find_bin(hist2, want, &above2);
-  want -= above2;
-  const uint32_t kstar = (prefix22 << 10) | (uint32_t)b2;  // the exact k-th largest key
-  const uint32_t take = want;                                 // ties at kstar to keep
-
-  // ordered emission, round by round: one scan gives, per thread, the keys
-  // above K* and the ties at K* in front of its run (16 bits each: a round
-  // holds at most 4096 candidates)
   int32_t *out = topk_idx + (size_t)t * k;
-  uint32_t gt_run = 0, tie_run = 0;
-  auto emit = [&](int r, const uint2 (&pr)[kFinPer]) {
-    uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i) {
-      const bool ok = valid(r, i);
-      n_gt += ok && pr[i].y > kstar;
-      n_eq += ok && pr[i].y == kstar;
-    }
-    uint32_t tot;
-    const uint32_t pre = block_exclusive_scan((n_eq << 16) | n_gt, scratch, &tot);
-    uint32_t tr = tie_run + (pre >> 16);                          // ties in front of this run
-    uint32_t o2 = gt_run + (pre & 0xFFFFu) + min(tr, take);       // outputs in front of it
-#pragma unroll
-    for (int i = 0; i < kFinPer; ++i) {
-      if (!valid(r, i)) continue;
-      bool sel = pr[i].y > kstar;
-      if (pr[i].y == kstar) {
-        sel = tr < take;
-        ++tr;
-      }
-      if (sel) {
-        if (o2 < (uint32_t)k) out[o2] = (int32_t)pr[i].x;
-        ++o2;
-      }
-    }
-    gt_run += tot & 0xFFFFu;
-    tie_run += tot >> 16;
-  };
-  emit(0, p0r);
-  for (int r = 1; r < rounds; ++r) {
-    uint2 pr[kFinPer];
-    load_round(r, cap, pr);
-    pin(pr);
-    emit(r, pr);
-  }
+  finish_query<kFinBlock>(k, ws, t, hist, scratch, res, [&](uint32_t o, int32_t pos) { out[o] = pos; });
 }
 
 }  // namespace
@@ -465,7 +337,7 @@ hipError_t launch_topk_hist0(const SeqMeta &m, int T, const float *scores, int64
 }
 
 hipError_t launch_topk_select(const SeqMeta &m, int T, int k, const float *scores, int64_t stride,
-                              const TopkWs &w, int32_t *topk_idx, hipStream_t s) {
+                              const TopkWs &w, int32_t *topk_idx, hipStream_t s, bool finish) {
   if (T == 0) return hipSuccess;
   int slots = 1;
   if (m.max_kv_len > k) {
@@ -482,7 +354,7 @@ hipError_t launch_topk_select(const SeqMeta &m, int T, int k, const float *score
   else
     hipLaunchKernelGGL(k_topk_select<false>, grid, dim3(kSelBlock), 0, s, m, k, scores, stride, w, topk_idx);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || m.max_kv_len <= k) return e;
+  if (e != hipSuccess || m.max_kv_len <= k || !finish) return e;
   hipLaunchKernelGGL(k_topk_finish, dim3(T), dim3(kFinBlock), 0, s, k, w, topk_idx);
   return hipGetLastError();
 }
