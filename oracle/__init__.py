@@ -7,6 +7,8 @@ it. The product path never calls it and has no CPU fallback.
 
 Modules:
   formats  exact decoders for fp32 / bf16 / E4M3FN / E8M0 / MXFP8 storage
+  quant    encoders into those formats and the cache append (new tokens
+           quantised into caller-chosen cache rows)
   sga      the four steps (index scores, top-k, sparse MLA, gate), the whole
            path, and a dense causal MLA reference
   case     glue that decodes a generated case (sga_inputs.SgaCase) for `sga`
@@ -18,4 +20,4 @@ of ReLU inside the indexer is a reading of the pages (they print no
 formula): that single modelling choice is "parity unpinned" by the pages.
 """
 
-from . import formats, sga  # noqa: F401
+from . import formats, quant, sga  # noqa: F401
