@@ -221,6 +221,100 @@ def indexer_only(args, case, prob, sga, torch):
     }), flush=True)
 
 
+def append_bytes(N, D, DI):
+    """Bytes one cache append of N tokens must move: bf16 source rows and keys
+    in, MXFP8 rows (values + one scale byte per 32) and FP8 keys out, and the
+    int64 slot of each token."""
+    return N * (2 * D + 2 * DI + D + D // 32 + DI + 8)
+
+
+def cache_append_bench(args, torch, sga):
+    """Cache append alone: a prefill chunk of new tokens quantised into the caches."""
+    from sga_inputs import block_scaled_rows
+    from sga_inputs.gen import FULL_DIMS
+
+    dev = torch.device("cuda", 0)
+    D = FULL_DIMS["d_latent"] + FULL_DIMS["d_rope"]
+    DI = FULL_DIMS["idx_dim"]
+    N = args.append_tokens
+    rows = max(N, 131072)
+    prob = sga.Problem.for_cache(num_kv_rows=rows, d_latent=FULL_DIMS["d_latent"],
+                                 d_rope=FULL_DIMS["d_rope"], idx_dim=DI, kv_dtype="mxfp8",
+                                 idx_dtype="fp8", device=dev)
+    srcs = [(block_scaled_rows(N, D, c, "bench.kv", device=dev),
+             block_scaled_rows(N, DI, c, "bench.ki", spread=2, device=dev))
+            for c in range(args.copies)]
+    caches = [(torch.empty((rows, D), dtype=torch.uint8, device=dev),
+               torch.empty((rows, D // 32), dtype=torch.uint8, device=dev),
+               torch.empty((rows, DI), dtype=torch.uint8, device=dev)) for _ in range(args.copies)]
+    slots = torch.arange(rows - N, rows, dtype=torch.int64, device=dev)
+
+    def step(i):
+        c = i % args.copies
+        kv, sc, ki = caches[c]
+        sga.sga_cache_append(prob, srcs[c][0], srcs[c][1], slots, kv, sc, ki)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = append_bytes(N, D, DI)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tps = N / (ms * 1e-3)
+    log(f"[bench] cache append of {N} tokens: {ms * 1e3:.1f} us per launch, {gbs:,.0f} GB/s "
+        f"({gbs / HBM_PEAK_GBS:.1%} of HBM), {tps:,.0f} tokens/s")
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline_append(srcs[0], D, DI)
+    print(json.dumps({
+        "metric": "SGA cache append tokens/s (bf16 -> MXFP8 latent rows + FP8 index keys); % of HBM roofline",
+        "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->fp8",
+        "data": "synthetic",
+        "config": {"workload": f"append_{N}_tokens", "tokens": N, "cache_rows": rows, "row": D,
+                   "idx_dim": DI, "kv": "mxfp8", "index": "fp8", "source": "bf16",
+                   "cache_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "k_cache_append (cache append)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                     "traffic": None},
+        "cpu_baseline": base,
+    }), flush=True)
+
+
+def cpu_baseline_append(src, D, DI, budget_s=10.0):
+    """The oracle's cache append timed on host cores over a bounded sample of
+    the same new tokens (as many leading tokens as fit the time budget)."""
+    import numpy as np
+
+    from oracle import quant
+
+    kv_new = src[0].float().cpu().numpy().astype(np.float64)
+    ki_new = src[1].float().cpu().numpy().astype(np.float64)
+    rows = 4096
+    kv = np.zeros((rows, D), np.uint8)
+    sc = np.zeros((rows, D // 32), np.uint8)
+    ki = np.zeros((rows, DI), np.uint8)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < min(rows, kv_new.shape[0]):
+        n = min(16, rows - done)
+        quant.cache_append(kv_new[done:done + n], ki_new[done:done + n], np.arange(done, done + n),
+                           kv, sc, ki, "mxfp8", "fp8")
+        done += n
+    dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {done} of the bench's new tokens (float64 Python encoder, one thread)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +326,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--indexer-only", action="store_true",
                     help="time only sga_index_scores (reported in TFLOP/s against the FP8 MFMA peak)")
+    ap.add_argument("--cache-append", action="store_true",
+                    help="time only sga_cache_append of --append-tokens new tokens (bf16 -> MXFP8 + FP8)")
+    ap.add_argument("--append-tokens", type=int, default=131072)
     args = ap.parse_args()
     if args.gpus != 1:
         log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -246,6 +343,8 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.cache_append:
+        return cache_append_bench(args, torch, sga)
     t0 = time.time()
     case = make_case(args.workload, device=dev)
     torch.cuda.synchronize()

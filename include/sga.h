@@ -188,6 +188,43 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
                          void *stream);
 
 /*
+ * Cache append: the step before the path in serving, which stores each new
+ * token's latent row and index key in the caches' storage formats. MXFP8 is
+ * the OCP microscaling FP8 that the A.X K2 Technical Report's FP8 section
+ * names (E4M3 elements, one shared scale per 32 consecutive values); the
+ * FP8 KV cache is the serving configuration of the inference sweep in the
+ * "Sparse Gated Attention" section of "A.X-K2: a sparse-attention upgrade
+ * that costs nothing, trained natively in FP8".
+ *   p          only num_kv_rows, d_latent, d_rope, idx_dim, kv_dtype and
+ *              idx_dtype are read (the sequence metadata may be NULL)
+ *   num_tokens N >= 0 new tokens
+ *   src_dtype  SGA_F32 or SGA_BF16: element type of kv_new and k_idx_new
+ *   kv_new     [N, Dc + Dr] new rows [c | kR], or NULL to write no latent rows
+ *   k_idx_new  [N, DI] new index keys, or NULL to write no index keys
+ *   slots      [N] int64 cache row of each token. A slot outside
+ *              [0, num_kv_rows) drops that token; valid slots must be
+ *              distinct (two tokens writing one row race). With a paged
+ *              cache the caller maps (sequence, position) to its slot.
+ *   kv         [num_kv_rows, Dc + Dr] kv_dtype: SGA_F32, SGA_BF16 or
+ *              SGA_MXFP8_E4M3FN (then kv_scale [num_kv_rows, (Dc + Dr) / 32])
+ *   k_idx      [num_kv_rows, DI] idx_dtype: SGA_F32 or SGA_FP8_E4M3FN
+ * Encodings: fp32 and bf16 sources are stored exactly in fp32 and a bf16
+ * source is copied to bf16; fp32 -> bf16 rounds to nearest even (NaN becomes
+ * the quiet NaN of its sign). FP8 E4M3FN rounds to nearest even and
+ * saturates at +-448; a NaN becomes 0x7F / 0xFF by its sign. An MXFP8 block
+ * of 32 values gets the scale 2^(floor(log2 max|v|) - 8), clamped to
+ * 2^-127 .. 2^127 (all zeros: 2^-127), and stores v / scale as E4M3FN; a
+ * block with an inf or NaN stores scale byte 0xFF and element bytes 0x7F.
+ * Index keys are stored unscaled.
+ * Requires Dc + Dr and DI to be multiples of 8 (Dc + Dr of 32 for MXFP8) and
+ * N * (Dc + Dr + DI) / 8 < 2^31. Rows not named by a valid slot are left
+ * untouched. Needs no workspace.
+ */
+sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dtype,
+                            const void *kv_new, const void *k_idx_new, const int64_t *slots,
+                            void *kv, uint8_t *kv_scale, void *k_idx, void *stream);
+
+/*
  * Phase timing of sga_layer_fwd, for measurement. While enabled, each
  * sga_layer_fwd call on this thread records HIP events on its stream around
  * each phase (0 index scores, 1 top-k, 2 sparse MLA, 3 combine + gate), for up

@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     CONFIG_NAMES,
     EXTRA_NAMES,
     SgaCase,
+    block_scaled_rows,
     config_dims,
     make_case,
     make_custom,

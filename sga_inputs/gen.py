@@ -172,6 +172,17 @@ def dyadic_weights(shape, seed, name, *, kind: str, device="cpu") -> torch.Tenso
     raise ValueError(kind)
 
 
+def block_scaled_rows(n: int, width: int, seed, name, *, dtype="bf16", spread: int = 12,
+                      device="cpu") -> torch.Tensor:
+    """[n, width] N(0, 1) values (bf16 or fp32) times 2^e, one e per 32 consecutive
+    values of a row, e uniform on {-spread..spread}: new cache rows whose blocks
+    span a range of magnitudes."""
+    x = normal((n, width), seed, name, dtype=dtype, device=device)
+    e = uniform_int((n, (width + 31) // 32), seed, name + ".e", -spread, spread, device=device)
+    f = torch.exp2(e.to(torch.float32)).repeat_interleave(32, dim=1)[:, :width]
+    return (x.float() * f).to(x.dtype)  # exact: scaling by a power of two
+
+
 def uniform01(n: int, seed: int, name: str) -> List[float]:
     """n floats in [0, 1) (host-side, float64), for metadata such as lengths."""
     h = hash32(seed, name, torch.arange(n, dtype=torch.int64))

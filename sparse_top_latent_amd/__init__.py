@@ -77,6 +77,17 @@ class Problem:
                    q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, idx_dtype=case.idx_dtype,
                    gate_dtype=case.gate_dtype, out_dtype=out_dtype or case.out_dtype)
 
+    @classmethod
+    def for_cache(cls, *, num_kv_rows, d_latent, d_rope, idx_dim, kv_dtype, idx_dtype,
+                  device="cuda") -> "Problem":
+        """Problem for sga_cache_append, which reads only the cache geometry and dtypes."""
+        e32 = torch.empty(0, dtype=torch.int32, device=device)
+        e64 = torch.empty(0, dtype=torch.int64, device=device)
+        return cls(q_seq=e32, q_pos=e32, kv_start=e64, kv_len=e32, max_kv_len=0,
+                   num_kv_rows=num_kv_rows, heads=1, d_latent=d_latent, d_rope=d_rope,
+                   idx_heads=1, idx_dim=idx_dim, topk=1, softmax_scale=1.0, q_dtype="bf16",
+                   kv_dtype=kv_dtype, idx_dtype=idx_dtype)
+
     @property
     def ptr(self):
         return ctypes.byref(self.c)
@@ -181,6 +192,34 @@ def sga_layer_fwd(prob: Problem, q_idx, w, k_idx, q, kv, kv_scale, gate, out, to
         _ptr(topk_idx_out, "topk_idx_out", None, T * c.topk),
         pl,
         _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def sga_cache_append(prob: Problem, kv_new, k_idx_new, slots, kv, kv_scale, k_idx,
+                     stream=None) -> None:
+    """Quantise new tokens into cache rows `slots` (see sga_cache_append in sga.h).
+
+    kv_new [N, Dc + Dr] and k_idx_new [N, DI] share one source dtype (float32
+    or bfloat16); either may be None to skip that part.
+    """
+    c = prob.c
+    D, DI = c.d_latent + c.d_rope, c.idx_dim
+    if slots.dtype != torch.int64:
+        raise ValueError("slots must be int64")
+    N = slots.numel()
+    srcs = [t for t in (kv_new, k_idx_new) if t is not None]
+    if any(t.dtype != srcs[0].dtype for t in srcs):
+        raise ValueError("kv_new and k_idx_new must share a dtype")
+    src = SGA_BF16 if srcs and srcs[0].dtype == torch.bfloat16 else SGA_F32
+    _ffi.check(lib().sga_cache_append(
+        prob.ptr, N, src,
+        _ptr(kv_new, "kv_new", (src,), N * D),
+        _ptr(k_idx_new, "k_idx_new", (src,), N * DI),
+        _ptr(slots, "slots", None, N),
+        _ptr(kv, "kv", (c.kv_dtype,), c.num_kv_rows * D if kv_new is not None else None),
+        _ptr(kv_scale, "kv_scale", (SGA_FP8_E4M3FN,),
+             c.num_kv_rows * (D // 32) if kv_scale is not None else None),
+        _ptr(k_idx, "k_idx", (c.idx_dtype,), c.num_kv_rows * DI if k_idx_new is not None else None),
         _stream(stream)))
 
 

@@ -35,6 +35,7 @@ EXPORTS = (
     "sga_topk_select",
     "sga_sparse_mla_fwd",
     "sga_layer_fwd",
+    "sga_cache_append",
     "sga_profile_enable",
     "sga_profile_collect",
 )
@@ -96,6 +97,8 @@ def load() -> ctypes.CDLL:
         "sga_topk_select": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
         "sga_sparse_mla_fwd": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "sga_layer_fwd": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "sga_cache_append": ([P, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp],
+                             ctypes.c_int),
         "sga_profile_enable": ([ctypes.c_int], ctypes.c_int),
         "sga_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int)], ctypes.c_int),

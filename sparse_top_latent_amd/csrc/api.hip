@@ -387,6 +387,53 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
   }
 }
 
+sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dtype,
+                            const void *kv_new, const void *k_idx_new, const int64_t *slots,
+                            void *kv, uint8_t *kv_scale, void *k_idx, void *stream) {
+  try {
+    if (!p) return fail(SGA_ERR_INVALID_ARGUMENT, "problem is NULL");
+    if (num_tokens < 0 || p->num_kv_rows < 0)
+      return fail(SGA_ERR_INVALID_ARGUMENT, "negative size (num_tokens=%lld num_kv_rows=%lld)",
+                  (long long)num_tokens, (long long)p->num_kv_rows);
+    if (src_dtype != SGA_F32 && src_dtype != SGA_BF16)
+      return fail(SGA_ERR_UNSUPPORTED, "source dtype must be SGA_F32 or SGA_BF16");
+    const int64_t D = (int64_t)p->d_latent + p->d_rope;
+    const int64_t DI = p->idx_dim;
+    if (kv_new) {
+      if (p->d_latent < 1 || p->d_rope < 0)
+        return fail(SGA_ERR_INVALID_ARGUMENT, "d_latent must be >= 1, d_rope >= 0");
+      if (p->kv_dtype != SGA_F32 && p->kv_dtype != SGA_BF16 && p->kv_dtype != SGA_MXFP8_E4M3FN)
+        return fail(SGA_ERR_UNSUPPORTED, "kv dtype must be SGA_F32, SGA_BF16 or SGA_MXFP8_E4M3FN");
+      if (D % (p->kv_dtype == SGA_MXFP8_E4M3FN ? 32 : 8))
+        return fail(SGA_ERR_UNSUPPORTED, "row width %lld must be a multiple of %d", (long long)D,
+                    p->kv_dtype == SGA_MXFP8_E4M3FN ? 32 : 8);
+      if (num_tokens > 0 && !kv) return fail(SGA_ERR_INVALID_ARGUMENT, "kv is NULL");
+      if (num_tokens > 0 && p->kv_dtype == SGA_MXFP8_E4M3FN && !kv_scale)
+        return fail(SGA_ERR_INVALID_ARGUMENT, "MXFP8 rows need kv_scale");
+    }
+    if (k_idx_new) {
+      if (DI < 1 || DI % 8)
+        return fail(SGA_ERR_UNSUPPORTED, "idx_dim %lld must be a positive multiple of 8",
+                    (long long)DI);
+      if (p->idx_dtype != SGA_F32 && p->idx_dtype != SGA_FP8_E4M3FN)
+        return fail(SGA_ERR_UNSUPPORTED, "index key dtype must be SGA_F32 or SGA_FP8_E4M3FN");
+      if (num_tokens > 0 && !k_idx) return fail(SGA_ERR_INVALID_ARGUMENT, "k_idx is NULL");
+    }
+    const int64_t units = num_tokens * ((kv_new ? D : 0) + (k_idx_new ? DI : 0)) / 8;
+    if (units >= ((int64_t)1 << 31))
+      return fail(SGA_ERR_UNSUPPORTED, "%lld tokens are more than one call takes",
+                  (long long)num_tokens);
+    if (num_tokens == 0 || (!kv_new && !k_idx_new)) return SGA_OK;
+    if (!slots) return fail(SGA_ERR_INVALID_ARGUMENT, "slots is NULL");
+    return launched(launch_cache_append(num_tokens, (int)D, (int)DI, src_dtype, kv_new, k_idx_new,
+                                        slots, p->num_kv_rows, p->kv_dtype, kv, kv_scale,
+                                        p->idx_dtype, k_idx, (hipStream_t)stream),
+                    "cache append");
+  } catch (...) {
+    return fail(SGA_ERR_DEVICE, "internal error");
+  }
+}
+
 sga_status sga_profile_enable(int max_calls) {
   try {
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);

@@ -85,4 +85,14 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s);
 bool mla_fuse_finish(int T, int k);
 hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s);
 
+// --- cache append ---------------------------------------------------------------
+// Token i's row kv_new[i] (D values) and key kidx_new[i] (DI values) go to cache
+// row slots[i] in kv_dtype / idx_dtype; slots outside [0, rows) are dropped.
+// A NULL kv_new or kidx_new skips that part. Needs D and DI multiples of 8
+// (D of 32 for MXFP8) and N * (D + DI) / 8 < 2^32.
+hipError_t launch_cache_append(int64_t N, int D, int DI, int src_dtype, const void *kv_new,
+                               const void *kidx_new, const int64_t *slots, int64_t rows,
+                               int kv_dtype, void *kv, uint8_t *kv_scale, int idx_dtype,
+                               void *k_idx, hipStream_t s);
+
 }  // namespace sga

@@ -147,3 +147,36 @@ def test_profile_collect_without_calls(lib):
     assert lib.sga_profile_collect(ms, 4, ctypes.byref(calls)) == 0
     assert calls.value == 0 and list(ms) == [0.0] * 4
     assert lib.sga_profile_collect(None, 4, ctypes.byref(calls)) == 1
+
+
+@pytest.mark.parametrize("kw,args,status", [
+    (dict(), dict(src=7), 2),                                     # source dtype
+    (dict(kv_dtype=2), dict(), 2),                                # FP8 latent rows: not a cache format
+    (dict(d_rope=48, kv_dtype=3), dict(), 2),                     # MXFP8 row not a multiple of 32
+    (dict(d_rope=60, kv_dtype=1), dict(), 2),                     # row not a multiple of 8
+    (dict(idx_dim=100), dict(), 2),                               # key not a multiple of 8
+    (dict(idx_dtype=1), dict(), 2),                               # bf16 keys: not a cache format
+    (dict(), dict(n=-1), 1),
+    (dict(), dict(slots=None), 1),
+    (dict(), dict(kv=None), 1),
+    (dict(kv_dtype=3), dict(kv_scale=None), 1),
+    (dict(), dict(k_idx=None), 1),
+    (dict(), dict(n=1 << 30), 2),                                 # more units than one launch takes
+])
+def test_cache_append_argument_errors(lib, kw, args, status):
+    p = _problem(**kw)
+    a = dict(n=16, src=1, kv_new=FAKE, k_idx_new=FAKE, slots=FAKE, kv=FAKE, kv_scale=FAKE,
+             k_idx=FAKE)
+    a.update(args)
+    st = lib.sga_cache_append(ctypes.byref(p), a["n"], a["src"], a["kv_new"], a["k_idx_new"],
+                              a["slots"], a["kv"], a["kv_scale"], a["k_idx"], None)
+    assert st == status, lib.sga_last_error()
+    assert lib.sga_last_error()
+
+
+def test_cache_append_nothing_to_do(lib):
+    p = _problem()
+    # no tokens, or neither part given: returns before touching any pointer
+    assert lib.sga_cache_append(ctypes.byref(p), 0, 1, FAKE, FAKE, None, None, None, None, None) == 0
+    assert lib.sga_cache_append(ctypes.byref(p), 16, 1, None, None, None, None, None, None, None) == 0
+    assert lib.sga_cache_append(None, 16, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
