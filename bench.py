@@ -33,6 +33,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_scores_fp8_traffic.json")
 # the sources the decode index kernel is compiled from
 INDEX_SRCS = [os.path.join(ROOT, "sparse_top_latent_amd", "csrc", f)
               for f in ("index_scores.hip", "index_common.h", "common.h", "kernels.h")]
+# the sources the cache append kernel is compiled from
+APPEND_SRCS = [os.path.join(ROOT, "sparse_top_latent_amd", "csrc", f)
+               for f in ("cache_append.hip", "common.h", "kernels.h")]
 
 
 def log(*a):
@@ -61,21 +64,21 @@ def algorithmic_bytes(case):
     return total + keys, index + keys
 
 
-def traffic_record(workload):
-    """Measured HBM bytes of the index kernel, if taken on the current source
-    and for this workload."""
+def traffic_record(workload, name=None, srcs=None):
+    """Measured HBM bytes of a kernel (by default the decode index kernel), if
+    taken on the current sources and for this workload."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(ROOT, "profiles", name) if name else TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != index_source_sha() or rec.get("workload") != workload:
+    if rec.get("source_sha256") != index_source_sha(srcs) or rec.get("workload") != workload:
         return None
-    return rec
+    return rec.get("hbm_bytes_per_launch") if name else rec
 
 
-def index_source_sha():
+def index_source_sha(srcs=None):
     h = hashlib.sha256()
-    for f in INDEX_SRCS:
+    for f in srcs or INDEX_SRCS:
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -269,8 +272,22 @@ def cache_append_bench(args, torch, sga):
     nbytes = append_bytes(N, D, DI)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tps = N / (ms * 1e-3)
+    # reference: a plain device copy moving the same bytes (half read, half written)
+    a = torch.empty(nbytes // 2, dtype=torch.uint8, device=dev)
+    bs = [torch.empty_like(a) for _ in range(args.copies)]
+    for b in bs:
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        bs[i % args.copies].copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbs = nbytes / (ev0.elapsed_time(ev1) / args.steps * 1e-3) / 1e9
+    del a, bs
     log(f"[bench] cache append of {N} tokens: {ms * 1e3:.1f} us per launch, {gbs:,.0f} GB/s "
-        f"({gbs / HBM_PEAK_GBS:.1%} of HBM), {tps:,.0f} tokens/s")
+        f"({gbs / HBM_PEAK_GBS:.1%} of HBM, {gbs / copy_gbs:.1%} of a plain device copy's "
+        f"{copy_gbs:,.0f} GB/s), {tps:,.0f} tokens/s")
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline_append(srcs[0], D, DI)
@@ -286,7 +303,9 @@ def cache_append_bench(args, torch, sga):
         "roofline": {"bound": "hbm", "kernel": "k_cache_append (cache append)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
-                     "traffic": None},
+                     "traffic": traffic_record(f"append_{N}_tokens", "cache_append_traffic.json",
+                                               APPEND_SRCS),
+                     "copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4)},
         "cpu_baseline": base,
     }), flush=True)
 

@@ -137,28 +137,40 @@ struct AppendArgs {
   uint32_t key_units;     // DI / 8
 };
 
+// One unit: 8 consecutive values of one token's latent row or index key.
+struct Unit {
+  F8 x;
+  uint4 raw;
+  int64_t slot;
+  uint32_t tok, j;
+  bool kv;
+};
+
+template <int kSrc>
+__device__ __forceinline__ void unit_load(const AppendArgs &a, uint32_t u, Unit &w) {
+  w.kv = u < a.kv_units;
+  const uint32_t v = w.kv ? u : u - a.kv_units;
+  const uint32_t per = w.kv ? a.row_units : a.key_units;
+  w.tok = v / per;
+  w.j = v - w.tok * per;
+  const void *src = w.kv ? a.kv_new : a.kidx_new;
+  // tok < N keeps the source load inside the new rows whatever the slot
+  load8<kSrc>(src, (int64_t)w.tok * per * 8 + w.j * 8, w.x, w.raw);
+  w.slot = a.slots[w.tok];
+}
+
 template <int kSrc, int kKv, int kIdx>
-__global__ __launch_bounds__(kAppendBlock) void k_cache_append(AppendArgs a) {
-  const uint32_t u = blockIdx.x * kAppendBlock + threadIdx.x;
-  if (u >= a.total_units) return;
-  if (u < a.kv_units) {
-    const uint32_t tok = u / a.row_units, j = u - tok * a.row_units;
-    const int64_t D = (int64_t)a.row_units * 8;
-    // the source load goes out before the slot is known (tok < N keeps it
-    // inside kv_new), so the two latencies overlap
-    F8 x;
-    uint4 raw;
-    load8<kSrc>(a.kv_new, (int64_t)tok * D + j * 8, x, raw);
-    const int64_t slot = a.slots[tok];
-    // a dropped token drops its whole row, so a quad stays together
-    if (slot < 0 || slot >= a.rows) return;
-    const int64_t dst = slot * D + j * 8;
+__device__ __forceinline__ void unit_store(const AppendArgs &a, const Unit &w) {
+  // a dropped token drops its whole row, so the quad of an MXFP8 block stays together
+  if (w.slot < 0 || w.slot >= a.rows) return;
+  if (w.kv) {
+    const int64_t dst = w.slot * a.row_units * 8 + w.j * 8;
     if (kKv == SGA_F32) {
-      store_f32(a.kv, dst, x);
+      store_f32(a.kv, dst, w.x);
     } else if (kKv == SGA_BF16) {
-      store_bf16<kSrc>(a.kv, dst, x, raw);
+      store_bf16<kSrc>(a.kv, dst, w.x, w.raw);
     } else {
-      const uint32_t ef = quad_max(abs_bits_max(x)) >> 23;  // biased exponent of the block max
+      const uint32_t ef = quad_max(abs_bits_max(w.x)) >> 23;  // biased exponent of the block max
       uint2 codes;
       uint32_t sbyte;
       if (ef == 255u) {  // inf or NaN in the block
@@ -171,32 +183,45 @@ __global__ __launch_bounds__(kAppendBlock) void k_cache_append(AppendArgs a) {
         const float inv = __uint_as_float((254u - sbyte) << 23);  // 2^-(sbyte - 127), exact
         F8 y;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y.v[e] = x.v[e] * inv;
+        for (int e = 0; e < 8; ++e) y.v[e] = w.x.v[e] * inv;
         codes = to_e4m3fn<false>(y);
       }
       *(uint2 *)((uint8_t *)a.kv + dst) = codes;
-      if ((j & 3u) == 0u) a.kv_scale[slot * (int64_t)(a.row_units / 4) + j / 4] = (uint8_t)sbyte;
+      if ((w.j & 3u) == 0u) a.kv_scale[w.slot * (int64_t)(a.row_units / 4) + w.j / 4] = (uint8_t)sbyte;
     }
   } else {
-    const uint32_t v = u - a.kv_units;
-    const uint32_t tok = v / a.key_units, j = v - tok * a.key_units;
-    const int64_t DI = (int64_t)a.key_units * 8;
-    F8 x;
-    uint4 raw;
-    load8<kSrc>(a.kidx_new, (int64_t)tok * DI + j * 8, x, raw);
-    const int64_t slot = a.slots[tok];
-    if (slot < 0 || slot >= a.rows) return;
-    const int64_t dst = slot * DI + j * 8;
+    const int64_t dst = w.slot * a.key_units * 8 + w.j * 8;
     if (kIdx == SGA_F32)
-      store_f32(a.k_idx, dst, x);
+      store_f32(a.k_idx, dst, w.x);
     else
-      *(uint2 *)((uint8_t *)a.k_idx + dst) = to_e4m3fn<true>(x);
+      *(uint2 *)((uint8_t *)a.k_idx + dst) = to_e4m3fn<true>(w.x);
+  }
+}
+
+// Each thread takes kAppendUnits units, kAppendBlock apart, and issues all of
+// their loads before converting any: more bytes in flight per wave.
+constexpr int kAppendUnits = 2;
+
+template <int kSrc, int kKv, int kIdx>
+__global__ __launch_bounds__(kAppendBlock) void k_cache_append(AppendArgs a) {
+  const uint32_t base = blockIdx.x * (kAppendBlock * kAppendUnits) + threadIdx.x;
+  Unit w[kAppendUnits];
+#pragma unroll
+  for (int r = 0; r < kAppendUnits; ++r) {
+    const uint32_t u = base + r * kAppendBlock;
+    if (u < a.total_units) unit_load<kSrc>(a, u, w[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < kAppendUnits; ++r) {
+    const uint32_t u = base + r * kAppendBlock;
+    if (u < a.total_units) unit_store<kSrc, kKv, kIdx>(a, w[r]);
   }
 }
 
 template <int kSrc, int kKv, int kIdx>
 hipError_t launch3(const AppendArgs &a, hipStream_t s) {
-  const uint32_t blocks = (a.total_units + kAppendBlock - 1) / kAppendBlock;
+  const uint32_t per_block = kAppendBlock * kAppendUnits;
+  const uint32_t blocks = (a.total_units + per_block - 1) / per_block;
   hipLaunchKernelGGL((k_cache_append<kSrc, kKv, kIdx>), dim3(blocks), dim3(kAppendBlock), 0, s, a);
   return hipGetLastError();
 }
