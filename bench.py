@@ -348,6 +348,9 @@ def main():
     ap.add_argument("--cache-append", action="store_true",
                     help="time only sga_cache_append of --append-tokens new tokens (bf16 -> MXFP8 + FP8)")
     ap.add_argument("--append-tokens", type=int, default=131072)
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="lay the caches out in pages of this many rows (seeded random page order, "
+                         "block table) instead of contiguous rows")
     args = ap.parse_args()
     if args.gpus != 1:
         log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -366,6 +369,10 @@ def main():
         return cache_append_bench(args, torch, sga)
     t0 = time.time()
     case = make_case(args.workload, device=dev)
+    if args.page_size:
+        from sga_inputs import paged_copy
+
+        case = paged_copy(case, args.page_size)
     torch.cuda.synchronize()
     log(f"[bench] generated {args.workload} on the GPU in {time.time() - t0:.1f} s "
         f"({case.num_kv_rows} cached rows, {case.num_q} queries)")
@@ -455,7 +462,7 @@ def main():
     stream_gbs = stream_read_gbs(torch, kvs[1 % args.copies])
     log(f"[bench] index kernel {achieved:,.0f} GB/s; plain streaming read (torch sum over "
         f"{kvs[0].numel() * kvs[0].element_size() / 1e9:.2f} GB) {stream_gbs:,.0f} GB/s")
-    rec = traffic_record(case.name)
+    rec = traffic_record(args.workload) if not args.page_size else None
     # Several queries per sequence share the scan of its index keys. With few
     # of them (multi-query decode) the index pass stays HBM-bound; with many
     # (prefill) its FLOP per key byte pass the FP8 ridge (625 FLOP/B) and it is
@@ -480,7 +487,7 @@ def main():
             "traffic": None if rec is None else rec["hbm_bytes_per_launch"],
             "frac_of_stream_read": round(achieved / stream_gbs, 4),
         }
-    if case.name == "decode_b16_n128k":
+    if case.name == "decode_b16_n128k" and not args.page_size:
         metric = METRIC
     elif mfma_bound:
         metric = f"SGA prefill layer queries/s ({T} queries over {case.num_seqs} sequence(s)); index pass % of FP8 MFMA peak"
@@ -505,7 +512,7 @@ def main():
                    "ctx": case.max_kv_len, "topk": case.topk, "heads": H, "d_latent": Dc,
                    "d_rope": case.d_rope, "idx_heads": case.idx_heads, "idx_dim": case.idx_dim,
                    "kv": case.kv_dtype, "index": case.idx_dtype, "out": case.out_dtype,
-                   "cache_copies": args.copies},
+                   "cache_copies": args.copies, "page_size": args.page_size},
         "step_hbm": None if mfma_bound else {
             "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(step_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": total_bytes,
@@ -515,7 +522,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.page_size:  # (the paged run adds no new oracle work)
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(result), flush=True)

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define SGA_ABI_VERSION 1
+#define SGA_ABI_VERSION 2
 
 typedef enum sga_status {
   SGA_OK = 0,
@@ -92,7 +92,7 @@ typedef struct sga_problem {
   int32_t num_seqs;      /* B: sequences in the caches                                   */
   int32_t num_q;         /* T: query rows                                                */
   int32_t max_kv_len;    /* host bound on every kv_len[b]; row stride of the score buffer */
-  int32_t reserved0;     /* must be 0                                                    */
+  int32_t page_size;     /* 0: contiguous rows (kv_start); else rows in pages (see below) */
   int64_t num_kv_rows;   /* rows in kv, kv_scale and k_idx                               */
   int32_t heads;         /* H: attention heads (64)                                      */
   int32_t d_latent;      /* Dc: latent width = value width (512)                          */
@@ -108,9 +108,29 @@ typedef struct sga_problem {
   int32_t out_dtype;     /* sga_dtype of out                                               */
   const int32_t *q_seq;  /* [T] sequence of each query row                                 */
   const int32_t *q_pos;  /* [T] position of each query row within its sequence             */
-  const int64_t *kv_start; /* [B] cache row holding position 0 of each sequence           */
+  const int64_t *kv_start; /* [B] cache row holding position 0 of each sequence (contiguous
+                              layout; ignored, may be NULL, when page_size > 0)          */
   const int32_t *kv_len;   /* [B] cached tokens of each sequence                           */
+  const int32_t *block_table; /* [B, max_pages] page of each sequence's positions, or NULL  */
+  int32_t max_pages;     /* row length of block_table (0 when page_size is 0)             */
+  int32_t reserved0;     /* must be 0                                                    */
 } sga_problem;
+
+/*
+ * Cache layouts (every entry point that reads kv, kv_scale or k_idx)
+ *   - contiguous (page_size = 0): position s of sequence b is cache row
+ *     kv_start[b] + s; the sequence's length is clipped to num_kv_rows -
+ *     kv_start[b].
+ *   - paged (page_size a power of two, 64 <= page_size <= 65536): the caches
+ *     are num_kv_rows / page_size pages of page_size rows, and position s of
+ *     sequence b is row block_table[b * max_pages + s / page_size] * page_size
+ *     + s % page_size (the block table of a paged KV cache; the serving stack
+ *     the pages deploy with keeps its cache this way). The sequence's length
+ *     is clipped to max_pages * page_size. A page id outside
+ *     [0, num_kv_rows / page_size) reads page 0 instead (the kernels stay
+ *     inside the caches; the result for those positions is unspecified).
+ *     The block table lives on the device and is not checked on the host.
+ */
 
 /* ABI version of the loaded library (SGA_ABI_VERSION). */
 int sga_abi_version(void);

@@ -29,6 +29,28 @@ def _dec(t, dtype: str, scales=None) -> np.ndarray:
     return formats.decode(raw(t), dtype, None if scales is None else raw(scales))
 
 
+def cache_rows(case, b: int, positions: np.ndarray, kv_start: np.ndarray, table) -> np.ndarray:
+    """Cache rows of positions of sequence b: kv_start[b] + s, or, in the paged
+    layout, table[b, s // P] * P + s % P, where a page id outside the cache
+    stands for page 0."""
+    positions = np.asarray(positions, dtype=np.int64)
+    if not case.page_size:
+        return int(kv_start[b]) + positions
+    P = int(case.page_size)
+    pg = table[b, positions // P].astype(np.int64)
+    pg = np.where((pg < 0) | (pg >= case.num_kv_rows // P), 0, pg)
+    return pg * P + positions % P
+
+
+def seq_capacity(case, b: int, kv_len: np.ndarray) -> int:
+    """Cached length of sequence b as the caches hold it (the paged layout
+    holds at most max_pages * page_size positions)."""
+    n = int(kv_len[b])
+    if case.page_size:
+        n = min(n, case.block_table.shape[1] * int(case.page_size))
+    return n
+
+
 def run_queries(case, queries: Optional[Iterable[int]] = None, *, keep_scores: bool = True,
                 topk: Optional[int] = None) -> Dict[str, object]:
     """Oracle SGA forward on the listed queries of `case` (all by default)."""
@@ -39,6 +61,7 @@ def run_queries(case, queries: Optional[Iterable[int]] = None, *, keep_scores: b
     q_pos = raw(case.q_pos).astype(np.int64)
     kv_start = raw(case.kv_start).astype(np.int64)
     kv_len = raw(case.kv_len).astype(np.int64)
+    table = raw(case.block_table).astype(np.int64) if case.page_size else None
     idx_dt = "fp8" if case.idx_dtype == "fp8" else "f32"
     H, Dc = case.heads, case.d_latent
     out_idx = np.full((len(qs), k), -1, dtype=np.int64)
@@ -46,12 +69,15 @@ def run_queries(case, queries: Optional[Iterable[int]] = None, *, keep_scores: b
     out_lse = np.full((len(qs), H), -np.inf)
     scores, exact = [], []
     for i, t in enumerate(qs):
+        import torch
+
         b = int(q_seq[t])
-        start = int(kv_start[b])
-        n = sga.visible_count(q_pos[t], kv_len[b])
+        n = sga.visible_count(q_pos[t], seq_capacity(case, b, kv_len))
         q_idx_t = _dec(case.q_idx[t], idx_dt)
         w_t = raw(case.w[t]).astype(np.float64)
-        keys = _dec(case.k_idx[start:start + n], idx_dt)
+        key_rows = torch.as_tensor(cache_rows(case, b, np.arange(n), kv_start, table),
+                                   dtype=torch.int64, device=case.k_idx.device)
+        keys = _dec(case.k_idx.index_select(0, key_rows), idx_dt)
         s64 = sga.index_scores(q_idx_t, w_t, keys)
         exact.append(sga.fp32_exact_bound(q_idx_t, w_t, keys))
         s32 = sga.to_fp32(s64)
@@ -60,9 +86,8 @@ def run_queries(case, queries: Optional[Iterable[int]] = None, *, keep_scores: b
         sel = sga.select_topk(s32, k)
         out_idx[i] = sel
         chosen = sel[sel >= 0]
-        import torch
-
-        rows_idx = torch.as_tensor(start + chosen, dtype=torch.int64, device=case.kv.device)
+        rows_idx = torch.as_tensor(cache_rows(case, b, chosen, kv_start, table), dtype=torch.int64,
+                                   device=case.kv.device)
         kv_rows = case.kv.index_select(0, rows_idx)
         if case.kv_dtype == "mxfp8":
             rows = _dec(kv_rows, "mxfp8", case.kv_scale.index_select(0, rows_idx))

@@ -20,4 +20,5 @@ from .gen import (  # noqa: F401
     config_dims,
     make_case,
     make_custom,
+    paged_copy,
 )

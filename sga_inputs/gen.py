@@ -229,6 +229,10 @@ class SgaCase:
     gate: Optional[torch.Tensor]
     seed: int = 0
     extra: Dict = field(default_factory=dict)
+    # paged layout: position s of sequence b is cache row
+    # block_table[b, s // page_size] * page_size + s % page_size (kv_start unused)
+    page_size: int = 0
+    block_table: Optional[torch.Tensor] = None
 
     @property
     def num_seqs(self) -> int:
@@ -240,7 +244,7 @@ class SgaCase:
 
     @property
     def num_kv_rows(self) -> int:
-        return int(sum(self.lens))
+        return int(self.kv.shape[0]) if self.page_size else int(sum(self.lens))
 
     @property
     def max_kv_len(self) -> int:
@@ -260,9 +264,55 @@ class SgaCase:
 
         c = SgaCase(**{k: getattr(self, k) for k in self.__dataclass_fields__})
         for k in ("q_seq", "q_pos", "kv_start", "kv_len", "q", "kv", "kv_scale",
-                  "q_idx", "k_idx", "w", "gate"):
+                  "q_idx", "k_idx", "w", "gate", "block_table"):
             setattr(c, k, mv(getattr(self, k)))
         return c
+
+
+def paged_copy(case: SgaCase, page_size: int, *, seed: int = 0, spare_pages: int = 3) -> SgaCase:
+    """The same logical caches laid out in pages of page_size rows.
+
+    Every sequence takes ceil(len / page_size) pages; the pages of all
+    sequences, plus `spare_pages` unused ones, are placed in a seeded random
+    order (the order of hash32 values), and block_table[b, j] names the
+    physical page of page j of sequence b (-1 past its last page). Rows of a
+    page past the sequence's end, and spare pages, hold zeros. Only data moves
+    here: the copy holds exactly the rows of `case`.
+    """
+    P = int(page_size)
+    dev = case.kv.device
+    lens = [int(n) for n in case.lens]
+    npages = [(n + P - 1) // P for n in lens]
+    total = sum(npages) + spare_pages
+    order = torch.argsort(hash32(seed, "pages", torch.arange(total, dtype=torch.int64)))
+    max_pages = max(max(npages), 1)
+    table = torch.full((len(lens), max_pages), -1, dtype=torch.int32)
+    src_of_dst = torch.full((total * P,), -1, dtype=torch.int64)
+    starts = case.kv_start.cpu().tolist()
+    g = 0
+    for b, n in enumerate(lens):
+        for j in range(npages[b]):
+            phys = int(order[g])
+            g += 1
+            table[b, j] = phys
+            m = min(P, n - j * P)
+            src_of_dst[phys * P: phys * P + m] = torch.arange(starts[b] + j * P, starts[b] + j * P + m)
+    valid = (src_of_dst >= 0).to(dev)
+    src = src_of_dst.clamp(min=0).to(dev)
+
+    def move(x):
+        if x is None:
+            return None
+        y = x.index_select(0, src)
+        y[~valid] = 0
+        return y
+
+    c = SgaCase(**{k: getattr(case, k) for k in case.__dataclass_fields__})
+    c.name = f"{case.name}_paged{P}"
+    c.kv, c.kv_scale, c.k_idx = move(case.kv), move(case.kv_scale), move(case.k_idx)
+    c.page_size = P
+    c.block_table = table.to(dev)
+    return c
 
 
 TINY_DIMS = dict(heads=8, d_latent=64, d_rope=16, idx_heads=2, idx_dim=32, topk=64)

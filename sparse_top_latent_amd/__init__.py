@@ -47,23 +47,35 @@ class Problem:
 
     def __init__(self, *, q_seq, q_pos, kv_start, kv_len, max_kv_len, num_kv_rows, heads,
                  d_latent, d_rope, idx_heads, idx_dim, topk, softmax_scale, q_dtype="bf16",
-                 kv_dtype="bf16", idx_dtype="fp8", gate_dtype="bf16", out_dtype="bf16"):
-        for name, t, dt in (("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
-                            ("kv_start", kv_start, torch.int64), ("kv_len", kv_len, torch.int32)):
+                 kv_dtype="bf16", idx_dtype="fp8", gate_dtype="bf16", out_dtype="bf16",
+                 page_size=0, block_table=None):
+        """Contiguous caches (kv_start) or, with page_size > 0, paged caches
+        addressed through block_table [num_seqs, max_pages] (int32)."""
+        metas = [("q_seq", q_seq, torch.int32), ("q_pos", q_pos, torch.int32),
+                 ("kv_len", kv_len, torch.int32)]
+        if page_size:
+            if block_table is None or block_table.dim() != 2 or block_table.shape[0] != kv_len.numel():
+                raise ValueError("paged caches need block_table [num_seqs, max_pages]")
+            metas.append(("block_table", block_table, torch.int32))
+        else:
+            metas.append(("kv_start", kv_start, torch.int64))
+        for name, t, dt in metas:
             if t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor")
-        if q_seq.numel() != q_pos.numel() or kv_start.numel() != kv_len.numel():
+        if q_seq.numel() != q_pos.numel() or (not page_size and kv_start.numel() != kv_len.numel()):
             raise ValueError("metadata lengths disagree")
-        self._keep = (q_seq, q_pos, kv_start, kv_len)
+        self._keep = (q_seq, q_pos, kv_start, kv_len, block_table)
         code = lambda d: d if isinstance(d, int) else _DTYPE_CODES[d]  # noqa: E731
         self.c = SgaProblem(
-            num_seqs=kv_len.numel(), num_q=q_pos.numel(), max_kv_len=int(max_kv_len), reserved0=0,
+            num_seqs=kv_len.numel(), num_q=q_pos.numel(), max_kv_len=int(max_kv_len),
             num_kv_rows=int(num_kv_rows), heads=heads, d_latent=d_latent, d_rope=d_rope,
             idx_heads=idx_heads, idx_dim=idx_dim, topk=topk, softmax_scale=float(softmax_scale),
             q_dtype=code(q_dtype), kv_dtype=code(kv_dtype), idx_dtype=code(idx_dtype),
             gate_dtype=code(gate_dtype or "f32"), out_dtype=code(out_dtype),
-            q_seq=q_seq.data_ptr(), q_pos=q_pos.data_ptr(), kv_start=kv_start.data_ptr(),
-            kv_len=kv_len.data_ptr())
+            q_seq=q_seq.data_ptr(), q_pos=q_pos.data_ptr(),
+            kv_start=None if page_size else kv_start.data_ptr(), kv_len=kv_len.data_ptr(),
+            page_size=int(page_size), block_table=block_table.data_ptr() if page_size else None,
+            max_pages=int(block_table.shape[1]) if page_size else 0, reserved0=0)
 
     @classmethod
     def from_case(cls, case, *, topk: Optional[int] = None, out_dtype: Optional[str] = None,
@@ -75,7 +87,8 @@ class Problem:
                    d_rope=case.d_rope, idx_heads=case.idx_heads, idx_dim=case.idx_dim,
                    topk=case.topk if topk is None else topk, softmax_scale=case.softmax_scale,
                    q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, idx_dtype=case.idx_dtype,
-                   gate_dtype=case.gate_dtype, out_dtype=out_dtype or case.out_dtype)
+                   gate_dtype=case.gate_dtype, out_dtype=out_dtype or case.out_dtype,
+                   page_size=case.page_size, block_table=case.block_table)
 
     @classmethod
     def for_cache(cls, *, num_kv_rows, d_latent, d_rope, idx_dim, kv_dtype, idx_dtype,

@@ -46,7 +46,7 @@ class SgaProblem(ctypes.Structure):
         ("num_seqs", ctypes.c_int32),
         ("num_q", ctypes.c_int32),
         ("max_kv_len", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
         ("num_kv_rows", ctypes.c_int64),
         ("heads", ctypes.c_int32),
         ("d_latent", ctypes.c_int32),
@@ -64,6 +64,9 @@ class SgaProblem(ctypes.Structure):
         ("q_pos", ctypes.c_void_p),
         ("kv_start", ctypes.c_void_p),
         ("kv_len", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
     ]
 
 

@@ -50,8 +50,18 @@ sga_status check_common(const sga_problem *p) {
   if (p->topk < 1) return fail(SGA_ERR_INVALID_ARGUMENT, "topk must be >= 1 (got %d)", p->topk);
   if (p->num_q > 0 && (!p->q_seq || !p->q_pos))
     return fail(SGA_ERR_INVALID_ARGUMENT, "q_seq / q_pos is NULL");
-  if (p->num_seqs > 0 && (!p->kv_start || !p->kv_len))
+  if (p->num_seqs > 0 && (!p->kv_len || (p->page_size == 0 && !p->kv_start)))
     return fail(SGA_ERR_INVALID_ARGUMENT, "kv_start / kv_len is NULL");
+  if (p->page_size != 0) {
+    if (p->page_size < 64 || p->page_size > 65536 || (p->page_size & (p->page_size - 1)))
+      return fail(SGA_ERR_INVALID_ARGUMENT, "page_size must be 0 or a power of two in [64, 65536] (got %d)",
+                  p->page_size);
+    if (p->max_pages < 1) return fail(SGA_ERR_INVALID_ARGUMENT, "max_pages must be >= 1 with pages");
+    if (p->num_seqs > 0 && !p->block_table)
+      return fail(SGA_ERR_INVALID_ARGUMENT, "block_table is NULL with page_size %d", p->page_size);
+  } else if (p->max_pages != 0 || p->block_table) {
+    return fail(SGA_ERR_INVALID_ARGUMENT, "block_table / max_pages given without page_size");
+  }
   if (!dtype_ok(p->q_dtype) || !dtype_ok(p->kv_dtype) || !dtype_ok(p->idx_dtype) ||
       !dtype_ok(p->gate_dtype) || !dtype_ok(p->out_dtype))
     return fail(SGA_ERR_INVALID_ARGUMENT, "unknown dtype code");
@@ -155,6 +165,9 @@ SeqMeta meta_of(const sga_problem *p) {
   m.num_seqs = p->num_seqs;
   m.max_kv_len = p->max_kv_len;
   m.num_kv_rows = p->num_kv_rows;
+  m.block_table = p->page_size ? p->block_table : nullptr;
+  m.page_shift = p->page_size ? __builtin_ctz((unsigned)p->page_size) : 0;
+  m.max_pages = p->page_size ? p->max_pages : 0;
   return m;
 }
 

@@ -50,24 +50,37 @@ struct SeqMeta {
   int32_t num_seqs;
   int32_t max_kv_len;
   int64_t num_kv_rows;
+  // paged layout (page_shift > 0): position s of sequence b is row
+  // block_table[b * max_pages + (s >> page_shift)] << page_shift | s & mask
+  const int32_t *block_table;
+  int32_t page_shift;  // 0: contiguous rows from kv_start
+  int32_t max_pages;
 };
 
-// Cached length of sequence b clipped to the buffers (0 for a bad b).
+// Cached length of sequence b clipped to the buffers (0 for a bad b). In the
+// contiguous layout *start is its first row; in the paged layout it is 0.
 __device__ __forceinline__ int32_t seq_len_clipped(const SeqMeta &m, int32_t b, int64_t *start) {
   if (b < 0 || b >= m.num_seqs) {
     *start = 0;
     return 0;
   }
-  int64_t s = m.kv_start[b];
   int64_t len = m.kv_len[b];
-  if (s < 0 || s > m.num_kv_rows) {
+  if (m.page_shift) {
     *start = 0;
-    return 0;
+    if ((m.num_kv_rows >> m.page_shift) == 0) return 0;
+    const int64_t cap = (int64_t)m.max_pages << m.page_shift;
+    if (len > cap) len = cap;
+  } else {
+    const int64_t s = m.kv_start[b];
+    if (s < 0 || s > m.num_kv_rows) {
+      *start = 0;
+      return 0;
+    }
+    if (len > m.num_kv_rows - s) len = m.num_kv_rows - s;
+    *start = s;
   }
-  if (len > m.num_kv_rows - s) len = m.num_kv_rows - s;
   if (len > m.max_kv_len) len = m.max_kv_len;
   if (len < 0) len = 0;
-  *start = s;
   return (int32_t)len;
 }
 
@@ -79,6 +92,51 @@ __device__ __forceinline__ int32_t query_candidates(const SeqMeta &m, int32_t t,
   if (n < 0) n = 0;
   return (int32_t)n;
 }
+
+// A page id as the kernels use it: ids outside the cache read page 0.
+__device__ __forceinline__ int64_t checked_page(const SeqMeta &m, int32_t pg) {
+  return (pg < 0 || (int64_t)pg >= (m.num_kv_rows >> m.page_shift)) ? 0 : pg;
+}
+
+// Cache row of position s (0 <= s < the clipped length) of sequence b; start
+// comes from seq_len_clipped.
+__device__ __forceinline__ int64_t kv_row(const SeqMeta &m, int32_t b, int64_t start, int32_t s) {
+  if (!m.page_shift) return start + s;
+  const int32_t pg = m.block_table[(int64_t)b * m.max_pages + (s >> m.page_shift)];
+  return (checked_page(m, pg) << m.page_shift) | (s & ((1 << m.page_shift) - 1));
+}
+
+// The pages under a workgroup's key range, for kernels that copy 64-key
+// tiles: lane l of ids[v] holds the checked page id of page first + 64 v + l
+// of sequence b (pages at or past the sequence's last page read as 0). Pages
+// hold at least 64 keys, so a tile that starts at a multiple of 64 lies in
+// one page, and row() of its first key gives the tile's first row.
+template <int kV>
+struct PageWindow {
+  int32_t ids[kV];
+  int32_t first;
+
+  __device__ __forceinline__ void load(const SeqMeta &m, int32_t b, int32_t key0, int32_t n) {
+    first = key0 >> m.page_shift;
+    const int32_t npages = n > 0 ? ((n - 1) >> m.page_shift) + 1 : 0;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const int32_t pg = first + 64 * v + lane;
+      ids[v] = pg < npages ? (int32_t)checked_page(m, m.block_table[(int64_t)b * m.max_pages + pg]) : 0;
+    }
+  }
+  // row of key (wave-uniform), which lies inside the window; keys outside
+  // it read a row of page 0
+  __device__ __forceinline__ int64_t row(const SeqMeta &m, int32_t key) const {
+    const int rel = __builtin_amdgcn_readfirstlane((key >> m.page_shift) - first);
+    int32_t id = 0;
+#pragma unroll
+    for (int v = 0; v < kV; ++v)
+      if ((rel >> 6) == v) id = __builtin_amdgcn_readlane(ids[v], rel & 63);
+    return ((int64_t)id << m.page_shift) | (key & ((1 << m.page_shift) - 1));
+  }
+};
 
 // ---------------------------------------------------------------------------
 // number formats

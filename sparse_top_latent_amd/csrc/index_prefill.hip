@@ -49,7 +49,7 @@ constexpr int kPfQpw = 1;       // queries per wave
 // weighted-ReLU epilogue brings about as much VALU work as there is MFMA work
 // and the two overlap only in part on a SIMD, so latency is hidden by wave
 // count: the register budget is held to 6 waves per SIMD (3 workgroups per CU).
-template <int kQpw, int kGroup, int kChunk, int kBufs>
+template <int kQpw, int kGroup, int kChunk, int kBufs, bool kPaged>
 __global__ __launch_bounds__(kGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta m, int T,
                                                                 const uint8_t *__restrict__ q_idx,
                                                                 const float *__restrict__ w,
@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta 
             [&](int kt) {
               int key = kbase + kt * 16 + c16;
               key = key < n ? key : n - 1;
-              const v4i *src = (const v4i *)(k_idx + (st + key) * 128 + kg * 32);
+              const int64_t row = kPaged ? kv_row(m, m.q_seq[t], st, key) : st + key;
+              const v4i *src = (const v4i *)(k_idx + row * 128 + kg * 32);
               const v4i lo = src[0], hi = src[1];
               return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
             },
@@ -133,17 +134,26 @@ __global__ __launch_bounds__(kGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta 
     return;
   }
   query_candidates(m, t0, &start);  // the group's sequence start
+  // paged caches: the page ids under this workgroup's keys, one per lane
+  PageWindow<(kChunk / kIdxTileKeys + 63) / 64> win;
+  if (kPaged) win.load(m, m.q_seq[t0], c0, nmax);
   // DMA pieces of this thread: piece p = u * kThreads + tid of the 8 KiB tile
   // holds tile row p / 8 and its swizzled 16-byte piece
   auto issue = [&](int i) {
+    const int base = c0 + i * kIdxTileKeys;
+    // paged: the tile's 64 keys lie in one page (wave-uniform row); a key
+    // past the group's last key takes that key's row
+    const int64_t rb = kPaged ? win.row(m, base) : 0;
+    const int64_t rlast = kPaged ? win.row(m, nmax - 1) : 0;
 #pragma unroll
     for (int u = 0; u < kDmaPer; ++u) {
       const int p = u * kThreads + tid;
       if (kThreads > 512 && p >= 512) break;  // wave-uniform: whole waves past the tile
       const int r = p >> 3;
-      int key = c0 + i * kIdxTileKeys + r;
+      int key = base + r;
       key = key < nmax ? key : nmax - 1;
-      const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
+      const int64_t row = kPaged ? (base + r < nmax ? rb + r : rlast) : start + key;
+      const uint8_t *src = k_idx + row * 128 + (((p & 7) ^ key_swz(r)) << 4);
       __builtin_amdgcn_global_load_lds(
           src, (lds_void *)(tiles + (i % kBufs) * kIdxTileBytes + (u * kThreads + wave * 64) * 16),
           16, 0, 0);
@@ -185,20 +195,29 @@ __global__ __launch_bounds__(kGroup / kQpw * 64, 6) void k_index_fp8_pf(SeqMeta 
 
 }  // namespace
 
-hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
-                                    const uint8_t *k_idx, float *scores, int64_t stride,
-                                    hipStream_t s) {
+template <bool kPaged>
+hipError_t launch_pf(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w, const uint8_t *k_idx,
+                     float *scores, int64_t stride, hipStream_t s) {
   if (T < 8 * m.num_seqs) {
     // a few queries per sequence (multi-query decode): groups of 4 rows
     dim3 grid((m.max_kv_len + 2047) / 2048, (T + 3) / 4);
-    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, 4, 2048, 4>), grid, dim3(4 / kPfQpw * 64), 4 * kIdxTileBytes, s,
-                       m, T, q_idx, w, k_idx, scores, stride);
+    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, 4, 2048, 4, kPaged>), grid, dim3(4 / kPfQpw * 64),
+                       4 * kIdxTileBytes, s, m, T, q_idx, w, k_idx, scores, stride);
   } else {
     dim3 grid((m.max_kv_len + 8191) / 8192, (T + kPfGroup - 1) / kPfGroup);
-    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, kPfGroup, 8192, 3>), grid, dim3(kPfGroup / kPfQpw * 64),
-                       3 * kIdxTileBytes, s, m, T, q_idx, w, k_idx, scores, stride);
+    hipLaunchKernelGGL((k_index_fp8_pf<kPfQpw, kPfGroup, 8192, 3, kPaged>), grid,
+                       dim3(kPfGroup / kPfQpw * 64), 3 * kIdxTileBytes, s, m, T, q_idx, w, k_idx, scores,
+                       stride);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_idx, const float *w,
+                                    const uint8_t *k_idx, float *scores, int64_t stride,
+                                    hipStream_t s) {
+  if (m.page_shift)
+    return launch_pf<true>(m, T, q_idx, w, k_idx, scores, stride, s);
+  return launch_pf<false>(m, T, q_idx, w, k_idx, scores, stride, s);
 }
 
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
   __syncthreads();
   const int s = base + threadIdx.x;
   if (s < n) {
-    const float *kr = k_idx + (start + s) * (int64_t)DI;
+    const float *kr = k_idx + kv_row(m, m.q_seq[t], start, s) * (int64_t)DI;
     float acc = 0.0f;
     for (int h = 0; h < HI; ++h) {
       float d = 0.0f;
@@ -131,7 +131,7 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
   }
 }
 
-template <bool kHist, int kR>
+template <bool kHist, int kR, bool kPaged>
 __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, int steps_per_wg,
                                                               const uint8_t *__restrict__ q_idx,
                                                               const float *__restrict__ w,
@@ -154,6 +154,10 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   if (kHist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = n;
   const int c0 = blockIdx.x * steps_per_wg * kIdxStepKeys;
   if (c0 >= n) return;
+  // paged caches: the page ids under this workgroup's keys, one per lane
+  // (requested first, so that waiting for them waits for nothing else)
+  PageWindow<1> win;
+  if (kPaged) win.load(m, m.q_seq[t], c0, n);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform loop bounds
   const int kg = lane >> 4, c16 = lane & 15;
@@ -162,12 +166,18 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   // its swizzled 16-byte piece; rows past the sequence repeat its last key
   // (their scores are dropped)
   auto issue = [&](int i) {
+    const int base = c0 + i * kIdxStepKeys;
+    // paged: the step's 64 keys lie in one page (wave-uniform row); a key
+    // past the sequence takes the row of its last key, as below
+    const int64_t rb = kPaged ? win.row(m, base) : 0;
+    const int64_t rlast = kPaged ? win.row(m, n - 1) : 0;
 #pragma unroll
     for (int u = 0; u < kIdxPieces; ++u) {
       const int p = u * kThreads + tid;
       const int r = p >> 3;
-      const int key = min(c0 + i * kIdxStepKeys + r, n - 1);
-      const uint8_t *src = k_idx + (start + key) * 128 + (((p & 7) ^ key_swz(r)) << 4);
+      const int key = min(base + r, n - 1);
+      const int64_t row = kPaged ? (base + r <= n - 1 ? rb + r : rlast) : start + key;
+      const uint8_t *src = k_idx + row * 128 + (((p & 7) ^ key_swz(r)) << 4);
       __builtin_amdgcn_global_load_lds(
           src, (lds_void *)(ring + (i % kR) * kIdxStepBytes + (u * kThreads + wave * 64) * 16), 16, 0,
           kKeyLoadPolicy);
@@ -316,9 +326,13 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
   if (!attr) {
     // ring plus the largest score stage (64 tiles)
     const int max_smem = kIdxRing * kIdxStepBytes + (kIdxStageScores ? 64 * kIdxTileKeys * 4 : 0);
-    (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing>,
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
-    (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing>,
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
+    (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
     (void)hipGetLastError();
     attr = true;
@@ -341,12 +355,21 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     sel->slot_words = 4 + (per_wg < kHist0Bins ? per_wg : kHist0Bins);
   }
   const size_t smem = (size_t)kIdxRing * kIdxStepBytes + (kIdxStageScores ? (size_t)per_wg * 4 : 0);
-  if (sel)
-    hipLaunchKernelGGL((k_index_fp8<true, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, steps,
-                       q_idx, w, k_idx, scores, stride, *sel);
-  else
-    hipLaunchKernelGGL((k_index_fp8<false, kIdxRing>), grid, dim3(kIdxWaves * 64), smem, s, m, T, steps,
-                       q_idx, w, k_idx, scores, stride, none);
+  const dim3 block(kIdxWaves * 64);
+  if (m.page_shift) {
+    if (sel)
+      hipLaunchKernelGGL((k_index_fp8<true, kIdxRing, true>), grid, block, smem, s, m, T, steps, q_idx, w,
+                         k_idx, scores, stride, *sel);
+    else
+      hipLaunchKernelGGL((k_index_fp8<false, kIdxRing, true>), grid, block, smem, s, m, T, steps, q_idx, w,
+                         k_idx, scores, stride, none);
+  } else if (sel) {
+    hipLaunchKernelGGL((k_index_fp8<true, kIdxRing, false>), grid, block, smem, s, m, T, steps, q_idx, w,
+                       k_idx, scores, stride, *sel);
+  } else {
+    hipLaunchKernelGGL((k_index_fp8<false, kIdxRing, false>), grid, block, smem, s, m, T, steps, q_idx, w,
+                       k_idx, scores, stride, none);
+  }
   return hipGetLastError();
 }
 

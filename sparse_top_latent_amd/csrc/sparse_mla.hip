@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kF32Block) void k_mla_f32(MlaArgs a) {
   for (int r = threadIdx.x; r < a.k; r += kF32Block) {
     int32_t pos = a.topk_idx[(size_t)t * a.k + r];
     bool ok = pos >= 0 && pos < L;
-    int64_t row = ok ? start + pos : -1;
+    int64_t row = ok ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
     float lg = -INFINITY;
     if (ok) {
       const float *kr = kv + row * D;
@@ -241,7 +241,8 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     const int my_row = min(tid, R * kMlaRowsPerSplit - 1);
     int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(my_row, nrows - 1)];
     const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
-    if (tid < R * kMlaRowsPerSplit) rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? (int32_t)(start + pos) : -1;
+    if (tid < R * kMlaRowsPerSplit)
+      rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
   } else {
     // The top-k's last step, done here for the workgroup's own output slots
     // [r0, r0 + nrows) of the query (every split workgroup of the query
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
     if (tid < R * kMlaRowsPerSplit) {
       const int32_t pos = (n <= a.k && tid < nrows && r0 + tid < n) ? r0 + tid : -1;
-      rows[tid] = (pos >= 0 && pos < L) ? (int32_t)(start + pos) : -1;
+      rows[tid] = (pos >= 0 && pos < L) ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
       if (n <= a.k && a.topk_out && tid < nrows) a.topk_out[(size_t)t * a.k + r0 + tid] = pos;
     }
     if (n > a.k) {  // uniform over the workgroup
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
       finish_query<512>(a.k, a.sel, t, fh, fh + 2 * kHist12Bins, (int *)(fh + 2 * kHist12Bins + 8),
                         [&](uint32_t o, int32_t p) {
                           if (o >= (uint32_t)r0 && o < (uint32_t)(r0 + nrows)) {
-                            rows[o - r0] = (p >= 0 && p < L) ? (int32_t)(start + p) : -1;
+                            rows[o - r0] =
+                                (p >= 0 && p < L) ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, p) : -1;
                             if (a.topk_out) a.topk_out[(size_t)t * a.k + o] = p;
                           }
                         });

@@ -30,7 +30,7 @@ def test_header_and_exports_agree(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sga_abi_version() == 1
+    assert lib.sga_abi_version() == 2
     for code in range(6):
         assert lib.sga_status_string(code)
     assert lib.sga_status_string(99) == b"unknown status"
@@ -40,10 +40,11 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 
 def _problem(**kw):
-    base = dict(num_seqs=16, num_q=16, max_kv_len=131072, reserved0=0, num_kv_rows=16 * 131072,
+    base = dict(num_seqs=16, num_q=16, max_kv_len=131072, page_size=0, num_kv_rows=16 * 131072,
                 heads=64, d_latent=512, d_rope=64, idx_heads=64, idx_dim=128, topk=2048,
                 softmax_scale=1 / 24, q_dtype=1, kv_dtype=1, idx_dtype=2, gate_dtype=1,
-                out_dtype=1, q_seq=FAKE, q_pos=FAKE, kv_start=FAKE, kv_len=FAKE)
+                out_dtype=1, q_seq=FAKE, q_pos=FAKE, kv_start=FAKE, kv_len=FAKE, block_table=None,
+                max_pages=0, reserved0=0)
     base.update(kw)
     return _ffi.SgaProblem(**base)
 
@@ -96,6 +97,13 @@ def test_workspace_sizes(lib):
     (dict(q_dtype=0), 2),
     (dict(out_dtype=2), 2),
     (dict(softmax_scale=float("nan")), 1),
+    (dict(page_size=32, block_table=FAKE, max_pages=4), 1),      # pages below 64 rows
+    (dict(page_size=96, block_table=FAKE, max_pages=4), 1),      # not a power of two
+    (dict(page_size=1 << 17, block_table=FAKE, max_pages=4), 1),
+    (dict(page_size=64, block_table=None, max_pages=4), 1),      # no block table
+    (dict(page_size=64, block_table=FAKE, max_pages=0), 1),
+    (dict(block_table=FAKE, max_pages=4), 1),                    # a table without pages
+    (dict(kv_start=None), 1),                                    # contiguous needs kv_start
 ])
 def test_invalid_problems(lib, kw, status):
     p = _problem(**kw)
@@ -105,6 +113,12 @@ def test_invalid_problems(lib, kw, status):
     st = lib.sga_layer_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
                            None, FAKE, 1 << 40, None)
     assert st == status
+
+
+def test_paged_problem_is_valid_without_kv_start(lib):
+    p = _problem(page_size=64, block_table=FAKE, max_pages=2048, kv_start=None)
+    st, n = _ws(lib, p, _ffi.SGA_OP_LAYER)
+    assert st == 0 and n > 0, lib.sga_last_error()
 
 
 def test_null_problem_and_null_buffers(lib):

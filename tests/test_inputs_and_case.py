@@ -78,3 +78,22 @@ def test_case_glue_matches_direct_oracle_call():
     ref = sga.sga_forward(**d, topk=16, tau=c.softmax_scale, d_latent=32)
     assert np.array_equal(res["topk_idx"], ref["topk_idx"])
     assert np.max(np.abs(res["y"] - ref["y"])) == 0.0
+
+
+def test_paged_copy_keeps_every_logical_row_and_the_oracle_agrees():
+    from oracle import case as ocase
+    from sga_inputs import make_case, paged_copy
+
+    c = make_case("tiny_fp32_L512")
+    for P in (64, 128):
+        p = paged_copy(c, P, seed=P)
+        table = p.block_table.numpy()
+        assert table.shape == (1, 512 // P)
+        assert sorted(table[0].tolist()) == sorted(set(table[0].tolist()))  # distinct pages
+        assert p.num_kv_rows == (512 // P + 3) * P
+        rows = ocase.cache_rows(p, 0, np.arange(512), None, table)
+        assert torch.equal(p.kv[torch.as_tensor(rows)], c.kv)
+        assert torch.equal(p.k_idx[torch.as_tensor(rows)], c.k_idx)
+        ref, got = ocase.run_queries(c, [0, 100, 511]), ocase.run_queries(p, [0, 100, 511])
+        assert np.array_equal(ref["topk_idx"], got["topk_idx"])
+        assert np.array_equal(ref["y"], got["y"])
