@@ -218,7 +218,14 @@ __device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int 
   }
 }
 
-template <bool kMx, int R, bool kFuse>
+// the cache row of position pos of the query's sequence (paged: through the
+// block table)
+template <bool kPaged>
+__device__ __forceinline__ int32_t split_row(const MlaArgs &a, int t, int64_t start, int32_t pos) {
+  return kPaged ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : (int32_t)(start + pos);
+}
+
+template <bool kMx, int R, bool kFuse, bool kPaged>
 __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
                                                     float2 *__restrict__ ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(my_row, nrows - 1)];
     const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
     if (tid < R * kMlaRowsPerSplit)
-      rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
+      rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? split_row<kPaged>(a, t, start, pos) : -1;
   } else {
     // The top-k's last step, done here for the workgroup's own output slots
     // [r0, r0 + nrows) of the query (every split workgroup of the query
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
     if (tid < R * kMlaRowsPerSplit) {
       const int32_t pos = (n <= a.k && tid < nrows && r0 + tid < n) ? r0 + tid : -1;
-      rows[tid] = (pos >= 0 && pos < L) ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
+      rows[tid] = (pos >= 0 && pos < L) ? split_row<kPaged>(a, t, start, pos) : -1;
       if (n <= a.k && a.topk_out && tid < nrows) a.topk_out[(size_t)t * a.k + r0 + tid] = pos;
     }
     if (n > a.k) {  // uniform over the workgroup
@@ -263,8 +270,7 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
       finish_query<512>(a.k, a.sel, t, fh, fh + 2 * kHist12Bins, (int *)(fh + 2 * kHist12Bins + 8),
                         [&](uint32_t o, int32_t p) {
                           if (o >= (uint32_t)r0 && o < (uint32_t)(r0 + nrows)) {
-                            rows[o - r0] =
-                                (p >= 0 && p < L) ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, p) : -1;
+                            rows[o - r0] = (p >= 0 && p < L) ? split_row<kPaged>(a, t, start, p) : -1;
                             if (a.topk_out) a.topk_out[(size_t)t * a.k + o] = p;
                           }
                         });
@@ -652,27 +658,35 @@ bool mla_fuse_finish(int T, int k) {
   return (int64_t)T * S <= cus;
 }
 
-template <bool kMx, int R, bool kFuse>
+template <bool kMx, int R, bool kFuse, bool kPaged>
 static void launch_split8(const MlaArgs &a, uint16_t *opart, float2 *ml, int S, hipStream_t s) {
   static bool attr = false;
   const size_t smem = kMx ? kMx8Smem : kBfSmem;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void *)k_mla_split8<kMx, R, kFuse>,
+    (void)hipFuncSetAttribute((const void *)k_mla_split8<kMx, R, kFuse, kPaged>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     (void)hipGetLastError();
     attr = true;
   }
-  hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse>), dim3(S, a.T), dim3(512), smem, s, a, opart, ml);
+  hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse, kPaged>), dim3(S, a.T), dim3(512), smem, s, a, opart, ml);
+}
+
+template <bool kMx, bool kFuse, bool kPaged>
+static void launch_split8_rp(const MlaArgs &a, uint16_t *opart, float2 *ml, int R, int S, hipStream_t s) {
+  if (R == 4)
+    launch_split8<kMx, 4, kFuse, kPaged>(a, opart, ml, S, s);
+  else if (R == 2)
+    launch_split8<kMx, 2, kFuse, kPaged>(a, opart, ml, S, s);
+  else
+    launch_split8<kMx, 1, kFuse, kPaged>(a, opart, ml, S, s);
 }
 
 template <bool kMx, bool kFuse>
 static void launch_split8_r(const MlaArgs &a, uint16_t *opart, float2 *ml, int R, int S, hipStream_t s) {
-  if (R == 4)
-    launch_split8<kMx, 4, kFuse>(a, opart, ml, S, s);
-  else if (R == 2)
-    launch_split8<kMx, 2, kFuse>(a, opart, ml, S, s);
+  if (a.meta.page_shift)
+    launch_split8_rp<kMx, kFuse, true>(a, opart, ml, R, S, s);
   else
-    launch_split8<kMx, 1, kFuse>(a, opart, ml, S, s);
+    launch_split8_rp<kMx, kFuse, false>(a, opart, ml, R, S, s);
 }
 
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
