@@ -11,6 +11,7 @@ Modules:
            quantised into caller-chosen cache rows)
   sga      the four steps (index scores, top-k, sparse MLA, gate), the whole
            path, and a dense causal MLA reference
+  kl       the indexer's KL loss over the sparse selection and its gradients
   case     glue that decodes a generated case (sga_inputs.SgaCase) for `sga`
 
 Parity status: every function is pinned by tests that do not reuse it
@@ -20,4 +21,4 @@ of ReLU inside the indexer is a reading of the pages (they print no
 formula): that single modelling choice is "parity unpinned" by the pages.
 """
 
-from . import formats, quant, sga  # noqa: F401
+from . import formats, kl, quant, sga  # noqa: F401

@@ -119,3 +119,52 @@ def decode_all(case) -> Dict[str, np.ndarray]:
         "kv_start": raw(case.kv_start).astype(np.int64),
         "kv_len": raw(case.kv_len).astype(np.int64),
     }
+
+
+def kl_queries(case, queries: Optional[Iterable[int]] = None) -> Dict[str, object]:
+    """The indexer KL loss and its gradients (oracle.kl) for the listed queries.
+
+    Every query's selection, attention probabilities and scores come from the
+    oracle itself (run as in run_queries). Returns loss [Q], dw [Q, HI],
+    dq_idx [Q, HI, DI] and d_k_idx as {cache row: [DI]} summed over the
+    listed queries.
+    """
+    import torch
+
+    from . import kl
+
+    T = case.num_q
+    qs = list(range(T)) if queries is None else [int(t) for t in queries]
+    q_seq = raw(case.q_seq).astype(np.int64)
+    q_pos = raw(case.q_pos).astype(np.int64)
+    kv_start = raw(case.kv_start).astype(np.int64)
+    kv_len = raw(case.kv_len).astype(np.int64)
+    table = raw(case.block_table).astype(np.int64) if case.page_size else None
+    idx_dt = "fp8" if case.idx_dtype == "fp8" else "f32"
+    HI, DI, Dc = case.idx_heads, case.idx_dim, case.d_latent
+    loss = np.zeros(len(qs))
+    dw = np.zeros((len(qs), HI))
+    dq = np.zeros((len(qs), HI, DI))
+    dk: Dict[int, np.ndarray] = {}
+    for i, t in enumerate(qs):
+        b = int(q_seq[t])
+        n = sga.visible_count(q_pos[t], seq_capacity(case, b, kv_len))
+        q_idx_t = _dec(case.q_idx[t], idx_dt)
+        w_t = raw(case.w[t]).astype(np.float64)
+        key_rows = cache_rows(case, b, np.arange(n), kv_start, table)
+        keys = _dec(case.k_idx.index_select(0, torch.as_tensor(key_rows, device=case.k_idx.device)),
+                    idx_dt)
+        s64 = sga.index_scores(q_idx_t, w_t, keys)
+        sel = sga.select_topk(sga.to_fp32(s64), case.topk)
+        chosen = sel[sel >= 0]
+        rows_idx = torch.as_tensor(key_rows[chosen], dtype=torch.int64, device=case.kv.device)
+        kv_rows = case.kv.index_select(0, rows_idx)
+        rows = (_dec(kv_rows, "mxfp8", case.kv_scale.index_select(0, rows_idx))
+                if case.kv_dtype == "mxfp8" else _dec(kv_rows, case.kv_dtype))
+        _, _, p = sga.attend(_dec(case.q[t], case.q_dtype), rows, case.softmax_scale, Dc)
+        target = kl.attention_target(p)
+        loss[i], g = kl.indexer_kl(s64[chosen], target)
+        dw[i], dq[i], dk_rows = kl.indexer_backward(q_idx_t, w_t, keys[chosen], g)
+        for r, v in zip(key_rows[chosen].tolist(), dk_rows):
+            dk[r] = dk.get(r, 0.0) + v
+    return {"loss": loss, "dw": dw, "dq_idx": dq, "dk_idx": dk, "queries": np.array(qs, dtype=np.int64)}

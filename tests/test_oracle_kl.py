@@ -1,0 +1,117 @@
+"""Pins for the oracle's indexer KL loss and gradients (CPU only).
+
+The loss is checked against torch's kl_div on log_softmax (a library
+routine); every gradient against central finite differences of the oracle's
+own loss, which does not share the closed forms; plus the invariants of a
+KL divergence.
+"""
+
+import numpy as np
+import torch
+
+from oracle import kl
+
+
+def _loss_of(I, target):
+    return kl.indexer_kl(I, target)[0]
+
+
+def test_loss_matches_torch_kl_div():
+    g = np.random.default_rng(0)
+    for m in (1, 5, 300):
+        I = g.standard_normal(m) * 3
+        p = g.random((4, m))
+        p /= p.sum(axis=1, keepdims=True)
+        t = kl.attention_target(p)
+        ref = torch.nn.functional.kl_div(torch.log_softmax(torch.tensor(I), 0), torch.tensor(t),
+                                         reduction="sum").item()
+        assert abs(_loss_of(I, t) - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_gradient_wrt_scores_by_finite_differences():
+    g = np.random.default_rng(1)
+    I = g.standard_normal(40) * 2
+    t = g.random(40)
+    t[3] = 0.0  # a zero-target term
+    t /= t.sum()
+    _, grad = kl.indexer_kl(I, t)
+    h = 1e-6
+    for s in range(40):
+        e = np.zeros(40)
+        e[s] = h
+        fd = (_loss_of(I + e, t) - _loss_of(I - e, t)) / (2 * h)
+        assert abs(fd - grad[s]) < 1e-7
+
+
+def test_kl_invariants():
+    g = np.random.default_rng(2)
+    t = g.random(50)
+    t /= t.sum()
+    for _ in range(5):
+        I = g.standard_normal(50) * 4
+        loss, grad = kl.indexer_kl(I, t)
+        assert loss >= 0 and abs(grad.sum()) < 1e-12
+    loss, grad = kl.indexer_kl(np.log(t) + 7.25, t)  # the indexer already matches the target
+    assert abs(loss) < 1e-12 and np.abs(grad).max() < 1e-12
+    assert kl.indexer_kl(np.zeros(0), np.zeros(0))[0] == 0.0
+
+
+def test_attention_target():
+    g = np.random.default_rng(3)
+    p = g.random((8, 30))
+    p /= p.sum(axis=1, keepdims=True)
+    t = kl.attention_target(p)
+    assert abs(t.sum() - 1) < 1e-12
+    assert np.allclose(kl.attention_target(p[:1]), p[0])
+    assert np.allclose(t, p.mean(axis=0))
+
+
+def test_indexer_gradients_by_finite_differences():
+    g = np.random.default_rng(4)
+    HI, DI, m = 3, 5, 7
+    q = g.standard_normal((HI, DI))
+    w = g.standard_normal(HI)
+    k = g.standard_normal((m, DI))
+    t = g.random(m)
+    t /= t.sum()
+
+    def loss(q, w, k):
+        z = q @ k.T
+        return _loss_of(np.maximum(z, 0).T @ w, t)
+
+    z = q @ k.T
+    assert np.abs(z).min() > 1e-3  # no ReLU kink within the step
+    I = np.maximum(z, 0).T @ w
+    _, gI = kl.indexer_kl(I, t)
+    dw, dq, dk = kl.indexer_backward(q, w, k, gI)
+    h = 1e-7
+    for arr, grad in ((w, dw), (q, dq), (k, dk)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            up = loss(q, w, k)
+            arr[idx] = old - h
+            dn = loss(q, w, k)
+            arr[idx] = old
+            assert abs((up - dn) / (2 * h) - grad[idx]) < 1e-6, (idx, grad[idx])
+
+
+def test_case_level_kl_on_the_tiny_case():
+    # the case glue against the step functions run by hand on one query
+    from oracle import case as ocase
+    from oracle import sga
+    from sga_inputs import make_case
+
+    c = make_case("tiny_fp32_L512")
+    r = ocase.kl_queries(c, [300, 511])
+    assert r["loss"].shape == (2,) and np.all(r["loss"] >= 0)
+    t = 511
+    d = ocase.decode_all(c)
+    s = sga.index_scores(d["q_idx"][t], d["w"][t], d["k_idx"][:512])
+    sel = sga.select_topk(sga.to_fp32(s), c.topk)
+    _, _, p = sga.attend(d["q"][t], d["kv"][sel], c.softmax_scale, c.d_latent)
+    loss, g = kl.indexer_kl(s[sel], kl.attention_target(p))
+    dw, dq, _ = kl.indexer_backward(d["q_idx"][t], d["w"][t], d["k_idx"][sel], g)
+    assert abs(r["loss"][1] - loss) < 1e-12 and np.allclose(r["dw"][1], dw) and np.allclose(r["dq_idx"][1], dq)
+    # rows selected by both queries collect both contributions
+    assert len(r["dk_idx"]) >= c.topk
