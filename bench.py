@@ -310,6 +310,79 @@ def cache_append_bench(args, torch, sga):
     }), flush=True)
 
 
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+
+
+def indexer_kl_flops(case, k):
+    """FLOPs of one sga_indexer_kl call: per selected (query, row) the attention
+    logits of every head (2 H D), the indexer scores twice (forward and again
+    in the backward, 2 x 2 HI DI) and the three gradient products (3 x 2 HI DI)."""
+    D, H, HI, DI = case.d_qk, case.heads, case.idx_heads, case.idx_dim
+    return case.num_q * k * (2.0 * H * D + 10.0 * HI * DI)
+
+
+def indexer_kl_bench(args, case, prob, sga, torch):
+    """The indexer KL loss and gradients alone (training side), after one forward."""
+    dev = case.q.device
+    T, H, HI, DI = case.num_q, case.heads, case.idx_heads, case.idx_dim
+    out = torch.empty((T, H, case.d_latent), dtype=sga.out_torch_dtype(prob.c.out_dtype), device=dev)
+    idx = torch.empty((T, case.topk), dtype=torch.int32, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = sga.workspace(prob, sga.SGA_OP_LAYER, device=dev)
+    sga.sga_layer_fwd(prob, case.q_idx, case.w, case.k_idx, case.q, case.kv, case.kv_scale, case.gate,
+                      out, idx, lse, ws)
+    loss = torch.empty((T,), device=dev)
+    d_w = torch.empty((T, HI), device=dev)
+    d_q = torch.empty((T, HI, DI), device=dev)
+    d_k = torch.zeros((case.num_kv_rows, DI), device=dev)
+    kws = sga.workspace(prob, sga.SGA_OP_INDEXER_KL, device=dev)
+
+    def step():
+        sga.sga_indexer_kl(prob, case.q_idx, case.w, case.k_idx, case.q, case.kv, case.kv_scale, idx, lse,
+                           loss, d_w, d_q, d_k, kws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = indexer_kl_flops(case, case.topk)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] indexer KL {case.name}: {ms * 1e3:.1f} us per call, {tflops:.1f} TFLOP/s "
+        f"({tflops / FP32_PEAK_TFLOPS:.1%} of the fp32 vector peak)")
+    base = None
+    if not args.no_cpu_baseline:
+        from oracle import case as ocase
+
+        t1 = time.perf_counter()
+        n = 0
+        while n < T and time.perf_counter() - t1 < 15.0:
+            ocase.kl_queries(case, [n])
+            n += 1
+        base = {"value": round(n / (time.perf_counter() - t1), 3), "unit": "queries/s", "cores": blas_threads(),
+                "kind": "oracle", "sample": f"the first {n} queries of the workload (float64, whole KL and gradients)"}
+    print(json.dumps({
+        "metric": "SGA indexer KL loss + gradients, queries/s (training side)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": case.name, "queries": T, "topk": case.topk, "heads": H, "idx_heads": HI,
+                   "idx_dim": DI},
+        "roofline": {"bound": "alu", "kernel": "indexer KL (4 kernels, per call)", "achieved": round(tflops, 2),
+                     "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+                     "flops_per_launch": flops, "traffic": None},
+        "cpu_baseline": base,
+    }), flush=True)
+
+
 def cpu_baseline_append(src, D, DI, budget_s=10.0):
     """The oracle's cache append timed on host cores over a bounded sample of
     the same new tokens (as many leading tokens as fit the time budget)."""
@@ -348,6 +421,8 @@ def main():
     ap.add_argument("--cache-append", action="store_true",
                     help="time only sga_cache_append of --append-tokens new tokens (bf16 -> MXFP8 + FP8)")
     ap.add_argument("--append-tokens", type=int, default=131072)
+    ap.add_argument("--indexer-kl", action="store_true",
+                    help="time only sga_indexer_kl (loss and gradients) after one forward of --workload")
     ap.add_argument("--page-size", type=int, default=0,
                     help="lay the caches out in pages of this many rows (seeded random page order, "
                          "block table) instead of contiguous rows")
@@ -380,6 +455,8 @@ def main():
     T, H, Dc = case.num_q, case.heads, case.d_latent
     if args.indexer_only:
         return indexer_only(args, case, prob, sga, torch)
+    if args.indexer_kl:
+        return indexer_kl_bench(args, case, prob, sga, torch)
     out = torch.empty((T, H, Dc), dtype=sga.out_torch_dtype(prob.c.out_dtype), device=dev)
     ws = sga.workspace(prob, sga.SGA_OP_LAYER, device=dev)
     # independent cache copies, rotated per step (defeats the 256 MB MALL)

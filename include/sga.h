@@ -84,7 +84,8 @@ typedef enum sga_op {
   SGA_OP_INDEX = 0, /* sga_index_scores   */
   SGA_OP_TOPK = 1,  /* sga_topk_select    */
   SGA_OP_MLA = 2,   /* sga_sparse_mla_fwd */
-  SGA_OP_LAYER = 3  /* sga_layer_fwd      */
+  SGA_OP_LAYER = 3, /* sga_layer_fwd      */
+  SGA_OP_INDEXER_KL = 4 /* sga_indexer_kl */
 } sga_op;
 
 /* Shapes, dtypes and sequence metadata of one call. */
@@ -243,6 +244,37 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
 sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dtype,
                             const void *kv_new, const void *k_idx_new, const int64_t *slots,
                             void *kv, uint8_t *kv_scale, void *k_idx, void *stream);
+
+/*
+ * Indexer KL loss and its gradients, the training side of the indexer ("A.X
+ * K2 Technical Report" section 3.4: the indexer is trained with a KL loss
+ * that aligns its scores with the attention distribution, over the sparse
+ * top-k selection from the start; "A.X-K2: a sparse-attention upgrade that
+ * costs nothing, trained natively in FP8", section "Sparse Gated
+ * Attention"). For query t with the selected positions S_t of a forward pass:
+ *   target_s = sum_h exp(tau q[t,h] . kv[s] - lse[t,h]), normalised over S_t
+ *   I_s      = sum_h w[t,h] max(0, q_idx[t,h] . k_idx[s])
+ *   loss[t]  = sum_s target_s (log target_s - log softmax_S(I)_s)
+ *   g_s      = softmax_S(I)_s - target_s          (the target is a constant)
+ *   d_w[t,h] = sum_s g_s max(0, z_hs);  d_q_idx[t,h] = sum_s g_s w[t,h] [z_hs > 0] k_idx[s]
+ *   d_k_idx[s] += sum_h g_s w[t,h] [z_hs > 0] q_idx[t,h]   (z_hs = q_idx[t,h] . k_idx[s])
+ * Arguments: q_idx, w, k_idx, q, kv, kv_scale as in sga_layer_fwd; topk_idx
+ * [T, topk] and lse [T, H] are that forward's outputs (topk_idx_out, lse);
+ * outputs loss [T], d_w [T, HI], d_q_idx [T, HI, DI] (fp32, written) and
+ * d_k_idx [num_kv_rows, DI] (fp32, ADDED to: the caller clears it; the
+ * order of the additions is not fixed). Queries without candidates give
+ * loss 0 and zero gradients.
+ * Shapes: H, HI <= 64, HI * DI <= 8192, Dc + Dr and DI multiples of 8, topk
+ * <= 4096, q in LDS (H * (Dc + Dr) bf16 or fp32) within 96 KiB; q SGA_F32 or
+ * SGA_BF16, kv SGA_F32, SGA_BF16 or SGA_MXFP8_E4M3FN, index SGA_F32 or
+ * SGA_FP8_E4M3FN. Arithmetic: fp32 on the vector ALUs. Workspace:
+ * sga_workspace_size(p, SGA_OP_INDEXER_KL).
+ */
+sga_status sga_indexer_kl(const sga_problem *p, const void *q_idx, const float *w,
+                          const void *k_idx, const void *q, const void *kv,
+                          const uint8_t *kv_scale, const int32_t *topk_idx, const float *lse,
+                          float *loss, float *d_w, float *d_q_idx, float *d_k_idx, void *ws,
+                          size_t ws_bytes, void *stream);
 
 /*
  * Phase timing of sga_layer_fwd, for measurement. While enabled, each

@@ -21,6 +21,7 @@ from ._ffi import (  # noqa: F401
     SGA_FP8_E4M3FN,
     SGA_MXFP8_E4M3FN,
     SGA_OP_INDEX,
+    SGA_OP_INDEXER_KL,
     SGA_OP_LAYER,
     SGA_OP_MLA,
     SGA_OP_TOPK,
@@ -234,6 +235,32 @@ def sga_cache_append(prob: Problem, kv_new, k_idx_new, slots, kv, kv_scale, k_id
              c.num_kv_rows * (D // 32) if kv_scale is not None else None),
         _ptr(k_idx, "k_idx", (c.idx_dtype,), c.num_kv_rows * DI if k_idx_new is not None else None),
         _stream(stream)))
+
+
+def sga_indexer_kl(prob: Problem, q_idx, w, k_idx, q, kv, kv_scale, topk_idx, lse, loss, d_w,
+                   d_q_idx, d_k_idx, ws, stream=None) -> None:
+    """Indexer KL loss and gradients (see sga_indexer_kl in sga.h); d_k_idx is added to."""
+    c = prob.c
+    T, H, HI, DI, D = c.num_q, c.heads, c.idx_heads, c.idx_dim, c.d_latent + c.d_rope
+    for name, t in (("topk_idx", topk_idx),):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    _ffi.check(lib().sga_indexer_kl(
+        prob.ptr,
+        _ptr(q_idx, "q_idx", (c.idx_dtype,), T * HI * DI),
+        _ptr(w, "w", (SGA_F32,), T * HI),
+        _ptr(k_idx, "k_idx", (c.idx_dtype,), c.num_kv_rows * DI),
+        _ptr(q, "q", (c.q_dtype,), T * H * D),
+        _ptr(kv, "kv", (c.kv_dtype,), c.num_kv_rows * D),
+        _ptr(kv_scale, "kv_scale", (SGA_FP8_E4M3FN,),
+             c.num_kv_rows * (D // 32) if kv_scale is not None else None),
+        _ptr(topk_idx, "topk_idx", None, T * c.topk),
+        _ptr(lse, "lse", (SGA_F32,), T * H),
+        _ptr(loss, "loss", (SGA_F32,), T),
+        _ptr(d_w, "d_w", (SGA_F32,), T * HI),
+        _ptr(d_q_idx, "d_q_idx", (SGA_F32,), T * HI * DI),
+        _ptr(d_k_idx, "d_k_idx", (SGA_F32,), c.num_kv_rows * DI),
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def sga_profile_enable(max_calls: int) -> None:

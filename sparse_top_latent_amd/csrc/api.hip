@@ -115,6 +115,29 @@ sga_status check_mla(const sga_problem *p, Plan *plan) {
               p->kv_dtype);
 }
 
+sga_status check_kl(const sga_problem *p) {
+  if (p->heads < 1 || p->heads > 64 || p->idx_heads < 1 || p->idx_heads > 64 || p->idx_dim < 8 ||
+      p->idx_heads * p->idx_dim > 8192)
+    return fail(SGA_ERR_UNSUPPORTED, "indexer KL needs heads, idx_heads <= 64 and idx_heads*idx_dim <= 8192");
+  const int D = p->d_latent + p->d_rope;
+  if (p->d_latent < 1 || p->d_rope < 0 || D % 8 || p->idx_dim % 8)
+    return fail(SGA_ERR_UNSUPPORTED, "indexer KL needs d_latent + d_rope and idx_dim multiples of 8");
+  if (p->topk > 4096) return fail(SGA_ERR_UNSUPPORTED, "indexer KL supports topk <= 4096");
+  if (!(p->softmax_scale == p->softmax_scale) || p->softmax_scale > 3.0e38f || p->softmax_scale < -3.0e38f)
+    return fail(SGA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (p->q_dtype != SGA_F32 && p->q_dtype != SGA_BF16)
+    return fail(SGA_ERR_UNSUPPORTED, "indexer KL: q must be SGA_F32 or SGA_BF16");
+  if (p->kv_dtype != SGA_F32 && p->kv_dtype != SGA_BF16 && p->kv_dtype != SGA_MXFP8_E4M3FN)
+    return fail(SGA_ERR_UNSUPPORTED, "indexer KL: kv must be SGA_F32, SGA_BF16 or SGA_MXFP8_E4M3FN");
+  if (p->kv_dtype == SGA_MXFP8_E4M3FN && D % 32)
+    return fail(SGA_ERR_UNSUPPORTED, "MXFP8 rows need a multiple of 32 values");
+  if (p->idx_dtype != SGA_F32 && p->idx_dtype != SGA_FP8_E4M3FN)
+    return fail(SGA_ERR_UNSUPPORTED, "indexer KL: index tensors must be SGA_F32 or SGA_FP8_E4M3FN");
+  if ((int64_t)p->heads * D * (p->q_dtype == SGA_BF16 ? 2 : 4) > 96 * 1024)
+    return fail(SGA_ERR_UNSUPPORTED, "indexer KL: q of one query must fit 96 KiB");
+  return SGA_OK;
+}
+
 int64_t score_stride(const sga_problem *p) { return ((int64_t)p->max_kv_len + 63) / 64 * 64; }
 
 sga_status plan_for(const sga_problem *p, int op, Plan *plan) {
@@ -131,6 +154,8 @@ sga_status plan_for(const sga_problem *p, int op, Plan *plan) {
       st = check_index(p, plan);
       if (st != SGA_OK) return st;
       return check_mla(p, plan);
+    case SGA_OP_INDEXER_KL:
+      return check_kl(p);
     default:
       return fail(SGA_ERR_INVALID_ARGUMENT, "unknown op %d", op);
   }
@@ -152,6 +177,8 @@ size_t ws_bytes(const sga_problem *p, int op, const Plan &plan) {
       return align256((size_t)p->num_q * score_stride(p) * 4) +
              align256((size_t)p->num_q * p->topk * 4) +
              align256(topk_ws_bytes(p->num_q, p->max_kv_len)) + mla_ws(p, plan);
+    case SGA_OP_INDEXER_KL:
+      return indexer_kl_ws_bytes(p->num_q, p->topk, p->idx_heads, p->idx_dim);
   }
   return 0;
 }
@@ -442,6 +469,32 @@ sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dt
                                         slots, p->num_kv_rows, p->kv_dtype, kv, kv_scale,
                                         p->idx_dtype, k_idx, (hipStream_t)stream),
                     "cache append");
+  } catch (...) {
+    return fail(SGA_ERR_DEVICE, "internal error");
+  }
+}
+
+sga_status sga_indexer_kl(const sga_problem *p, const void *q_idx, const float *w,
+                          const void *k_idx, const void *q, const void *kv,
+                          const uint8_t *kv_scale, const int32_t *topk_idx, const float *lse,
+                          float *loss, float *d_w, float *d_q_idx, float *d_k_idx, void *ws,
+                          size_t ws_size, void *stream) {
+  try {
+    Plan plan;
+    SGA_TRY(plan_for(p, SGA_OP_INDEXER_KL, &plan));
+    if (p->num_q == 0) return SGA_OK;
+    if (!q_idx || !w || !k_idx || !q || !kv || !topk_idx || !lse || !loss || !d_w || !d_q_idx || !d_k_idx)
+      return fail(SGA_ERR_INVALID_ARGUMENT, "a tensor argument is NULL");
+    if (p->kv_dtype == SGA_MXFP8_E4M3FN && !kv_scale)
+      return fail(SGA_ERR_INVALID_ARGUMENT, "MXFP8 rows need kv_scale");
+    const size_t need = ws_bytes(p, SGA_OP_INDEXER_KL, plan);
+    if (!ws || ws_size < need)
+      return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_size);
+    return launched(launch_indexer_kl(meta_of(p), p->num_q, p->heads, p->d_latent + p->d_rope,
+                                      p->idx_heads, p->idx_dim, p->topk, p->softmax_scale, q, p->q_dtype,
+                                      kv, p->kv_dtype, kv_scale, q_idx, w, k_idx, p->idx_dtype, topk_idx,
+                                      lse, loss, d_w, d_q_idx, d_k_idx, ws, (hipStream_t)stream),
+                    "indexer KL");
   } catch (...) {
     return fail(SGA_ERR_DEVICE, "internal error");
   }

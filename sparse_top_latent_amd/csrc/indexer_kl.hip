@@ -1,0 +1,374 @@
+// Indexer KL loss over the sparse top-k selection and its gradients (the
+// training side of the indexer, "A.X K2 Technical Report" section 3.4: a KL
+// loss aligns the indexer's scores with the attention distribution, computed
+// over the sparse selection from the start).
+//
+// For query t with selected positions S_t (the forward's top-k list) and the
+// forward's per-head log-sum-exp lse[t, h]:
+//   target_s = sum_h exp(tau q_h . kv_s - lse_h), normalised over S_t
+//   I_s      = sum_h w_h ReLU(qI_h . kI_s),  q = softmax over S_t of I
+//   loss_t   = sum_s target_s (log target_s - log q_s)
+//   g_s      = q_s - target_s                 (the target is a constant)
+//   d_w[h]   = sum_s g_s ReLU(z_hs)
+//   d_qI[h]  = sum_s g_s w_h [z_hs > 0] kI_s
+//   d_kI[s] += sum_h g_s w_h [z_hs > 0] qI_h  (added into the caller's buffer)
+//
+// Three kernels per call:
+//   k_kl_rows      one workgroup per (64 selected rows, query): the head-summed
+//                  attention mass of each row (fp32 dot products from q in LDS)
+//                  and its indexer score;
+//   k_kl_loss      one workgroup per query: the two normalisations, the loss
+//                  and g;
+//   k_kl_backward  one workgroup per (64 rows, query): z again, d_kI by fp32
+//                  atomics, and per-chunk partials of d_w and d_qI;
+//   k_kl_reduce    sums the partials over the chunks (fixed order).
+// The arithmetic is fp32 on the vector ALUs: per query it is a few hundred
+// MFLOP, against the milliseconds a training step spends elsewhere.
+
+#include "kernels.h"
+
+namespace sga {
+namespace {
+
+constexpr int kKlRows = 64;     // selected rows per workgroup
+constexpr int kKlThreads = 256; // 4 threads per row
+
+// 8 consecutive values of element type dt starting at element i of p (i a
+// multiple of 8); MXFP8 values take the E8M0 scale of their 32-value block.
+__device__ __forceinline__ void load8(const void *p, int dt, const uint8_t *scale, int64_t row_elems,
+                                      int64_t row, int d, float v[8]) {
+  const int64_t i = row * row_elems + d;
+  if (dt == SGA_BF16) {
+    const uint4 r = *(const uint4 *)((const uint16_t *)p + i);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  } else if (dt == SGA_F32) {
+    const float4 a = *(const float4 *)((const float *)p + i), b = *(const float4 *)((const float *)p + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint2 r = *(const uint2 *)((const uint8_t *)p + i);
+    const float sc = dt == SGA_MXFP8_E4M3FN ? e8m0_to_f32(scale[row * (row_elems / 32) + d / 32]) : 1.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = e4m3fn_to_f32((r.x >> (8 * k)) & 0xffu) * sc;
+      v[4 + k] = e4m3fn_to_f32((r.y >> (8 * k)) & 0xffu) * sc;
+    }
+  }
+}
+
+struct KlArgs {
+  SeqMeta meta;
+  int T, H, D, HI, DI, k;
+  float tau;
+  const void *q;
+  int q_dtype;
+  const void *kv;
+  int kv_dtype;
+  const uint8_t *kv_scale;
+  const void *q_idx;
+  const float *w;
+  const void *k_idx;
+  int idx_dtype;
+  const int32_t *topk_idx;
+  const float *lse;
+  float *loss, *d_w, *d_q_idx, *d_k_idx;
+  float *mass, *score, *grad;  // [T, k] each
+  float *part_w, *part_q;      // [T, chunks, HI], [T, chunks, HI, DI]
+  int chunks;
+};
+
+// cache row of selected slot r of query t (-1: none)
+__device__ __forceinline__ int64_t sel_row(const KlArgs &a, int t, int r, int n, int64_t start) {
+  const int32_t pos = a.topk_idx[(size_t)t * a.k + r];
+  return (pos >= 0 && pos < n) ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
+}
+
+__global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float *qi = (float *)smem;                          // [HI, DI] index query, fp32
+  float *wsh = qi + a.HI * a.DI;                      // [HI]
+  unsigned char *qs = (unsigned char *)(wsh + 64);   // [H, D] query as stored (bf16 or fp32)
+  const bool qbf = a.q_dtype == SGA_BF16;
+  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
+  const int tid = threadIdx.x, j = tid >> 2, hg = tid & 3;
+  int64_t start;
+  const int n = query_candidates(a.meta, t, &start);
+  for (int i = tid; i < a.HI * a.DI; i += kKlThreads)
+    qi[i] = a.idx_dtype == SGA_F32 ? ((const float *)a.q_idx)[(size_t)t * a.HI * a.DI + i]
+                                   : e4m3fn_to_f32(((const uint8_t *)a.q_idx)[(size_t)t * a.HI * a.DI + i]);
+  for (int i = tid; i < a.HI; i += kKlThreads) wsh[i] = a.w[(size_t)t * a.HI + i];
+  for (int i = tid; i < a.H * a.D; i += kKlThreads) {
+    if (qbf)
+      ((uint16_t *)qs)[i] = ((const uint16_t *)a.q)[(size_t)t * a.H * a.D + i];
+    else
+      ((float *)qs)[i] = ((const float *)a.q)[(size_t)t * a.H * a.D + i];
+  }
+  __syncthreads();
+  const int r = r0 + j;
+  const int64_t row = r < a.k ? sel_row(a, t, r, n, start) : -1;
+  // attention mass: heads hg, hg + 4, ... of row j
+  float dot[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dot[i] = 0.0f;
+  if (row >= 0) {
+    for (int d = 0; d < a.D; d += 8) {
+      float v[8];
+      load8(a.kv, a.kv_dtype, a.kv_scale, a.D, row, d, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = hg + 4 * i;
+        if (h < a.H) {
+          float qv[8];
+          if (qbf) {
+            const uint4 r = *(const uint4 *)((const uint16_t *)qs + h * a.D + d);
+            const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              qv[2 * e] = __uint_as_float(wd[e] << 16);
+              qv[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+            }
+          } else {
+            const float4 x = *(const float4 *)((const float *)qs + h * a.D + d);
+            const float4 y = *(const float4 *)((const float *)qs + h * a.D + d + 4);
+            qv[0] = x.x; qv[1] = x.y; qv[2] = x.z; qv[3] = x.w;
+            qv[4] = y.x; qv[5] = y.y; qv[6] = y.z; qv[7] = y.w;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dot[i] = fmaf(qv[e], v[e], dot[i]);
+        }
+      }
+    }
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = hg + 4 * i;
+    if (h < a.H && row >= 0) m += __expf(a.tau * dot[i] - a.lse[(size_t)t * a.H + h]);
+  }
+  // indexer score: index heads hg, hg + 4, ...
+  float z[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  if (row >= 0) {
+    for (int d = 0; d < a.DI; d += 8) {
+      float v[8];
+      load8(a.k_idx, a.idx_dtype, nullptr, a.DI, row, d, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = hg + 4 * i;
+        if (h < a.HI) {
+          const float *qh = qi + h * a.DI + d;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[i] = fmaf(qh[e], v[e], z[i]);
+        }
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = hg + 4 * i;
+    if (h < a.HI) s = fmaf(fmaxf(z[i], 0.0f), wsh[h], s);
+  }
+  // sum over the 4 threads of the row (consecutive lanes)
+  m += __shfl_xor(m, 1);
+  m += __shfl_xor(m, 2);
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  if (hg == 0 && r < a.k) {
+    a.mass[(size_t)t * a.k + r] = row >= 0 ? m : 0.0f;
+    a.score[(size_t)t * a.k + r] = row >= 0 ? s : -INFINITY;
+  }
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = 0.0f;
+  for (int i = 0; i < kKlThreads / 64; ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float s = -INFINITY;
+  for (int i = 0; i < kKlThreads / 64; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+__global__ __launch_bounds__(kKlThreads) void k_kl_loss(KlArgs a) {
+  __shared__ float red[kKlThreads / 64];
+  const int t = blockIdx.x;
+  const float *sc = a.score + (size_t)t * a.k, *ms = a.mass + (size_t)t * a.k;
+  float mx = -INFINITY, tot = 0.0f;
+  for (int r = threadIdx.x; r < a.k; r += kKlThreads) {
+    mx = fmaxf(mx, sc[r]);
+    tot += ms[r];
+  }
+  mx = block_max(mx, red);
+  tot = block_sum(tot, red);
+  float z = 0.0f;
+  if (mx > -INFINITY)
+    for (int r = threadIdx.x; r < a.k; r += kKlThreads) z += __expf(sc[r] - mx);
+  z = block_sum(z, red);
+  const float lz = mx + __logf(z);
+  float loss = 0.0f;
+  for (int r = threadIdx.x; r < a.k; r += kKlThreads) {
+    float g = 0.0f;
+    if (sc[r] > -INFINITY) {
+      const float logq = sc[r] - lz;
+      const float tg = tot > 0.0f ? ms[r] / tot : 0.0f;
+      if (tg > 0.0f) loss += tg * (__logf(tg) - logq);
+      g = __expf(logq) - tg;
+    }
+    a.grad[(size_t)t * a.k + r] = g;
+  }
+  loss = block_sum(loss, red);
+  if (threadIdx.x == 0) a.loss[t] = mx > -INFINITY ? loss : 0.0f;
+}
+
+__global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float *qi = (float *)smem;                 // [HI, DI]
+  float *wsh = qi + a.HI * a.DI;             // [64]
+  float *kr = wsh + 64;                      // [kKlRows, DI] selected index keys
+  float *gz = kr + kKlRows * a.DI;           // [kKlRows, 64]: g w [z > 0]
+  float *rz = gz + kKlRows * 64;             // [kKlRows, 64]: g ReLU(z)
+  __shared__ float gr[kKlRows];
+  __shared__ int64_t rows[kKlRows];
+  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
+  const int tid = threadIdx.x;
+  int64_t start;
+  const int n = query_candidates(a.meta, t, &start);
+  for (int i = tid; i < a.HI * a.DI; i += kKlThreads)
+    qi[i] = a.idx_dtype == SGA_F32 ? ((const float *)a.q_idx)[(size_t)t * a.HI * a.DI + i]
+                                   : e4m3fn_to_f32(((const uint8_t *)a.q_idx)[(size_t)t * a.HI * a.DI + i]);
+  for (int i = tid; i < a.HI; i += kKlThreads) wsh[i] = a.w[(size_t)t * a.HI + i];
+  if (tid < kKlRows) {
+    const int r = r0 + tid;
+    const int64_t row = r < a.k ? sel_row(a, t, r, n, start) : -1;
+    rows[tid] = row;
+    gr[tid] = row >= 0 ? a.grad[(size_t)t * a.k + r] : 0.0f;
+  }
+  __syncthreads();
+  for (int i = tid; i < kKlRows * (a.DI / 8); i += kKlThreads) {
+    const int j = i / (a.DI / 8), d = (i % (a.DI / 8)) * 8;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (rows[j] >= 0) load8(a.k_idx, a.idx_dtype, nullptr, a.DI, rows[j], d, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kr[j * a.DI + d + e] = v[e];
+  }
+  __syncthreads();
+  // z of (row j, index head h) for 4 threads per row
+  {
+    const int j = tid >> 2, hg = tid & 3;
+    for (int h = hg; h < a.HI; h += 4) {
+      float z = 0.0f;
+      for (int d = 0; d < a.DI; ++d) z = fmaf(qi[h * a.DI + d], kr[j * a.DI + d], z);
+      gz[j * 64 + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
+      rz[j * 64 + h] = gr[j] * fmaxf(z, 0.0f);
+    }
+  }
+  __syncthreads();
+  const size_t chunk = (size_t)t * a.chunks + blockIdx.x;
+  for (int h = tid; h < a.HI; h += kKlThreads) {
+    float s = 0.0f;
+    for (int j = 0; j < kKlRows; ++j) s += rz[j * 64 + h];
+    a.part_w[chunk * a.HI + h] = s;
+  }
+  for (int i = tid; i < a.HI * a.DI; i += kKlThreads) {
+    const int h = i / a.DI, d = i % a.DI;
+    float s = 0.0f;
+    for (int j = 0; j < kKlRows; ++j) s = fmaf(gz[j * 64 + h], kr[j * a.DI + d], s);
+    a.part_q[chunk * a.HI * a.DI + i] = s;
+  }
+  for (int i = tid; i < kKlRows * a.DI; i += kKlThreads) {
+    const int j = i / a.DI, d = i % a.DI;
+    if (rows[j] < 0 || gr[j] == 0.0f) continue;
+    float s = 0.0f;
+    for (int h = 0; h < a.HI; ++h) s = fmaf(gz[j * 64 + h], qi[h * a.DI + d], s);
+    atomicAdd(a.d_k_idx + rows[j] * a.DI + d, s);
+  }
+}
+
+__global__ __launch_bounds__(kKlThreads) void k_kl_reduce(KlArgs a) {
+  const int t = blockIdx.y;
+  const int i = blockIdx.x * kKlThreads + threadIdx.x;  // over HI * DI + HI outputs
+  const int nq = a.HI * a.DI;
+  if (i >= nq + a.HI) return;
+  float s = 0.0f;
+  if (i < nq) {
+    for (int c = 0; c < a.chunks; ++c) s += a.part_q[((size_t)t * a.chunks + c) * nq + i];
+    a.d_q_idx[(size_t)t * nq + i] = s;
+  } else {
+    const int h = i - nq;
+    for (int c = 0; c < a.chunks; ++c) s += a.part_w[((size_t)t * a.chunks + c) * a.HI + h];
+    a.d_w[(size_t)t * a.HI + h] = s;
+  }
+}
+
+}  // namespace
+
+size_t indexer_kl_ws_bytes(int T, int k, int HI, int DI) {
+  const size_t chunks = (k + kKlRows - 1) / kKlRows;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return 3 * al((size_t)T * k * 4) + al((size_t)T * chunks * HI * 4) + al((size_t)T * chunks * HI * DI * 4);
+}
+
+size_t indexer_kl_smem(int H, int D, int HI, int DI, int q_dtype) {
+  const size_t rows = ((size_t)HI * DI + 64) * 4 + (size_t)H * D * (q_dtype == SGA_BF16 ? 2 : 4);
+  const size_t back = ((size_t)HI * DI + 64 + (size_t)kKlRows * DI + 2 * kKlRows * 64) * 4;
+  return rows > back ? rows : back;
+}
+
+hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int DI, int k, float tau,
+                             const void *q, int q_dtype, const void *kv, int kv_dtype,
+                             const uint8_t *kv_scale, const void *q_idx, const float *w,
+                             const void *k_idx, int idx_dtype, const int32_t *topk_idx,
+                             const float *lse, float *loss, float *d_w, float *d_q_idx, float *d_k_idx,
+                             void *ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  KlArgs a;
+  a.meta = m;
+  a.T = T; a.H = H; a.D = D; a.HI = HI; a.DI = DI; a.k = k; a.tau = tau;
+  a.q = q; a.q_dtype = q_dtype; a.kv = kv; a.kv_dtype = kv_dtype; a.kv_scale = kv_scale;
+  a.q_idx = q_idx; a.w = w; a.k_idx = k_idx; a.idx_dtype = idx_dtype;
+  a.topk_idx = topk_idx; a.lse = lse;
+  a.loss = loss; a.d_w = d_w; a.d_q_idx = d_q_idx; a.d_k_idx = d_k_idx;
+  a.chunks = (k + kKlRows - 1) / kKlRows;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char *c = (char *)ws;
+  a.mass = (float *)c; c += al((size_t)T * k * 4);
+  a.score = (float *)c; c += al((size_t)T * k * 4);
+  a.grad = (float *)c; c += al((size_t)T * k * 4);
+  a.part_w = (float *)c; c += al((size_t)T * a.chunks * HI * 4);
+  a.part_q = (float *)c;
+  const size_t smem = indexer_kl_smem(H, D, HI, DI, q_dtype);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)k_kl_rows, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_kl_backward, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  const dim3 grid(a.chunks, T);
+  hipLaunchKernelGGL(k_kl_rows, grid, dim3(kKlThreads), smem, s, a);
+  hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
+  hipLaunchKernelGGL(k_kl_backward, grid, dim3(kKlThreads), smem, s, a);
+  hipLaunchKernelGGL(k_kl_reduce, dim3((HI * DI + HI + kKlThreads - 1) / kKlThreads, T), dim3(kKlThreads), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace sga

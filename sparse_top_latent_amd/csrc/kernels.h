@@ -95,4 +95,15 @@ hipError_t launch_cache_append(int64_t N, int D, int DI, int src_dtype, const vo
                                int kv_dtype, void *kv, uint8_t *kv_scale, int idx_dtype,
                                void *k_idx, hipStream_t s);
 
+// --- indexer KL loss (training side) ------------------------------------------
+size_t indexer_kl_ws_bytes(int T, int k, int HI, int DI);
+// LDS bytes the KL kernels need (must stay within 160 KiB)
+size_t indexer_kl_smem(int H, int D, int HI, int DI, int q_dtype);
+hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int DI, int k, float tau,
+                             const void *q, int q_dtype, const void *kv, int kv_dtype,
+                             const uint8_t *kv_scale, const void *q_idx, const float *w,
+                             const void *k_idx, int idx_dtype, const int32_t *topk_idx,
+                             const float *lse, float *loss, float *d_w, float *d_q_idx, float *d_k_idx,
+                             void *ws, hipStream_t s);
+
 }  // namespace sga

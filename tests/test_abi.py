@@ -194,3 +194,36 @@ def test_cache_append_nothing_to_do(lib):
     assert lib.sga_cache_append(ctypes.byref(p), 0, 1, FAKE, FAKE, None, None, None, None, None) == 0
     assert lib.sga_cache_append(ctypes.byref(p), 16, 1, None, None, None, None, None, None, None) == 0
     assert lib.sga_cache_append(None, 16, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=80), 2),
+    (dict(idx_dim=100), 2),
+    (dict(topk=5000), 2),
+    (dict(q_dtype=2), 2),
+    (dict(kv_dtype=2), 2),
+    (dict(idx_dtype=1), 2),
+    (dict(d_latent=1000, d_rope=24), 2),   # q of one query past 96 KiB
+    (dict(num_q=-1), 1),
+])
+def test_indexer_kl_argument_errors(lib, kw, status):
+    p = _problem(**kw)
+    st, _ = _ws(lib, p, _ffi.SGA_OP_INDEXER_KL)
+    assert st == status, lib.sga_last_error()
+    st = lib.sga_indexer_kl(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == status
+
+
+def test_indexer_kl_null_buffers_and_workspace(lib):
+    p = _problem()
+    st, n = _ws(lib, p, _ffi.SGA_OP_INDEXER_KL)
+    assert st == 0 and n > 16 * 2048 * 12
+    args = [FAKE] * 12
+    for i in range(12):
+        if i == 5:  # kv_scale may be NULL for bf16 rows
+            continue
+        a = list(args)
+        a[i] = None
+        assert lib.sga_indexer_kl(ctypes.byref(p), *a, FAKE, 1 << 40, None) == 1
+    assert lib.sga_indexer_kl(ctypes.byref(p), *args, FAKE, 16, None) == 3
