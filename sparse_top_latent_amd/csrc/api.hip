@@ -133,7 +133,8 @@ sga_status check_kl(const sga_problem *p) {
     return fail(SGA_ERR_UNSUPPORTED, "MXFP8 rows need a multiple of 32 values");
   if (p->idx_dtype != SGA_F32 && p->idx_dtype != SGA_FP8_E4M3FN)
     return fail(SGA_ERR_UNSUPPORTED, "indexer KL: index tensors must be SGA_F32 or SGA_FP8_E4M3FN");
-  if ((int64_t)p->heads * D * (p->q_dtype == SGA_BF16 ? 2 : 4) > 96 * 1024)
+  if ((int64_t)p->heads * D * (p->q_dtype == SGA_BF16 ? 2 : 4) > 96 * 1024 ||
+      indexer_kl_smem(p->heads, D, p->idx_heads, p->idx_dim, p->q_dtype) > 160 * 1024)
     return fail(SGA_ERR_UNSUPPORTED, "indexer KL: q of one query must fit 96 KiB");
   return SGA_OK;
 }

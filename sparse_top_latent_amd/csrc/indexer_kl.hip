@@ -88,25 +88,66 @@ __device__ __forceinline__ int64_t sel_row(const KlArgs &a, int t, int r, int n,
   return (pos >= 0 && pos < n) ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
 }
 
+constexpr int kKlBatch = 4;
+
+// LDS row stride (in dwords) of a table read by four threads of different
+// rows at once (the 4 head groups of k_kl_rows): congruent to 4 mod 64, so
+// that their 16-byte reads fall on four different groups of banks
+__host__ __device__ __forceinline__ int kl_ld(int dwords) { return dwords + (68 - dwords % 64) % 64; }  // 8-value chunks of a latent row requested together by k_kl_rows
+
+// dot[i] += q[h] . v over 8 values at d, for the heads h = hg + 4 i of this thread
+__device__ __forceinline__ void head_dots(const unsigned char *qs, bool qbf, int H, int D, int hg, int d,
+                                          const float v[8], float dot[16]) {
+  const int ld = kl_ld(qbf ? D / 2 : D) * (qbf ? 2 : 1);  // row stride in elements
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = hg + 4 * i;
+    if (h < H) {
+      float qv[8];
+      if (qbf) {
+        const uint4 r = *(const uint4 *)((const uint16_t *)qs + h * ld + d);
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[2 * e] = __uint_as_float(wd[e] << 16);
+          qv[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+        }
+      } else {
+        const float4 x = *(const float4 *)((const float *)qs + h * ld + d);
+        const float4 y = *(const float4 *)((const float *)qs + h * ld + d + 4);
+        qv[0] = x.x; qv[1] = x.y; qv[2] = x.z; qv[3] = x.w;
+        qv[4] = y.x; qv[5] = y.y; qv[6] = y.z; qv[7] = y.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot[i] = fmaf(qv[e], v[e], dot[i]);
+    }
+  }
+}
+
+template <bool kMass>
 __global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float *qi = (float *)smem;                          // [HI, DI] index query, fp32
-  float *wsh = qi + a.HI * a.DI;                      // [HI]
-  unsigned char *qs = (unsigned char *)(wsh + 64);   // [H, D] query as stored (bf16 or fp32)
   const bool qbf = a.q_dtype == SGA_BF16;
+  const int qild = kl_ld(a.DI);                                    // padded rows (see kl_ld)
+  const int qld = kl_ld(qbf ? a.D / 2 : a.D) * (qbf ? 2 : 1);
+  float *qi = (float *)smem;                          // [HI, qild] index query, fp32
+  float *wsh = qi + a.HI * qild;                      // [HI]
+  unsigned char *qs = (unsigned char *)(wsh + 64);   // [H, qld] query as stored (bf16 or fp32)
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
   const int tid = threadIdx.x, j = tid >> 2, hg = tid & 3;
   int64_t start;
   const int n = query_candidates(a.meta, t, &start);
   for (int i = tid; i < a.HI * a.DI; i += kKlThreads)
-    qi[i] = a.idx_dtype == SGA_F32 ? ((const float *)a.q_idx)[(size_t)t * a.HI * a.DI + i]
-                                   : e4m3fn_to_f32(((const uint8_t *)a.q_idx)[(size_t)t * a.HI * a.DI + i]);
+    qi[(i / a.DI) * qild + i % a.DI] =
+        a.idx_dtype == SGA_F32 ? ((const float *)a.q_idx)[(size_t)t * a.HI * a.DI + i]
+                               : e4m3fn_to_f32(((const uint8_t *)a.q_idx)[(size_t)t * a.HI * a.DI + i]);
   for (int i = tid; i < a.HI; i += kKlThreads) wsh[i] = a.w[(size_t)t * a.HI + i];
-  for (int i = tid; i < a.H * a.D; i += kKlThreads) {
+  for (int i = tid; kMass && i < a.H * a.D; i += kKlThreads) {
+    const int o = (i / a.D) * qld + i % a.D;
     if (qbf)
-      ((uint16_t *)qs)[i] = ((const uint16_t *)a.q)[(size_t)t * a.H * a.D + i];
+      ((uint16_t *)qs)[o] = ((const uint16_t *)a.q)[(size_t)t * a.H * a.D + i];
     else
-      ((float *)qs)[i] = ((const float *)a.q)[(size_t)t * a.H * a.D + i];
+      ((float *)qs)[o] = ((const float *)a.q)[(size_t)t * a.H * a.D + i];
   }
   __syncthreads();
   const int r = r0 + j;
@@ -115,33 +156,54 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
   float dot[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) dot[i] = 0.0f;
-  if (row >= 0) {
+  // bf16 and MXFP8 rows are requested kKlBatch chunks of 8 values at a time
+  // before any arithmetic on them: one memory latency per batch instead of
+  // one per chunk
+  const bool staged = a.kv_dtype == SGA_BF16 || a.kv_dtype == SGA_MXFP8_E4M3FN;
+  if (kMass && row >= 0 && staged) {
+    for (int base = 0; base < a.D; base += 8 * kKlBatch) {
+      uint4 st[kKlBatch];
+#pragma unroll
+      for (int c = 0; c < kKlBatch; ++c) {
+        const int d = base + c * 8;
+        if (d < a.D) {
+          if (a.kv_dtype == SGA_BF16) {
+            st[c] = *(const uint4 *)((const uint16_t *)a.kv + row * a.D + d);
+          } else {
+            const uint2 r = *(const uint2 *)((const uint8_t *)a.kv + row * a.D + d);
+            st[c] = make_uint4(r.x, r.y, a.kv_scale[row * (a.D / 32) + d / 32], 0u);
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kKlBatch; ++c) {
+        const int d = base + c * 8;
+        if (d < a.D) {
+          float v[8];
+          if (a.kv_dtype == SGA_BF16) {
+            const uint32_t wd[4] = {st[c].x, st[c].y, st[c].z, st[c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[2 * e] = __uint_as_float(wd[e] << 16);
+              v[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
+            }
+          } else {
+            const float sc = e8m0_to_f32(st[c].z);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = e4m3fn_to_f32((st[c].x >> (8 * e)) & 0xffu) * sc;
+              v[4 + e] = e4m3fn_to_f32((st[c].y >> (8 * e)) & 0xffu) * sc;
+            }
+          }
+          head_dots(qs, qbf, a.H, a.D, hg, d, v, dot);
+        }
+      }
+    }
+  } else if (kMass && row >= 0) {
     for (int d = 0; d < a.D; d += 8) {
       float v[8];
       load8(a.kv, a.kv_dtype, a.kv_scale, a.D, row, d, v);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = hg + 4 * i;
-        if (h < a.H) {
-          float qv[8];
-          if (qbf) {
-            const uint4 r = *(const uint4 *)((const uint16_t *)qs + h * a.D + d);
-            const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              qv[2 * e] = __uint_as_float(wd[e] << 16);
-              qv[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
-            }
-          } else {
-            const float4 x = *(const float4 *)((const float *)qs + h * a.D + d);
-            const float4 y = *(const float4 *)((const float *)qs + h * a.D + d + 4);
-            qv[0] = x.x; qv[1] = x.y; qv[2] = x.z; qv[3] = x.w;
-            qv[4] = y.x; qv[5] = y.y; qv[6] = y.z; qv[7] = y.w;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dot[i] = fmaf(qv[e], v[e], dot[i]);
-        }
-      }
+      head_dots(qs, qbf, a.H, a.D, hg, d, v, dot);
     }
   }
   float m = 0.0f;
@@ -155,16 +217,24 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.0f;
   if (row >= 0) {
-    for (int d = 0; d < a.DI; d += 8) {
-      float v[8];
-      load8(a.k_idx, a.idx_dtype, nullptr, a.DI, row, d, v);
+    // the key row is requested 4 chunks of 8 values at a time
+    for (int base = 0; base < a.DI; base += 32) {
+      float kv8[4][8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = hg + 4 * i;
-        if (h < a.HI) {
-          const float *qh = qi + h * a.DI + d;
+      for (int c = 0; c < 4; ++c)
+        if (base + c * 8 < a.DI) load8(a.k_idx, a.idx_dtype, nullptr, a.DI, row, base + c * 8, kv8[c]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) z[i] = fmaf(qh[e], v[e], z[i]);
+      for (int c = 0; c < 4; ++c) {
+        if (base + c * 8 < a.DI) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int h = hg + 4 * i;
+            if (h < a.HI) {
+              const float *qh = qi + h * qild + base + c * 8;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) z[i] = fmaf(qh[e], kv8[c][e], z[i]);
+            }
+          }
         }
       }
     }
@@ -181,8 +251,79 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
   if (hg == 0 && r < a.k) {
-    a.mass[(size_t)t * a.k + r] = row >= 0 ? m : 0.0f;
+    if (kMass) a.mass[(size_t)t * a.k + r] = row >= 0 ? m : 0.0f;
     a.score[(size_t)t * a.k + r] = row >= 0 ? s : -INFINITY;
+  }
+}
+
+// Attention mass of 64 selected rows with bf16 MFMA (64 heads, bf16 q, bf16
+// or MXFP8 rows, Dc + Dr = 32 kKlKsteps): wave w takes heads 16 w .. 16 w + 15
+// and all 64 rows, S^T = rows . q^T per 16-row tile (16x16x32 bf16 MFMA; the
+// query slice stays in VGPRs as the B operand; MXFP8 rows are expanded
+// exactly to bf16 on the way in).
+constexpr int kKlKsteps = 18;
+
+__global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
+  __shared__ float part[kKlThreads / 64][kKlRows];
+  __shared__ int64_t rows[kKlRows];
+  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  int64_t start;
+  const int n = query_candidates(a.meta, t, &start);
+  if (tid < kKlRows) {
+    const int r = r0 + tid;
+    rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
+  }
+  const int head = wave * 16 + c16;
+  const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
+  v4i qreg[kKlKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
+  const float lse_h = a.lse[(size_t)t * 64 + head];
+  const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
+  __syncthreads();
+  for (int rt = 0; rt < kKlRows / 16; ++rt) {
+    const int64_t row = rows[rt * 16 + c16];
+    v4i av[kKlKsteps];
+#pragma unroll
+    for (int ks = 0; ks < kKlKsteps; ++ks) {
+      const int d = ks * 32 + 8 * g;
+      if (row < 0) {
+        av[ks] = (v4i){0, 0, 0, 0};
+      } else if (!mx) {
+        av[ks] = *(const v4i *)((const uint16_t *)a.kv + row * a.D + d);
+      } else {
+        const uint2 w8 = *(const uint2 *)((const uint8_t *)a.kv + row * a.D + d);
+        const float sc = e8m0_to_f32(a.kv_scale[row * (a.D / 32) + ks]);
+        av[ks] = (v4i){(int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, sc, false)),
+                       (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, sc, true)),
+                       (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, sc, false)),
+                       (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, sc, true))};
+      }
+    }
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKlKsteps; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[ks]), __builtin_bit_cast(v8bf, qreg[ks]),
+                                                     acc, 0, 0, 0);
+    // acc[i]: logit of row rt*16 + 4 g + i for this lane's head
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = rt * 16 + 4 * g + i;
+      float e = rows[j] >= 0 ? __expf(a.tau * acc[i] - lse_h) : 0.0f;
+      e += __shfl_xor(e, 1);
+      e += __shfl_xor(e, 2);
+      e += __shfl_xor(e, 4);
+      e += __shfl_xor(e, 8);
+      if (c16 == 0) part[wave][j] = e;
+    }
+  }
+  __syncthreads();
+  if (tid < kKlRows && r0 + tid < a.k) {
+    float m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
+    a.mass[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? m : 0.0f;
   }
 }
 
@@ -239,10 +380,13 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_loss(KlArgs a) {
 
 __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float *qi = (float *)smem;                 // [HI, DI]
-  float *wsh = qi + a.HI * a.DI;             // [64]
-  float *kr = wsh + 64;                      // [kKlRows, DI] selected index keys
-  float *gz = kr + kKlRows * a.DI;           // [kKlRows, 64]: g w [z > 0]
+  // rows of qi and kr are padded by one word, so that the z loop's lanes
+  // (16 rows x 4 heads per wave, same d) hit distinct LDS banks
+  const int ld = a.DI + 1;
+  float *qi = (float *)smem;                 // [HI, DI + 1]
+  float *wsh = qi + a.HI * ld;               // [64]
+  float *kr = wsh + 64;                      // [kKlRows, DI + 1] selected index keys
+  float *gz = kr + kKlRows * ld;             // [kKlRows, 64]: g w [z > 0]
   float *rz = gz + kKlRows * 64;             // [kKlRows, 64]: g ReLU(z)
   __shared__ float gr[kKlRows];
   __shared__ int64_t rows[kKlRows];
@@ -251,8 +395,9 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   int64_t start;
   const int n = query_candidates(a.meta, t, &start);
   for (int i = tid; i < a.HI * a.DI; i += kKlThreads)
-    qi[i] = a.idx_dtype == SGA_F32 ? ((const float *)a.q_idx)[(size_t)t * a.HI * a.DI + i]
-                                   : e4m3fn_to_f32(((const uint8_t *)a.q_idx)[(size_t)t * a.HI * a.DI + i]);
+    qi[(i / a.DI) * ld + i % a.DI] =
+        a.idx_dtype == SGA_F32 ? ((const float *)a.q_idx)[(size_t)t * a.HI * a.DI + i]
+                               : e4m3fn_to_f32(((const uint8_t *)a.q_idx)[(size_t)t * a.HI * a.DI + i]);
   for (int i = tid; i < a.HI; i += kKlThreads) wsh[i] = a.w[(size_t)t * a.HI + i];
   if (tid < kKlRows) {
     const int r = r0 + tid;
@@ -266,7 +411,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (rows[j] >= 0) load8(a.k_idx, a.idx_dtype, nullptr, a.DI, rows[j], d, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) kr[j * a.DI + d + e] = v[e];
+    for (int e = 0; e < 8; ++e) kr[j * ld + d + e] = v[e];
   }
   __syncthreads();
   // z of (row j, index head h) for 4 threads per row
@@ -274,7 +419,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     const int j = tid >> 2, hg = tid & 3;
     for (int h = hg; h < a.HI; h += 4) {
       float z = 0.0f;
-      for (int d = 0; d < a.DI; ++d) z = fmaf(qi[h * a.DI + d], kr[j * a.DI + d], z);
+      for (int d = 0; d < a.DI; ++d) z = fmaf(qi[h * ld + d], kr[j * ld + d], z);
       gz[j * 64 + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
       rz[j * 64 + h] = gr[j] * fmaxf(z, 0.0f);
     }
@@ -289,14 +434,14 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   for (int i = tid; i < a.HI * a.DI; i += kKlThreads) {
     const int h = i / a.DI, d = i % a.DI;
     float s = 0.0f;
-    for (int j = 0; j < kKlRows; ++j) s = fmaf(gz[j * 64 + h], kr[j * a.DI + d], s);
+    for (int j = 0; j < kKlRows; ++j) s = fmaf(gz[j * 64 + h], kr[j * ld + d], s);
     a.part_q[chunk * a.HI * a.DI + i] = s;
   }
   for (int i = tid; i < kKlRows * a.DI; i += kKlThreads) {
     const int j = i / a.DI, d = i % a.DI;
     if (rows[j] < 0 || gr[j] == 0.0f) continue;
     float s = 0.0f;
-    for (int h = 0; h < a.HI; ++h) s = fmaf(gz[j * 64 + h], qi[h * a.DI + d], s);
+    for (int h = 0; h < a.HI; ++h) s = fmaf(gz[j * 64 + h], qi[h * ld + d], s);
     atomicAdd(a.d_k_idx + rows[j] * a.DI + d, s);
   }
 }
@@ -326,8 +471,8 @@ size_t indexer_kl_ws_bytes(int T, int k, int HI, int DI) {
 }
 
 size_t indexer_kl_smem(int H, int D, int HI, int DI, int q_dtype) {
-  const size_t rows = ((size_t)HI * DI + 64) * 4 + (size_t)H * D * (q_dtype == SGA_BF16 ? 2 : 4);
-  const size_t back = ((size_t)HI * DI + 64 + (size_t)kKlRows * DI + 2 * kKlRows * 64) * 4;
+  const size_t rows = ((size_t)HI * kl_ld(DI) + 64) * 4 + (size_t)H * kl_ld(q_dtype == SGA_BF16 ? D / 2 : D) * 4;
+  const size_t back = ((size_t)HI * (DI + 1) + 64 + (size_t)kKlRows * (DI + 1) + 2 * kKlRows * 64) * 4;
   return rows > back ? rows : back;
 }
 
@@ -353,17 +498,28 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
   a.grad = (float *)c; c += al((size_t)T * k * 4);
   a.part_w = (float *)c; c += al((size_t)T * a.chunks * HI * 4);
   a.part_q = (float *)c;
-  const size_t smem = indexer_kl_smem(H, D, HI, DI, q_dtype);
+  size_t smem = indexer_kl_smem(H, D, HI, DI, q_dtype);
+  // the MI355X shapes take the attention mass from the MFMA kernel
+  const bool mfma = H == 64 && q_dtype == SGA_BF16 && D == 32 * kKlKsteps &&
+                    (kv_dtype == SGA_BF16 || kv_dtype == SGA_MXFP8_E4M3FN);
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void *)k_kl_rows, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_kl_rows<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_kl_rows<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
     (void)hipFuncSetAttribute((const void *)k_kl_backward, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipGetLastError();
     attr = true;
   }
   const dim3 grid(a.chunks, T);
-  hipLaunchKernelGGL(k_kl_rows, grid, dim3(kKlThreads), smem, s, a);
+  if (mfma) {
+    hipLaunchKernelGGL(k_kl_mass_mfma, grid, dim3(kKlThreads), 0, s, a);
+    hipLaunchKernelGGL(k_kl_rows<false>, grid, dim3(kKlThreads), ((size_t)HI * kl_ld(DI) + 64) * 4, s, a);
+  } else {
+    hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
+  }
   hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
   hipLaunchKernelGGL(k_kl_backward, grid, dim3(kKlThreads), smem, s, a);
   hipLaunchKernelGGL(k_kl_reduce, dim3((HI * DI + HI + kKlThreads - 1) / kKlThreads, T), dim3(kKlThreads), 0, s,
