@@ -380,9 +380,9 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_loss(KlArgs a) {
 
 __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // rows of qi and kr are padded by one word, so that the z loop's lanes
-  // (16 rows x 4 heads per wave, same d) hit distinct LDS banks
-  const int ld = a.DI + 1;
+  // rows of qi and kr are padded by four words: 16-byte aligned, and the z
+  // loop's lanes (16 rows x 4 heads per wave, same d) hit distinct banks
+  const int ld = a.DI + 4;
   float *qi = (float *)smem;                 // [HI, DI + 1]
   float *wsh = qi + a.HI * ld;               // [64]
   float *kr = wsh + 64;                      // [kKlRows, DI + 1] selected index keys
@@ -419,7 +419,10 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     const int j = tid >> 2, hg = tid & 3;
     for (int h = hg; h < a.HI; h += 4) {
       float z = 0.0f;
-      for (int d = 0; d < a.DI; ++d) z = fmaf(qi[h * ld + d], kr[j * ld + d], z);
+      for (int d = 0; d < a.DI; d += 4) {
+        const float4 x = *(const float4 *)(qi + h * ld + d), y = *(const float4 *)(kr + j * ld + d);
+        z = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, z))));
+      }
       gz[j * 64 + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
       rz[j * 64 + h] = gr[j] * fmaxf(z, 0.0f);
     }
@@ -431,18 +434,31 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     for (int j = 0; j < kKlRows; ++j) s += rz[j * 64 + h];
     a.part_w[chunk * a.HI + h] = s;
   }
-  for (int i = tid; i < a.HI * a.DI; i += kKlThreads) {
+  // four consecutive outputs per thread (16-byte LDS reads)
+  for (int i = 4 * tid; i < a.HI * a.DI; i += 4 * kKlThreads) {
     const int h = i / a.DI, d = i % a.DI;
-    float s = 0.0f;
-    for (int j = 0; j < kKlRows; ++j) s = fmaf(gz[j * 64 + h], kr[j * ld + d], s);
-    a.part_q[chunk * a.HI * a.DI + i] = s;
+    float4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kKlRows; ++j) {
+      const float gv = gz[j * 64 + h];
+      const float4 x = *(const float4 *)(kr + j * ld + d);
+      s.x = fmaf(gv, x.x, s.x); s.y = fmaf(gv, x.y, s.y); s.z = fmaf(gv, x.z, s.z); s.w = fmaf(gv, x.w, s.w);
+    }
+    *(float4 *)(a.part_q + chunk * a.HI * a.DI + i) = s;
   }
-  for (int i = tid; i < kKlRows * a.DI; i += kKlThreads) {
+  for (int i = 4 * tid; i < kKlRows * a.DI; i += 4 * kKlThreads) {
     const int j = i / a.DI, d = i % a.DI;
     if (rows[j] < 0 || gr[j] == 0.0f) continue;
-    float s = 0.0f;
-    for (int h = 0; h < a.HI; ++h) s = fmaf(gz[j * 64 + h], qi[h * ld + d], s);
-    atomicAdd(a.d_k_idx + rows[j] * a.DI + d, s);
+    float4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < a.HI; ++h) {
+      const float gv = gz[j * 64 + h];
+      const float4 x = *(const float4 *)(qi + h * ld + d);
+      s.x = fmaf(gv, x.x, s.x); s.y = fmaf(gv, x.y, s.y); s.z = fmaf(gv, x.z, s.z); s.w = fmaf(gv, x.w, s.w);
+    }
+    float *dk = a.d_k_idx + rows[j] * a.DI + d;
+    atomicAdd(dk, s.x);
+    atomicAdd(dk + 1, s.y);
+    atomicAdd(dk + 2, s.z);
+    atomicAdd(dk + 3, s.w);
   }
 }
 
@@ -472,7 +488,7 @@ size_t indexer_kl_ws_bytes(int T, int k, int HI, int DI) {
 
 size_t indexer_kl_smem(int H, int D, int HI, int DI, int q_dtype) {
   const size_t rows = ((size_t)HI * kl_ld(DI) + 64) * 4 + (size_t)H * kl_ld(q_dtype == SGA_BF16 ? D / 2 : D) * 4;
-  const size_t back = ((size_t)HI * (DI + 1) + 64 + (size_t)kKlRows * (DI + 1) + 2 * kKlRows * 64) * 4;
+  const size_t back = ((size_t)HI * (DI + 4) + 64 + (size_t)kKlRows * (DI + 4) + 2 * kKlRows * 64) * 4;
   return rows > back ? rows : back;
 }
 
