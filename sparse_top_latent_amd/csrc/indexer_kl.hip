@@ -13,17 +13,19 @@
 //   d_qI[h]  = sum_s g_s w_h [z_hs > 0] kI_s
 //   d_kI[s] += sum_h g_s w_h [z_hs > 0] qI_h  (added into the caller's buffer)
 //
-// Three kernels per call:
-//   k_kl_rows      one workgroup per (64 selected rows, query): the head-summed
-//                  attention mass of each row (fp32 dot products from q in LDS)
-//                  and its indexer score;
-//   k_kl_loss      one workgroup per query: the two normalisations, the loss
-//                  and g;
-//   k_kl_backward  one workgroup per (64 rows, query): z again, d_kI by fp32
-//                  atomics, and per-chunk partials of d_w and d_qI;
-//   k_kl_reduce    sums the partials over the chunks (fixed order).
-// The arithmetic is fp32 on the vector ALUs: per query it is a few hundred
-// MFLOP, against the milliseconds a training step spends elsewhere.
+// Kernels per call:
+//   k_kl_mass_mfma  one workgroup per (64 selected rows, query), MI355X shapes:
+//                   the head-summed attention mass of each row, logits by bf16
+//                   MFMA with the query slice in VGPRs;
+//   k_kl_rows       one workgroup per (64 rows, query): each row's indexer score
+//                   (and, for the other shapes, its attention mass, fp32 dot
+//                   products from q in LDS);
+//   k_kl_loss       one workgroup per query: the two normalisations, the loss
+//                   and g;
+//   k_kl_backward   one workgroup per (64 rows, query): z again, d_kI by fp32
+//                   atomics, and per-chunk partials of d_w and d_qI;
+//   k_kl_reduce     sums the partials over the chunks (fixed order).
+// Everything after the logits is fp32 on the vector ALUs.
 
 #include "kernels.h"
 
