@@ -16,14 +16,16 @@
 // Kernels per call:
 //   k_kl_mass_mfma  one workgroup per (64 selected rows, query), MI355X shapes:
 //                   the head-summed attention mass of each row, logits by bf16
-//                   MFMA with the query slice in VGPRs;
+//                   MFMA with the query slice in VGPRs, and (FP8 index
+//                   tensors) each row's indexer score;
 //   k_kl_rows       one workgroup per (64 rows, query): each row's indexer score
 //                   (and, for the other shapes, its attention mass, fp32 dot
 //                   products from q in LDS);
 //   k_kl_loss       one workgroup per query: the two normalisations, the loss
 //                   and g;
-//   k_kl_backward   one workgroup per (64 rows, query): z again, d_kI by fp32
-//                   atomics, and per-chunk partials of d_w and d_qI;
+//   k_kl_backward   one workgroup per (64 rows, query): z again (bf16 MFMA for
+//                   FP8 index tensors), d_kI by fp32 atomics, and per-chunk
+//                   partials of d_w and d_qI;
 //   k_kl_reduce     sums the partials over the chunks (fixed order).
 // Everything after the logits is fp32 on the vector ALUs.
 
@@ -265,8 +267,22 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
 // exactly to bf16 on the way in).
 constexpr int kKlKsteps = 18;
 
+// 8 E4M3FN bytes -> 8 bf16 (exact), as a 16-byte MFMA operand
+__device__ __forceinline__ v4i fp8x8_to_bf16(uint2 w8) {
+  return (v4i){(int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, 1.0f, false)),
+               (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, 1.0f, true)),
+               (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, 1.0f, false)),
+               (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, 1.0f, true))};
+}
+
+// With kScores (64 FP8 index heads x 128 dims) the same workgroup also
+// computes each row's indexer score: z = kI . qI^T per 16-row tile by bf16
+// MFMA (E4M3FN values are exact in bf16, so z is the fp32 sum of exact
+// products), then sum_h w_h ReLU(z) over the wave's 16 heads and the 4 waves.
+template <bool kScores>
 __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
   __shared__ float part[kKlThreads / 64][kKlRows];
+  __shared__ float spart[kKlThreads / 64][kKlRows];
   __shared__ int64_t rows[kKlRows];
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
@@ -283,6 +299,15 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
   for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
   const float lse_h = a.lse[(size_t)t * 64 + head];
   const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
+  // index query of index head `head` (B operand) and its weight
+  v4i qireg[4];
+  float w_h = 0.0f;
+  if (kScores) {
+    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+    w_h = a.w[(size_t)t * 64 + head];
+  }
   __syncthreads();
   for (int rt = 0; rt < kKlRows / 16; ++rt) {
     const int64_t row = rows[rt * 16 + c16];
@@ -308,7 +333,17 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
     for (int ks = 0; ks < kKlKsteps; ++ks)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[ks]), __builtin_bit_cast(v8bf, qreg[ks]),
                                                      acc, 0, 0, 0);
-    // acc[i]: logit of row rt*16 + 4 g + i for this lane's head
+    v4f zc = {0.f, 0.f, 0.f, 0.f};
+    if (kScores) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0}
+                               : fp8x8_to_bf16(*(const uint2 *)((const uint8_t *)a.k_idx + row * 128 + ks * 32 + 8 * g));
+        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
+                                                    zc, 0, 0, 0);
+      }
+    }
+    // acc[i]: logit of row rt*16 + 4 g + i for this lane's head; zc[i]: its z
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = rt * 16 + 4 * g + i;
@@ -318,6 +353,14 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
       e += __shfl_xor(e, 4);
       e += __shfl_xor(e, 8);
       if (c16 == 0) part[wave][j] = e;
+      if (kScores) {
+        float sc = fmaxf(zc[i], 0.0f) * w_h;
+        sc += __shfl_xor(sc, 1);
+        sc += __shfl_xor(sc, 2);
+        sc += __shfl_xor(sc, 4);
+        sc += __shfl_xor(sc, 8);
+        if (c16 == 0) spart[wave][j] = sc;
+      }
     }
   }
   __syncthreads();
@@ -326,6 +369,12 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
 #pragma unroll
     for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
     a.mass[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? m : 0.0f;
+    if (kScores) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kKlThreads / 64; ++w) sc += spart[w][tid];
+      a.score[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? sc + 0.0f : -INFINITY;
+    }
   }
 }
 
@@ -380,6 +429,9 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_loss(KlArgs a) {
   if (threadIdx.x == 0) a.loss[t] = mx > -INFINITY ? loss : 0.0f;
 }
 
+// kMfmaZ (64 FP8 index heads x 128 dims): z by bf16 MFMA as in
+// k_kl_mass_mfma, wave w taking index heads 16 w .. 16 w + 15
+template <bool kMfmaZ>
 __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // rows of qi and kr are padded by four words: 16-byte aligned, and the z
@@ -416,8 +468,33 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     for (int e = 0; e < 8; ++e) kr[j * ld + d + e] = v[e];
   }
   __syncthreads();
-  // z of (row j, index head h) for 4 threads per row
-  {
+  if (kMfmaZ) {
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+    const int h = wave * 16 + c16;
+    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + h) * 128;
+    v4i qireg[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+#pragma unroll
+    for (int rt = 0; rt < kKlRows / 16; ++rt) {
+      const int64_t row = rows[rt * 16 + c16];
+      v4f zc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0}
+                               : fp8x8_to_bf16(*(const uint2 *)((const uint8_t *)a.k_idx + row * 128 + ks * 32 + 8 * g));
+        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
+                                                    zc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = rt * 16 + 4 * g + i;
+        gz[j * 64 + h] = zc[i] > 0.0f ? gr[j] * wsh[h] : 0.0f;
+        rz[j * 64 + h] = gr[j] * fmaxf(zc[i], 0.0f);
+      }
+    }
+  } else {
+    // z of (row j, index head h) for 4 threads per row
     const int j = tid >> 2, hg = tid & 3;
     for (int h = hg; h < a.HI; h += 4) {
       float z = 0.0f;
@@ -526,20 +603,27 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
                               160 * 1024);
     (void)hipFuncSetAttribute((const void *)k_kl_rows<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    (void)hipFuncSetAttribute((const void *)k_kl_backward, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void *)k_kl_backward<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_kl_backward<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipGetLastError();
     attr = true;
   }
   const dim3 grid(a.chunks, T);
-  if (mfma) {
-    hipLaunchKernelGGL(k_kl_mass_mfma, grid, dim3(kKlThreads), 0, s, a);
+  if (mfma && HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN) {
+    hipLaunchKernelGGL(k_kl_mass_mfma<true>, grid, dim3(kKlThreads), 0, s, a);
+  } else if (mfma) {
+    hipLaunchKernelGGL(k_kl_mass_mfma<false>, grid, dim3(kKlThreads), 0, s, a);
     hipLaunchKernelGGL(k_kl_rows<false>, grid, dim3(kKlThreads), ((size_t)HI * kl_ld(DI) + 64) * 4, s, a);
   } else {
     hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
   }
   hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
-  hipLaunchKernelGGL(k_kl_backward, grid, dim3(kKlThreads), smem, s, a);
+  if (HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN)
+    hipLaunchKernelGGL(k_kl_backward<true>, grid, dim3(kKlThreads), smem, s, a);
+  else
+    hipLaunchKernelGGL(k_kl_backward<false>, grid, dim3(kKlThreads), smem, s, a);
   hipLaunchKernelGGL(k_kl_reduce, dim3((HI * DI + HI + kKlThreads - 1) / kKlThreads, T), dim3(kKlThreads), 0, s,
                      a);
   return hipGetLastError();
