@@ -23,11 +23,12 @@
 //                   products from q in LDS);
 //   k_kl_loss       one workgroup per query: the two normalisations, the loss
 //                   and g;
-//   k_kl_backward   one workgroup per (64 rows, query): z again (bf16 MFMA for
-//                   FP8 index tensors), d_kI by fp32 atomics, and per-chunk
-//                   partials of d_w and d_qI;
+//   k_kl_backward   one workgroup per (64 rows, query): z again and the
+//                   gradient products (bf16 and fp32 MFMA for 64 x 128 FP8
+//                   index tensors), d_kI by fp32 atomics, per-chunk partials
+//                   of d_w and d_qI;
 //   k_kl_reduce     sums the partials over the chunks (fixed order).
-// Everything after the logits is fp32 on the vector ALUs.
+// The softmax, loss and reductions are fp32 on the vector ALUs.
 
 #include "kernels.h"
 
@@ -93,6 +94,7 @@ __device__ __forceinline__ int64_t sel_row(const KlArgs &a, int t, int r, int n,
 }
 
 constexpr int kKlBatch = 4;
+constexpr int kGzLd = 65;  // LDS row stride of the backward's g-weighted masks (odd: no bank conflicts)
 
 // LDS row stride (in dwords) of a table read by four threads of different
 // rows at once (the 4 head groups of k_kl_rows): congruent to 4 mod 64, so
@@ -440,8 +442,8 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   float *qi = (float *)smem;                 // [HI, DI + 1]
   float *wsh = qi + a.HI * ld;               // [64]
   float *kr = wsh + 64;                      // [kKlRows, DI + 1] selected index keys
-  float *gz = kr + kKlRows * ld;             // [kKlRows, 64]: g w [z > 0]
-  float *rz = gz + kKlRows * 64;             // [kKlRows, 64]: g ReLU(z)
+  float *gz = kr + kKlRows * ld;             // [kKlRows, kGzLd]: g w [z > 0]
+  float *rz = gz + kKlRows * kGzLd;          // [kKlRows, kGzLd]: g ReLU(z)
   __shared__ float gr[kKlRows];
   __shared__ int64_t rows[kKlRows];
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
@@ -489,8 +491,8 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = rt * 16 + 4 * g + i;
-        gz[j * 64 + h] = zc[i] > 0.0f ? gr[j] * wsh[h] : 0.0f;
-        rz[j * 64 + h] = gr[j] * fmaxf(zc[i], 0.0f);
+        gz[j * kGzLd + h] = zc[i] > 0.0f ? gr[j] * wsh[h] : 0.0f;
+        rz[j * kGzLd + h] = gr[j] * fmaxf(zc[i], 0.0f);
       }
     }
   } else {
@@ -502,23 +504,55 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
         const float4 x = *(const float4 *)(qi + h * ld + d), y = *(const float4 *)(kr + j * ld + d);
         z = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, z))));
       }
-      gz[j * 64 + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
-      rz[j * 64 + h] = gr[j] * fmaxf(z, 0.0f);
+      gz[j * kGzLd + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
+      rz[j * kGzLd + h] = gr[j] * fmaxf(z, 0.0f);
     }
   }
   __syncthreads();
   const size_t chunk = (size_t)t * a.chunks + blockIdx.x;
   for (int h = tid; h < a.HI; h += kKlThreads) {
     float s = 0.0f;
-    for (int j = 0; j < kKlRows; ++j) s += rz[j * 64 + h];
+    for (int j = 0; j < kKlRows; ++j) s += rz[j * kGzLd + h];
     a.part_w[chunk * a.HI + h] = s;
+  }
+  if (kMfmaZ) {
+    // 64 x 128 shapes: both gradient products by fp32 MFMA 16x16x4 (fp32
+    // operands, as g is too small for bf16 at this precision). Wave w takes
+    // index-head tile w of d_qI = gz^T kr and row tile w of d_kI = gz qi,
+    // each over the 8 tiles of 16 d.
+    const int lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, c16 = lane & 15;
+    v4f accq[8], acck[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) accq[dt] = acck[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ks = 0; ks < 16; ++ks) {
+      const int kk = ks * 4 + g4;  // row (d_qI) or index head (d_kI) of this lane's k
+      const float aq = gz[kk * kGzLd + wave * 16 + c16];          // A[i = head][k = row]
+      const float ak = gz[(wave * 16 + c16) * kGzLd + kk];        // A[i = row][k = head]
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        accq[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, kr[kk * ld + dt * 16 + c16], accq[dt], 0, 0, 0);
+        acck[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, qi[kk * ld + dt * 16 + c16], acck[dt], 0, 0, 0);
+      }
+    }
+    // C[i = 4 g4 + r][j = c16] of each tile
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g4 + r, d = dt * 16 + c16;
+        a.part_q[chunk * 64 * 128 + (size_t)(wave * 16 + i) * 128 + d] = accq[dt][r];
+        const int j = wave * 16 + i;
+        if (rows[j] >= 0 && gr[j] != 0.0f) atomicAdd(a.d_k_idx + rows[j] * 128 + d, acck[dt][r]);
+      }
+    return;
   }
   // four consecutive outputs per thread (16-byte LDS reads)
   for (int i = 4 * tid; i < a.HI * a.DI; i += 4 * kKlThreads) {
     const int h = i / a.DI, d = i % a.DI;
     float4 s = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < kKlRows; ++j) {
-      const float gv = gz[j * 64 + h];
+      const float gv = gz[j * kGzLd + h];
       const float4 x = *(const float4 *)(kr + j * ld + d);
       s.x = fmaf(gv, x.x, s.x); s.y = fmaf(gv, x.y, s.y); s.z = fmaf(gv, x.z, s.z); s.w = fmaf(gv, x.w, s.w);
     }
@@ -529,7 +563,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     if (rows[j] < 0 || gr[j] == 0.0f) continue;
     float4 s = {0.f, 0.f, 0.f, 0.f};
     for (int h = 0; h < a.HI; ++h) {
-      const float gv = gz[j * 64 + h];
+      const float gv = gz[j * kGzLd + h];
       const float4 x = *(const float4 *)(qi + h * ld + d);
       s.x = fmaf(gv, x.x, s.x); s.y = fmaf(gv, x.y, s.y); s.z = fmaf(gv, x.z, s.z); s.w = fmaf(gv, x.w, s.w);
     }
@@ -567,7 +601,7 @@ size_t indexer_kl_ws_bytes(int T, int k, int HI, int DI) {
 
 size_t indexer_kl_smem(int H, int D, int HI, int DI, int q_dtype) {
   const size_t rows = ((size_t)HI * kl_ld(DI) + 64) * 4 + (size_t)H * kl_ld(q_dtype == SGA_BF16 ? D / 2 : D) * 4;
-  const size_t back = ((size_t)HI * (DI + 4) + 64 + (size_t)kKlRows * (DI + 4) + 2 * kKlRows * 64) * 4;
+  const size_t back = ((size_t)HI * (DI + 4) + 64 + (size_t)kKlRows * (DI + 4) + 2 * kKlRows * kGzLd) * 4;
   return rows > back ? rows : back;
 }
 
