@@ -327,7 +327,7 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     // ntiles read the zero block, so every thread issues the same number of
     // copies a tile). bf16: rows land swizzled in their tile; MXFP8: the raw
     // 576-byte rows land in order (36 chunks each) and are expanded below.
-    auto issue_tile = [&](int tt) {
+    auto issue_tile = [&](const int32_t *rrows, int ntiles, int tt) {
       if (!kMx) {
         unsigned char *tbase = smem + tt * kTileBytes;
         int64_t gr[kBfDma];
@@ -362,9 +362,10 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
       }
     };
     // both tiles of the set at once: with 8 waves issuing, the gather runs near
-    // the random-row rate of the memory system
-    issue_tile(set);
-    issue_tile(set + 2);
+    // the random-row rate of the memory system. From the second round on, tile
+    // `set` was requested during the previous round (see below).
+    if (rd == 0) issue_tile(rrows, ntiles, set);
+    issue_tile(rrows, ntiles, set + 2);
     if (kMx) {
   #pragma unroll
       for (int j = 0; j < kSclPer; ++j) {
@@ -377,6 +378,13 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     for (int u = 0; u < 2; ++u) {
       if (u == 0) wait_vmcnt<kMx ? kMxDma : kBfDma>(); else wait_vmcnt<0>();
       barrier_lds();  // tiles 2u and 2u + 1 have landed (MXFP8: and the scales; u = 1: the set's expanded tile is free)
+      if (u == 1 && rd + 1 < rounds) {
+        // every wave is past tile `set` of this round (its reads, and for
+        // MXFP8 its expansion, came before this barrier): the next round's
+        // tile `set` is requested now and lands during this tile's arithmetic
+        const int32_t *nrows_ = rows + (rd + 1) * kMlaRowsPerSplit;
+        issue_tile(nrows_, (min(kMlaRowsPerSplit, nrows - (rd + 1) * kMlaRowsPerSplit) + kTile - 1) / kTile, set);
+      }
       const int tt = set + 2 * u;
       const unsigned char *tile = smem + tt * kTileBytes;
       if (kMx) {
