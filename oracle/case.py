@@ -31,14 +31,18 @@ def _dec(t, dtype: str, scales=None) -> np.ndarray:
 
 def cache_rows(case, b: int, positions: np.ndarray, kv_start: np.ndarray, table) -> np.ndarray:
     """Cache rows of positions of sequence b: kv_start[b] + s, or, in the paged
-    layout, table[b, s // P] * P + s % P, where a page id outside the cache
-    stands for page 0."""
+    layout, table[b, s // P] * P + s % P.
+
+    A page id outside the cache has no defined meaning (the library leaves
+    the result of such a query unspecified), so the oracle refuses it.
+    """
     positions = np.asarray(positions, dtype=np.int64)
     if not case.page_size:
         return int(kv_start[b]) + positions
     P = int(case.page_size)
     pg = table[b, positions // P].astype(np.int64)
-    pg = np.where((pg < 0) | (pg >= case.num_kv_rows // P), 0, pg)
+    if np.any((pg < 0) | (pg >= case.num_kv_rows // P)):
+        raise ValueError(f"sequence {b}: a page id outside the cache; the result is undefined")
     return pg * P + positions % P
 
 

@@ -1,11 +1,11 @@
-"""Indexer KL loss over the sparse top-k selection, and its gradients (oracle side).
+"""Indexer KL loss restricted to the sparse selection, and its gradients (oracle side).
 
 Test infrastructure only: see the package docstring.
 
-Sources: "A.X K2 Technical Report", section 3.4 (Stage 3C: the indexer is
-trained with a KL-divergence loss that aligns its selection scores with the
-attention distribution; the loss is computed over the sparse top-k selection
-from the start, a "sparse warmup"); "A.X-K2: a sparse-attention upgrade that
+Sources: "A.X K2 Technical Report", section 3.4 (Stage 3C: the indexer
+learns from a KL objective that pulls its scores toward the attention
+weights, evaluated only on the sparse selection right from the beginning of
+that stage); "A.X-K2: a sparse-attention upgrade that
 costs nothing, trained natively in FP8", section "Sparse Gated Attention"
 (the indexer imitates the already gated attention distribution). The pages
 give no formula. Readings, following the published form of the indexer

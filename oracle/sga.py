@@ -15,8 +15,8 @@ Sources (page title, then section):
 * [AK2-CARD] "A.X-K2" model card, sections "Sparse Gated Attention (SGA)" and
   "Model Details".
 * [AK2-TR] "A.X K2 Technical Report": section 2 (architecture: MLA with a
-  head-specific output gate), section 3.4 (Stage 3C: an indexer that keeps the
-  top 2,048 tokens per query; YaRN with mscale 1.0) and the MXFP8 training
+  per-head output gate), section 3.4 (Stage 3C: an indexer whose selection
+  holds 2,048 positions per query; YaRN with mscale 1.0) and the MXFP8 training
   paragraph.
 
 Readings where the pages are silent (each is also listed in the design notes):
@@ -37,6 +37,8 @@ R9  the gate is elementwise over [head, latent channel], applied to the
     latent-space output before any up/output projection.
 R10 index lists are ascending positions (the output does not depend on order).
 R11 a query with no candidates outputs y = 0 and lse = -inf.
+R15 in the selection a NaN score ranks above every number (+inf included);
+    NaNs tie with each other, so the lower position wins among them.
 """
 
 from __future__ import annotations
@@ -99,12 +101,14 @@ def to_fp32(scores: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# step 2: top-k selection  ([AK2-ART]: keep the top 2,048 tokens per query at
-# individual-token granularity; [AK2-TR] section 3.4; readings R4, R6, R10)
+# step 2: top-k selection  ([AK2-ART]: 2,048 single positions survive per
+# query, chosen one by one rather than in blocks; [AK2-TR] section 3.4; readings R4, R6, R10)
 # --------------------------------------------------------------------------
 def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
     """Positions of the k best scores, ordered by (score desc, position asc).
 
+    A NaN score ranks above every number, +inf included, and NaNs tie with
+    each other whatever their sign or payload (reading R15); -0 equals +0.
     Returns an int64 array of length k holding the chosen positions in
     ascending order, padded with -1 when fewer than k candidates exist.
     """
@@ -114,7 +118,10 @@ def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
         out[:n] = np.arange(n)
         return out
     pos = np.arange(n)
-    order = np.lexsort((pos, -scores.astype(np.float64)))  # last key is primary
+    s64 = scores.astype(np.float64)
+    nan = np.isnan(s64)
+    value = np.where(nan, 0.0, s64)
+    order = np.lexsort((pos, -value, ~nan))  # last key is primary: NaN class first
     out[:] = np.sort(order[:k])
     return out
 

@@ -135,3 +135,17 @@ def test_topk_special_cases():
     # -0.0 and +0.0 are the same score: the lower position wins the tie
     s2 = np.array([0.0, -0.0, 0.0], np.float32)[[1, 0, 2]]
     assert list(sga.select_topk(s2, 1)) == [0]
+
+
+def test_topk_nan_ranks_first_and_ties_by_position():
+    # R15: every NaN (either sign, any payload) ranks above +inf; NaNs tie with
+    # each other, so the lower position wins among them. Worked by hand.
+    neg_nan = np.array([0xFFC00001], dtype=np.uint32).view(np.float32)[0]
+    pos_nan = np.array([0x7FC00000], dtype=np.uint32).view(np.float32)[0]
+    s = np.array([1.0, neg_nan, np.inf, 3.0, pos_nan, -np.inf, neg_nan], np.float32)
+    assert list(sga.select_topk(s, 1)) == [1]
+    assert list(sga.select_topk(s, 2)) == [1, 4]
+    assert list(sga.select_topk(s, 3)) == [1, 4, 6]
+    assert list(sga.select_topk(s, 4)) == [1, 2, 4, 6]
+    assert list(sga.select_topk(s, 5)) == [1, 2, 3, 4, 6]
+    assert list(sga.select_topk(s, 6)) == [0, 1, 2, 3, 4, 6]

@@ -115,3 +115,68 @@ def test_case_level_kl_on_the_tiny_case():
     assert abs(r["loss"][1] - loss) < 1e-12 and np.allclose(r["dw"][1], dw) and np.allclose(r["dq_idx"][1], dq)
     # rows selected by both queries collect both contributions
     assert len(r["dk_idx"]) >= c.topk
+
+
+def _golden_case(layout):
+    """The hand-worked two-query case of tests/golden/kl_two_queries_shared_row.json
+    as a case object (contiguous or paged caches); cache rows that hold no
+    position carry other keys, so keying by the wrong row changes the result."""
+    import json
+    import os
+    from types import SimpleNamespace
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "kl_two_queries_shared_row.json")) as f:
+        gold = json.load(f)
+    c = gold["case"]
+    lay = c[layout]
+    rows = lay["rows_by_position"]
+    n_rows = lay["num_kv_rows"]
+    k_idx = torch.full((n_rows, c["index_dim"]), 5.0)
+    for pos, r in enumerate(rows):
+        k_idx[r] = torch.tensor(c["keys_by_position"][pos], dtype=torch.float32)
+    H, Dc, Dr = 2, 2, 1
+    case = SimpleNamespace(
+        num_q=2, q_seq=torch.zeros(2, dtype=torch.int32),
+        q_pos=torch.tensor([q["position"] for q in c["queries"]], dtype=torch.int32),
+        kv_start=torch.tensor([lay.get("kv_start", 0)], dtype=torch.int64),
+        kv_len=torch.tensor([3], dtype=torch.int32),
+        page_size=lay.get("page_size", 0),
+        block_table=torch.tensor([lay["block_table"]], dtype=torch.int32) if "block_table" in lay else None,
+        num_kv_rows=n_rows, idx_dtype="f32", idx_heads=c["index_heads"], idx_dim=c["index_dim"],
+        q_idx=torch.tensor([[q["q_idx"]] for q in c["queries"]], dtype=torch.float32),
+        w=torch.tensor([c["w"], c["w"]], dtype=torch.float32), k_idx=k_idx,
+        kv=torch.randn(n_rows, Dc + Dr, generator=torch.Generator().manual_seed(0)),
+        kv_dtype="f32", kv_scale=None, q=torch.zeros(2, H, Dc + Dr), q_dtype="f32",
+        heads=H, d_latent=Dc, d_rope=Dr, softmax_scale=1.0, topk=c["topk"])
+    return case, rows, gold["expected"]
+
+
+def test_kl_case_golden_two_queries_share_a_row():
+    # d_k_idx sums the contributions of every query that selects a cache row,
+    # keyed by the cache row (not the position), in both cache layouts
+    import math
+
+    from oracle import case as ocase
+
+    for layout in ("contiguous", "paged"):
+        case, rows, exp = _golden_case(layout)
+        assert abs(exp["tau"] - math.tanh(0.5)) < 1e-15
+        r = ocase.kl_queries(case)
+        assert np.allclose(r["loss"], exp["loss"], rtol=0, atol=1e-12), layout
+        assert np.allclose(r["dw"], exp["d_w"], rtol=0, atol=1e-12), layout
+        assert np.allclose(r["dq_idx"], exp["d_q_idx"], rtol=0, atol=1e-12), layout
+        want = {rows[int(p)]: np.array(v) for p, v in exp["d_k_by_position"].items()}
+        assert set(r["dk_idx"]) == set(want), (layout, sorted(r["dk_idx"]), sorted(want))
+        for row, v in want.items():
+            assert np.allclose(r["dk_idx"][row], v, rtol=0, atol=1e-12), (layout, row)
+
+
+def test_kl_case_refuses_page_ids_outside_the_cache():
+    import pytest
+
+    from oracle import case as ocase
+
+    case, _, _ = _golden_case("paged")
+    case.block_table[0, 1] = 4  # 8 rows in pages of 2: ids 0..3 exist
+    with pytest.raises(ValueError):
+        ocase.kl_queries(case)
