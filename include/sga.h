@@ -4,16 +4,16 @@
  *
  * SGA is the attention sublayer described on the A.X K2 pages:
  *   - "A.X-K2: a sparse-attention upgrade that costs nothing, trained natively
- *     in FP8", section "Sparse Gated Attention": a lightweight indexer scores
- *     every cached key, the top 2,048 tokens per query are kept at token
- *     granularity, MLA runs over exactly the selected rows KV[I_topk], and a
- *     learned head-specific gate scales the attention output before Wo;
+ *     in FP8", section "Sparse Gated Attention": a small indexer rates each
+ *     cached key, 2,048 single positions survive for each query (not
+ *     blocks), attention reads only those latent rows, and a per-head
+ *     learned gate multiplies the attention result ahead of Wo;
  *   - "SK Telecom Opens A.X K2: 688B Parameters and One Telling Benchmark",
  *     section "Sparse Gated Attention" and its block-diagram caption (indexer
  *     and top-k selector feed MLA; a sigmoid output gate);
  *   - "A.X K2 Technical Report", section 2 (MLA backbone with a head-specific
- *     output gate) and section 3.4 (Stage 3C: the indexer selects the top 2,048
- *     tokens per query).
+ *     output gate) and section 3.4 (Stage 3C: the indexer's selection holds
+ *     2,048 positions for each query).
  * The pages print no formula. The operations below implement these readings:
  *   scores  I[t,s] = sum_h w[t,h] * max(0, qI[t,h,:] . kI[s,:])   for s <= p_t
  *   select  S_t    = the k positions of largest I[t,.], ties to the lowest
@@ -128,9 +128,11 @@ typedef struct sga_problem {
  *     + s % page_size (the block table of a paged KV cache; the serving stack
  *     the pages deploy with keeps its cache this way). The sequence's length
  *     is clipped to max_pages * page_size. A page id outside
- *     [0, num_kv_rows / page_size) reads page 0 instead (the kernels stay
- *     inside the caches; the result for those positions is unspecified).
- *     The block table lives on the device and is not checked on the host.
+ *     [0, num_kv_rows / page_size) is an error the library does not detect:
+ *     the kernels still read only rows inside the caches, but the results
+ *     of every query of that sequence are unspecified. Queries of other
+ *     sequences are unaffected. The block table lives on the device and is
+ *     not checked on the host.
  */
 
 /* ABI version of the loaded library (SGA_ABI_VERSION). */
@@ -147,8 +149,8 @@ const char *sga_last_error(void);
 sga_status sga_workspace_size(const sga_problem *p, int op, size_t *bytes);
 
 /*
- * Indexer score pass (the pages' "lightweight indexer scores every cached
- * key"; see the header comment for sources).
+ * Indexer score pass: one score per (query, visible cached key); see the
+ * header comment for sources.
  *   q_idx  [T, HI, DI]   idx_dtype (SGA_F32 or SGA_FP8_E4M3FN)
  *   w      [T, HI]       fp32 per-(query, head) weights
  *   k_idx  [num_kv_rows, DI] idx_dtype, one key per cached token, shared by all
@@ -164,22 +166,25 @@ sga_status sga_index_scores(const sga_problem *p, const void *q_idx, const float
                             const void *k_idx, float *scores, void *stream);
 
 /*
- * Per-query top-k selection (the pages' selector: "keeps only the top 2,048
- * tokens per query, selected at individual-token granularity").
+ * Per-query top-k selection: the selector of the "Sparse Gated Attention"
+ * section keeps k = 2,048 single positions per query, chosen one by one
+ * rather than in blocks.
  *   scores   [T, max_kv_len] fp32, only s < n_t is read
  *   topk_idx [T, topk] int32 output: the selected positions within the
  *            sequence in ascending order; -1 fills the tail when n_t < topk.
  * Order: larger score first, ties to the lower position; -0.0 equals +0.0;
- * NaN orders above +inf. Exact (radix select on the fp32 bit pattern), so the
- * result is deterministic.
+ * every NaN (either sign) orders above +inf and ties with the other NaNs.
+ * Exact (radix select on the fp32 bit pattern), so the result is
+ * deterministic.
  */
 sga_status sga_topk_select(const sga_problem *p, const float *scores, int32_t *topk_idx,
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Sparse MLA over the selected latent rows plus the sigmoid output gate (the
- * pages' "MLA then runs exactly over the selected set"; "head-specific output
- * gate ... before the Wo projection").
+ * Sparse MLA over the selected latent rows plus the sigmoid output gate:
+ * attention reads only the chosen rows, and each head's output is scaled by
+ * its own gate ahead of the Wo projection ("Sparse Gated Attention" section;
+ * technical report section 2).
  *   q        [T, H, Dc + Dr]  q_dtype (absorbed query: latent part then rope part)
  *   kv       [num_kv_rows, Dc + Dr] kv_dtype, row = [c_s | kR_s]
  *   kv_scale [num_kv_rows, (Dc + Dr) / 32] E8M0 bytes for SGA_MXFP8_E4M3FN, else NULL
@@ -247,11 +252,11 @@ sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dt
 
 /*
  * Indexer KL loss and its gradients, the training side of the indexer ("A.X
- * K2 Technical Report" section 3.4: the indexer is trained with a KL loss
- * that aligns its scores with the attention distribution, over the sparse
- * top-k selection from the start; "A.X-K2: a sparse-attention upgrade that
- * costs nothing, trained natively in FP8", section "Sparse Gated
- * Attention"). For query t with the selected positions S_t of a forward pass:
+ * K2 Technical Report" section 3.4: a KL objective pulls the indexer's
+ * scores toward the attention weights, evaluated only on the sparse
+ * selection from the first step of that stage; "A.X-K2: a sparse-attention
+ * upgrade that costs nothing, trained natively in FP8", section "Sparse
+ * Gated Attention"). For query t with the selected positions S_t of a forward pass:
  *   target_s = sum_h exp(tau q[t,h] . kv[s] - lse[t,h]), normalised over S_t
  *   I_s      = sum_h w[t,h] max(0, q_idx[t,h] . k_idx[s])
  *   loss[t]  = sum_s target_s (log target_s - log softmax_S(I)_s)
@@ -267,8 +272,13 @@ sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dt
  * Shapes: H, HI <= 64, HI * DI <= 8192, Dc + Dr and DI multiples of 8, topk
  * <= 4096, q in LDS (H * (Dc + Dr) bf16 or fp32) within 96 KiB; q SGA_F32 or
  * SGA_BF16, kv SGA_F32, SGA_BF16 or SGA_MXFP8_E4M3FN, index SGA_F32 or
- * SGA_FP8_E4M3FN. Arithmetic: fp32 on the vector ALUs. Workspace:
- * sga_workspace_size(p, SGA_OP_INDEXER_KL).
+ * SGA_FP8_E4M3FN. Arithmetic: fp32 accumulation throughout. For 64 heads
+ * with bf16 q and 576-wide bf16 or MXFP8 rows, the attention logits q . kv
+ * run on bf16 MFMA (MXFP8 rows expanded exactly to bf16); with 64 x 128 FP8
+ * index tensors, z = q_idx . k_idx runs on bf16 MFMA too (E4M3FN values are
+ * exact in bf16) and the gradient products d_q_idx and d_k_idx on fp32 MFMA
+ * 16x16x4. Every other shape, and the softmax, loss and reductions, use the
+ * fp32 vector ALUs. Workspace: sga_workspace_size(p, SGA_OP_INDEXER_KL).
  */
 sga_status sga_indexer_kl(const sga_problem *p, const void *q_idx, const float *w,
                           const void *k_idx, const void *q, const void *kv,

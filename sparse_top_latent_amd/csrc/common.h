@@ -32,9 +32,11 @@ constexpr int kHist12Bins = 1024;
 constexpr int kTopkChunk = 4096;  // scores per top-k scan workgroup
 
 // fp32 score -> uint32 key whose unsigned order is the numeric order of the
-// scores; -0.0 maps to the key of +0.0 and NaN above +inf.
+// scores; -0.0 maps to the key of +0.0, and every NaN (either sign, any
+// payload) to the one top key, above +inf.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0xFFFFFFFFu;
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }

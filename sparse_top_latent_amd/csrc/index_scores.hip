@@ -3,7 +3,7 @@
 // Source: "A.X-K2: a sparse-attention upgrade that costs nothing, trained
 // natively in FP8", section "Sparse Gated Attention" (a lightweight indexer
 // scores every cached key for each query); "A.X-K2" model card, section
-// "Sparse Gated Attention (SGA)" (the indexer scores and ranks key-value
+// "Sparse Gated Attention (SGA)" (the indexer rates and orders the cached
 // candidates). The weighted-ReLU form is the reading this library implements.
 //
 // Three kernels (device helpers shared with the prefill kernel live in
@@ -322,8 +322,9 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
                             const uint8_t *k_idx, float *scores, int64_t stride, TopkWs *sel,
                             hipStream_t s) {
   if (T == 0 || m.max_kv_len == 0) return hipSuccess;
-  static bool attr = false;
-  if (!attr) {
+  // one-time set-up (a function-local static is initialised exactly once,
+  // also when several host threads arrive together)
+  static const bool attr = [] {
     // ring plus the largest score stage (64 tiles)
     const int max_smem = kIdxRing * kIdxStepBytes + (kIdxStageScores ? 64 * kIdxTileKeys * 4 : 0);
     (void)hipFuncSetAttribute((const void *)k_index_fp8<true, kIdxRing, false>,
@@ -335,8 +336,9 @@ hipError_t launch_index_fp8(const SeqMeta &m, int T, int k, const uint8_t *q_idx
     (void)hipFuncSetAttribute((const void *)k_index_fp8<false, kIdxRing, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, max_smem);
     (void)hipGetLastError();
-    attr = true;
-  }
+    return true;
+  }();
+  (void)attr;
   // many query rows per sequence: the query-tiled kernel (it also scores the
   // row groups that span a sequence boundary); the level-0 histogram then
   // comes from a separate pass over the scores

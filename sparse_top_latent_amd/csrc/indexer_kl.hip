@@ -1,4 +1,4 @@
-// Indexer KL loss over the sparse top-k selection and its gradients (the
+// Indexer KL loss restricted to the sparse selection, and its gradients (the
 // training side of the indexer, "A.X K2 Technical Report" section 3.4: a KL
 // loss aligns the indexer's scores with the attention distribution, computed
 // over the sparse selection from the start).
@@ -631,8 +631,9 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
   // the MI355X shapes take the attention mass from the MFMA kernel
   const bool mfma = H == 64 && q_dtype == SGA_BF16 && D == 32 * kKlKsteps &&
                     (kv_dtype == SGA_BF16 || kv_dtype == SGA_MXFP8_E4M3FN);
-  static bool attr = false;
-  if (!attr) {
+  // one-time set-up (a function-local static is initialised exactly once,
+  // also when several host threads arrive together)
+  static const bool attr = [] {
     (void)hipFuncSetAttribute((const void *)k_kl_rows<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipFuncSetAttribute((const void *)k_kl_rows<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -642,8 +643,9 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
     (void)hipFuncSetAttribute((const void *)k_kl_backward<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipGetLastError();
-    attr = true;
-  }
+    return true;
+  }();
+  (void)attr;
   const dim3 grid(a.chunks, T);
   if (mfma && HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN) {
     hipLaunchKernelGGL(k_kl_mass_mfma<true>, grid, dim3(kKlThreads), 0, s, a);

@@ -1,9 +1,30 @@
 // Host-side launchers of the SGA kernels (one translation unit per kernel family).
 #pragma once
 
+#include <atomic>
+
 #include "common.h"
 
 namespace sga {
+
+// Compute units of the current device, looked up once per device (safe to
+// call from several host threads: a race only repeats the lookup).
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+    (void)hipGetLastError();
+    c = 256;
+  }
+  cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
 
 // --- indexer score pass ----------------------------------------------------
 // scores[t * stride + s] for s < n_t.

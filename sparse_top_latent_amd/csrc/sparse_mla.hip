@@ -1,11 +1,11 @@
 // Sparse MLA over the selected latent rows, followed by the sigmoid output gate.
 //
 // Source: "A.X-K2: a sparse-attention upgrade that costs nothing, trained
-// natively in FP8", section "Sparse Gated Attention" (MLA runs exactly over the
-// selected set KV[I_topk]; a learned head-specific gate is applied to the
-// attention output before Wo); "SK Telecom Opens A.X K2: 688B Parameters and
-// One Telling Benchmark", block-diagram caption (sigmoid output gate); "A.X K2
-// Technical Report", section 2 (MLA backbone with a head-specific output gate).
+// natively in FP8", section "Sparse Gated Attention" (attention reads only the
+// chosen latent rows; a learned per-head gate multiplies the attention result
+// ahead of Wo); "SK Telecom Opens A.X K2: 688B Parameters and One Telling
+// Benchmark", block-diagram caption (sigmoid output gate); "A.X K2 Technical
+// Report", section 2 (the MLA backbone carries a per-head output gate).
 //
 // Absorbed MLA: all heads share one cached row [c_s | kR_s] per position, so a
 // gathered row serves every head. For query t and head h:
@@ -634,14 +634,7 @@ static int mla_splits(int k) { return (k + kMlaRowsPerSplit - 1) / kMlaRowsPerSp
 // More rounds mean fewer partials to write and combine, and no second wave of
 // workgroups waiting for a CU.
 static void mla_plan(int T, int k, int *R, int *S) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    (void)hipGetLastError();
-  }
+  const int cus = device_cu_count();
   int r = 1;
   while (r < kMaxRounds && (int64_t)T * ((k + r * kMlaRowsPerSplit - 1) / (r * kMlaRowsPerSplit)) > cus) r *= 2;
   *R = r;
@@ -659,23 +652,21 @@ bool mla_fuse_finish(int T, int k) {
   // (prefill: 4,096 queries x 4 splits, 0.35 ms more).
   int R, S;
   mla_plan(T, k, &R, &S);
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
-  (void)hipGetLastError();
-  return (int64_t)T * S <= cus;
+  return (int64_t)T * S <= device_cu_count();
 }
 
 template <bool kMx, int R, bool kFuse, bool kPaged>
 static void launch_split8(const MlaArgs &a, uint16_t *opart, float2 *ml, int S, hipStream_t s) {
-  static bool attr = false;
   const size_t smem = kMx ? kMx8Smem : kBfSmem;
-  if (!attr) {
+  // one-time set-up per instance (a function-local static is initialised
+  // exactly once, also when several host threads arrive together)
+  static const bool attr = [smem] {
     (void)hipFuncSetAttribute((const void *)k_mla_split8<kMx, R, kFuse, kPaged>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     (void)hipGetLastError();
-    attr = true;
-  }
+    return true;
+  }();
+  (void)attr;
   hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse, kPaged>), dim3(S, a.T), dim3(512), smem, s, a, opart, ml);
 }
 

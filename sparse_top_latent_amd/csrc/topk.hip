@@ -2,9 +2,9 @@
 // position, returned in ascending position order (-1 padding when n_t < k).
 //
 // Source: "A.X-K2: a sparse-attention upgrade that costs nothing, trained
-// natively in FP8", section "Sparse Gated Attention" (keep the top 2,048 tokens
-// per query, at individual-token granularity rather than in blocks); "A.X K2
-// Technical Report", section 3.4 (the indexer selects the top 2,048 tokens).
+// natively in FP8", section "Sparse Gated Attention" (2,048 single positions
+// survive per query, chosen one by one rather than in blocks); "A.X K2
+// Technical Report", section 3.4 (the indexer's selection size).
 //
 // Exact radix select on the order-preserving 32-bit key of each fp32 score,
 // most significant digit first (12 + 10 + 10 bits):

@@ -15,12 +15,16 @@ pytestmark = pytest.mark.gpu
 
 
 def _check_scores(case, queries=None):
-    got = run_scores(case).cpu().numpy()
+    # fp32 scores compared as bit patterns; only the compared rows leave the GPU
+    scores = run_scores(case)
     ref = ocase.run_queries(case, queries)
     assert all(ref["scores_exact"])
+    rows = torch.as_tensor(ref["queries"], device=scores.device)
+    got = scores.index_select(0, rows).cpu().numpy()
+    del scores
     for i, t in enumerate(ref["queries"]):
         r = ref["scores"][i]
-        g = got[t, : r.size]
+        g = got[i, : r.size]
         assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), \
             f"query {t}: {np.count_nonzero(g != r)} scores differ"
 
@@ -41,8 +45,22 @@ def test_index_scores_fp8_ragged():
 
 def test_index_scores_fp8_full_decode_b32_n32k():
     case = make_case("decode_b32_n32k", device="cuda")
-    say("case decode_b32_n32k index scores, 4 sampled queries")
-    _check_scores(case, [0, 7, 20, 31])
+    say("case decode_b32_n32k index scores, all 32 queries")
+    _check_scores(case)
+
+
+def test_index_scores_fp8_full_decode_b16_n128k():
+    case = make_case("decode_b16_n128k", device="cuda")
+    say("case decode_b16_n128k index scores, all 16 queries")
+    _check_scores(case)
+
+
+def test_index_scores_fp8_prefill_q4096_n128k_sampled():
+    # first and last rows of spread 8-row groups of the query-tiled kernel
+    case = make_case("prefill_q4096_n128k", device="cuda")
+    qs = [0, 7, 8, 1023, 1024, 2047, 2048, 3071, 3072, 4088, 4095]
+    say(f"case prefill_q4096_n128k index scores, {len(qs)} sampled queries")
+    _check_scores(case, qs)
 
 
 # --------------------------------------------------------------------------
@@ -171,3 +189,21 @@ def test_topk_threshold_deep_in_wide_histograms():
         rows.append(x.tolist())
     _check_topk(rows, 2048, "wide histograms, k ~ n/2 and below")
     _check_topk([r[:4100] for r in rows], 2048, "wide histograms, k = n/2")
+
+
+def test_topk_nan_ranks_above_inf_and_ties_by_position():
+    # every NaN, either sign and any payload, ranks above +inf; NaNs tie with
+    # each other (lower position first). Row 0: a few NaNs and infs among
+    # normal scores; row 1: more NaNs than k, so the selection is the first k
+    # NaN positions.
+    g = np.random.default_rng(7)
+    a = g.standard_normal(9000).astype(np.float32)
+    bits = a.view(np.uint32)
+    nan_pos = g.choice(9000, 60, replace=False)
+    bits[nan_pos] = np.where(np.arange(60) % 2 == 0, 0x7FC00000, 0xFFC00001) + np.arange(60, dtype=np.uint32)
+    a[g.choice(np.setdiff1d(np.arange(9000), nan_pos), 10, replace=False)] = np.inf
+    b = g.standard_normal(12000).astype(np.float32)
+    bb = b.view(np.uint32)
+    many = g.choice(12000, 3000, replace=False)
+    bb[many] = np.where(many % 3 == 0, 0xFF800001, 0x7F800005).astype(np.uint32)
+    _check_topk([a, b], 2048, "NaN scores")

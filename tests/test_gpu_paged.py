@@ -86,16 +86,24 @@ def test_paged_decode_b16_n128k_sampled():
 
 
 def test_paged_large_pages_and_bad_page_ids():
-    # pages larger than a workgroup's key range; then a block table with an id
-    # outside the cache: the kernels read page 0 for it (the oracle does the
-    # same) and every other query is unaffected
+    # pages larger than a workgroup's key range; then a block table with ids
+    # outside the cache for sequence 0. The results of sequence 0's query are
+    # unspecified (only: the run completes and its list names positions of
+    # the sequence); the queries of sequence 1 must be exactly what they are
+    # with a valid table, and match the oracle.
     lens = [40000, 70000]
     case = make_custom(lens, [(0, 39999), (1, 69999), (1, 5000)], dims=FULL_DIMS, precision="bf16",
                        seed=55, device="cuda")
     _check_paged(case, 8192, [0, 1, 2], "pages of 8192")
     paged = paged_copy(case, 1024, seed=3)
+    o0, i0, l0 = run_layer(paged)
     paged.block_table[0, 3] = 1 << 20
     paged.block_table[0, 5] = -2
     say("case paged: out-of-range page ids")
-    o, i, l = run_layer(paged)
-    compare_layer(paged, [0, 1, 2], out=o, idx=i, lse=l, label="bad page ids")
+    o1, i1, l1 = run_layer(paged)
+    _same(i0[1:], i1[1:], "top-k of sequence 1")
+    _same(o0[1:], o1[1:], "y of sequence 1")
+    _same(l0[1:], l1[1:], "lse of sequence 1")
+    sel = i1[0]
+    assert bool(torch.all((sel == -1) | ((sel >= 0) & (sel < lens[0]))))
+    compare_layer(paged, [1, 2], out=o1, idx=i1, lse=l1, label="sequence 1 beside bad page ids")
