@@ -78,31 +78,38 @@ def test_layer_decode_b32_n32k_all_queries():
     compare_layer(case, label="decode_b32_n32k")
 
 
-def test_layer_decode_b16_n128k_sampled_and_deterministic():
+def test_layer_decode_b16_n128k_all_queries_and_deterministic():
     case = make_case("decode_b16_n128k", device="cuda")
-    say("case layer decode_b16_n128k")
+    say("case layer decode_b16_n128k (all 16 queries)")
     out1, idx1, lse1 = run_layer(case)
     out2, idx2, _ = run_layer(case)
     assert torch.equal(idx1, idx2) and torch.equal(out1, out2)
-    compare_layer(case, [0, 5, 10, 15], out=out1, idx=idx1, lse=lse1, label="decode_b16_n128k")
+    compare_layer(case, out=out1, idx=idx1, lse=lse1, label="decode_b16_n128k")
 
 
-def test_layer_decode_b16_n128k_mq4_sampled():
+def test_layer_decode_b16_n128k_mq4_all_queries():
     # 4 queries per sequence at its last 4 positions share one index scan
     case = make_case("decode_b16_n128k_mq4", device="cuda")
-    say("case layer decode_b16_n128k_mq4")
-    compare_layer(case, [0, 1, 2, 3, 22, 63], label="decode_b16_n128k_mq4")
+    say("case layer decode_b16_n128k_mq4 (all 64 queries)")
+    compare_layer(case, label="decode_b16_n128k_mq4")
 
 
-def test_layer_varlen_mxfp8_b64_sampled():
+def test_layer_varlen_mxfp8_b64_all_queries():
     case = make_case("varlen_mxfp8_b64", device="cuda")
-    lens = np.array(case.lens)
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 3, 17, 40, 63})
-    say(f"case layer varlen_mxfp8_b64 queries {pick}")
-    compare_layer(case, pick, label="varlen_mxfp8_b64")
+    say("case layer varlen_mxfp8_b64 (all 64 queries)")
+    compare_layer(case, label="varlen_mxfp8_b64")
+
+
+def prefill_sample(T=4096, group=8, groups=34):
+    """The first and last query row of evenly spaced 8-row groups of the
+    prefill chunk (both chunk ends included)."""
+    g = np.unique(np.linspace(0, T // group - 1, groups).round().astype(int))
+    return sorted({int(x) for gi in g for x in (gi * group, gi * group + group - 1)})
 
 
 def test_layer_prefill_q4096_n128k_sampled():
     case = make_case("prefill_q4096_n128k", device="cuda")
-    say("case layer prefill_q4096_n128k")
-    compare_layer(case, [0, 1, 2048, 4095], label="prefill")
+    qs = prefill_sample()
+    assert len(qs) >= 64 and qs[0] == 0 and qs[-1] == 4095
+    say(f"case layer prefill_q4096_n128k ({len(qs)} sampled queries)")
+    compare_layer(case, qs, label="prefill")
