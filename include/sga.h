@@ -214,6 +214,27 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
                          void *stream);
 
 /*
+ * sga_layer_fwd without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. Arguments and results are those of
+ * sga_layer_fwd minus ws / ws_bytes. The workspace is the library's own
+ * static device buffer of SGA_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU that
+ * runs it, held until the process ends; the call allocates and frees no
+ * device memory. A problem whose sga_workspace_size(p, SGA_OP_LAYER) exceeds
+ * it returns SGA_ERR_WORKSPACE before any work is enqueued (16 x 128K and
+ * 32 x 32K decode batches with k = 2048 fit; use sga_layer_fwd for larger
+ * ones). Every call on one GPU shares that GPU's buffer: calls that overlap
+ * in time on one GPU (on different streams or host threads) race, and the
+ * caller must serialise them. Nothing in the buffer needs clearing between
+ * calls (every kernel writes what it later reads).
+ */
+#define SGA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sga_status sga_layer_fwd_noalloc(const sga_problem *p, const void *q_idx, const float *w,
+                                 const void *k_idx, const void *q, const void *kv,
+                                 const uint8_t *kv_scale, const void *gate, void *out,
+                                 int32_t *topk_idx_out, float *lse, void *stream);
+
+/*
  * Cache append: the step before the path in serving, which stores each new
  * token's latent row and index key in the caches' storage formats. MXFP8 is
  * the OCP microscaling FP8 that the A.X K2 Technical Report's FP8 section

@@ -21,6 +21,7 @@ from ._ffi import (  # noqa: F401
     SGA_FP8_E4M3FN,
     SGA_MXFP8_E4M3FN,
     SGA_OP_INDEX,
+    SGA_NOALLOC_SCRATCH_BYTES,
     SGA_OP_INDEXER_KL,
     SGA_OP_LAYER,
     SGA_OP_MLA,
@@ -206,6 +207,26 @@ def sga_layer_fwd(prob: Problem, q_idx, w, k_idx, q, kv, kv_scale, gate, out, to
         _ptr(topk_idx_out, "topk_idx_out", None, T * c.topk),
         pl,
         _ptr(ws, "ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def sga_layer_fwd_noalloc(prob: Problem, q_idx, w, k_idx, q, kv, kv_scale, gate, out,
+                          topk_idx_out=None, lse=None, stream=None) -> None:
+    """sga_layer_fwd on the library's static per-GPU scratch (no workspace
+    argument, no allocation); calls on one GPU must not overlap in time."""
+    c = prob.c
+    T, HI, DI = c.num_q, c.idx_heads, c.idx_dim
+    pq, pkv, psc, pg, po, pl = _mla_ptrs(c, q, kv, kv_scale, gate, out, lse)
+    if topk_idx_out is not None and topk_idx_out.dtype != torch.int32:
+        raise ValueError("topk_idx_out must be int32")
+    _ffi.check(lib().sga_layer_fwd_noalloc(
+        prob.ptr,
+        _ptr(q_idx, "q_idx", (c.idx_dtype,), T * HI * DI),
+        _ptr(w, "w", (SGA_F32,), T * HI),
+        _ptr(k_idx, "k_idx", (c.idx_dtype,), c.num_kv_rows * DI),
+        pq, pkv, psc, pg, po,
+        _ptr(topk_idx_out, "topk_idx_out", None, T * c.topk),
+        pl,
         _stream(stream)))
 
 

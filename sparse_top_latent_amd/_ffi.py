@@ -25,6 +25,7 @@ SGA_OP_TOPK = 1
 SGA_OP_MLA = 2
 SGA_OP_LAYER = 3
 SGA_OP_INDEXER_KL = 4
+SGA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/sga.h declares
 EXPORTS = (
@@ -36,6 +37,7 @@ EXPORTS = (
     "sga_topk_select",
     "sga_sparse_mla_fwd",
     "sga_layer_fwd",
+    "sga_layer_fwd_noalloc",
     "sga_cache_append",
     "sga_indexer_kl",
     "sga_profile_enable",
@@ -102,6 +104,7 @@ def load() -> ctypes.CDLL:
         "sga_topk_select": ([P, vp, vp, vp, sz, vp], ctypes.c_int),
         "sga_sparse_mla_fwd": ([P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "sga_layer_fwd": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "sga_layer_fwd_noalloc": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
         "sga_cache_append": ([P, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp],
                              ctypes.c_int),
         "sga_indexer_kl": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -278,6 +279,102 @@ sga_status run_mla(const MlaArgs &a, const Plan &plan, void *ws, hipStream_t s, 
   return launched(launch_mla_combine(a, ws, s), "sparse mla combine");
 }
 
+// Argument checks of sga_layer_fwd and its allocation-free variant; *need
+// receives the workspace bytes.
+sga_status layer_check(const sga_problem *p, const void *q_idx, const float *w, const void *k_idx,
+                       const void *q, const void *kv, const uint8_t *kv_scale, void *out, Plan *plan,
+                       size_t *need) {
+  SGA_TRY(plan_for(p, SGA_OP_LAYER, plan));
+  *need = 0;
+  if (p->num_q == 0) return SGA_OK;
+  if (!q || !kv || !out) return fail(SGA_ERR_INVALID_ARGUMENT, "q / kv / out is NULL");
+  if (p->max_kv_len > 0 && (!q_idx || !w || !k_idx))
+    return fail(SGA_ERR_INVALID_ARGUMENT, "q_idx / w / k_idx is NULL");
+  if (plan->mla == MlaPath::kMx && !kv_scale)
+    return fail(SGA_ERR_INVALID_ARGUMENT, "MXFP8 rows need kv_scale");
+  *need = ws_bytes(p, SGA_OP_LAYER, *plan);
+  return SGA_OK;
+}
+
+// The a1 -> a4 launch sequence of one layer call on workspace `ws` (already
+// checked to be large enough).
+sga_status layer_launch(const sga_problem *p, const Plan &plan, const void *q_idx, const float *w,
+                        const void *k_idx, const void *q, const void *kv, const uint8_t *kv_scale,
+                        const void *gate, void *out, int32_t *topk_idx_out, float *lse, void *ws,
+                        hipStream_t stream) {
+  hipStream_t s = stream;
+  const int T = p->num_q;
+  const int64_t stride = score_stride(p);
+  char *c = (char *)ws;
+  float *scores = (float *)c;
+  c += align256((size_t)T * stride * 4);
+  int32_t *idx = (int32_t *)c;
+  c += align256((size_t)T * p->topk * 4);
+  if (topk_idx_out) idx = topk_idx_out;
+  void *tws = c;
+  c += align256(topk_ws_bytes(T, p->max_kv_len));
+  void *mws = c;
+  const SeqMeta m = meta_of(p);
+  TopkWs tw = topk_ws_carve(tws, T, p->max_kv_len);
+  const bool prof = g_prof.used < g_prof.max_calls;
+
+  if (prof) prof_mark(s, 0);
+  SGA_TRY(run_index(p, plan, q_idx, w, k_idx, scores, stride, &tw, s));
+  if (prof) prof_mark(s, 1);
+  // The MI355X MLA path can do the top-k's last step itself (MlaArgs::fuse)
+  // when its grid fits the CUs at once: only the select kernel runs here,
+  // and the split kernel derives its rows from the select's candidates and
+  // writes topk_idx_out.
+  const bool fuse = plan.mla != MlaPath::kF32 && p->max_kv_len > p->topk && mla_fuse_finish(T, p->topk);
+  SGA_TRY(launched(launch_topk_select(m, T, p->topk, scores, stride, tw, idx, s, !fuse), "topk select"));
+  if (prof) prof_mark(s, 2);
+  MlaArgs a = mla_args(p, q, kv, kv_scale, idx, gate, out, lse);
+  if (fuse) {
+    a.fuse = true;
+    a.sel = tw;
+    a.topk_out = topk_idx_out;
+  }
+  SGA_TRY(run_mla(a, plan, mws, s, prof));
+  if (prof) {
+    prof_mark(s, 4);
+    ++g_prof.used;
+  }
+  return SGA_OK;
+}
+
+// --------------------------------------------------------------------------
+// static scratch of the allocation-free layer call
+// --------------------------------------------------------------------------
+// One buffer per GPU, part of this library's device code: the runtime places
+// it on each device that loads the library and keeps it until the process
+// ends. In host code the array's name is only a stand-in; its device address
+// comes from hipGetSymbolAddress, once per device with that device current,
+// and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = SGA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+sga_status scratch_device_ptr(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SGA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SGA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(SGA_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return SGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -375,54 +472,36 @@ sga_status sga_layer_fwd(const sga_problem *p, const void *q_idx, const float *w
                          void *stream) {
   try {
     Plan plan;
-    SGA_TRY(plan_for(p, SGA_OP_LAYER, &plan));
+    size_t need = 0;
+    SGA_TRY(layer_check(p, q_idx, w, k_idx, q, kv, kv_scale, out, &plan, &need));
     if (p->num_q == 0) return SGA_OK;
-    if (!q || !kv || !out) return fail(SGA_ERR_INVALID_ARGUMENT, "q / kv / out is NULL");
-    if (p->max_kv_len > 0 && (!q_idx || !w || !k_idx))
-      return fail(SGA_ERR_INVALID_ARGUMENT, "q_idx / w / k_idx is NULL");
-    if (plan.mla == MlaPath::kMx && !kv_scale)
-      return fail(SGA_ERR_INVALID_ARGUMENT, "MXFP8 rows need kv_scale");
-    const size_t need = ws_bytes(p, SGA_OP_LAYER, plan);
     if (!ws || ws_size < need)
       return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_size);
-    hipStream_t s = (hipStream_t)stream;
-    const int T = p->num_q;
-    const int64_t stride = score_stride(p);
-    char *c = (char *)ws;
-    float *scores = (float *)c;
-    c += align256((size_t)T * stride * 4);
-    int32_t *idx = (int32_t *)c;
-    c += align256((size_t)T * p->topk * 4);
-    if (topk_idx_out) idx = topk_idx_out;
-    void *tws = c;
-    c += align256(topk_ws_bytes(T, p->max_kv_len));
-    void *mws = c;
-    const SeqMeta m = meta_of(p);
-    TopkWs tw = topk_ws_carve(tws, T, p->max_kv_len);
-    const bool prof = g_prof.used < g_prof.max_calls;
+    return layer_launch(p, plan, q_idx, w, k_idx, q, kv, kv_scale, gate, out, topk_idx_out, lse, ws,
+                        (hipStream_t)stream);
+  } catch (...) {
+    return fail(SGA_ERR_DEVICE, "internal error");
+  }
+}
 
-    if (prof) prof_mark(s, 0);
-    SGA_TRY(run_index(p, plan, q_idx, w, k_idx, scores, stride, &tw, s));
-    if (prof) prof_mark(s, 1);
-    // The MI355X MLA path can do the top-k's last step itself (MlaArgs::fuse)
-    // when its grid fits the CUs at once: only the select kernel runs here,
-    // and the split kernel derives its rows from the select's candidates and
-    // writes topk_idx_out.
-    const bool fuse = plan.mla != MlaPath::kF32 && p->max_kv_len > p->topk && mla_fuse_finish(T, p->topk);
-    SGA_TRY(launched(launch_topk_select(m, T, p->topk, scores, stride, tw, idx, s, !fuse), "topk select"));
-    if (prof) prof_mark(s, 2);
-    MlaArgs a = mla_args(p, q, kv, kv_scale, idx, gate, out, lse);
-    if (fuse) {
-      a.fuse = true;
-      a.sel = tw;
-      a.topk_out = topk_idx_out;
-    }
-    SGA_TRY(run_mla(a, plan, mws, s, prof));
-    if (prof) {
-      prof_mark(s, 4);
-      ++g_prof.used;
-    }
-    return SGA_OK;
+sga_status sga_layer_fwd_noalloc(const sga_problem *p, const void *q_idx, const float *w,
+                                 const void *k_idx, const void *q, const void *kv,
+                                 const uint8_t *kv_scale, const void *gate, void *out,
+                                 int32_t *topk_idx_out, float *lse, void *stream) {
+  try {
+    Plan plan;
+    size_t need = 0;
+    SGA_TRY(layer_check(p, q_idx, w, k_idx, q, kv, kv_scale, out, &plan, &need));
+    if (p->num_q == 0) return SGA_OK;
+    if (need > kScratchBytes)
+      return fail(SGA_ERR_WORKSPACE,
+                  "this problem needs %zu bytes of workspace; the static scratch holds %zu "
+                  "(call sga_layer_fwd with a caller workspace instead)",
+                  need, kScratchBytes);
+    void *ws = nullptr;
+    SGA_TRY(scratch_device_ptr(&ws));
+    return layer_launch(p, plan, q_idx, w, k_idx, q, kv, kv_scale, gate, out, topk_idx_out, lse, ws,
+                        (hipStream_t)stream);
   } catch (...) {
     return fail(SGA_ERR_DEVICE, "internal error");
   }

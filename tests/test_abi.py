@@ -227,3 +227,23 @@ def test_indexer_kl_null_buffers_and_workspace(lib):
         a[i] = None
         assert lib.sga_indexer_kl(ctypes.byref(p), *a, FAKE, 1 << 40, None) == 1
     assert lib.sga_indexer_kl(ctypes.byref(p), *args, FAKE, 16, None) == 3
+
+
+def test_noalloc_layer_rejects_problems_beyond_its_scratch(lib):
+    # checked on the host before any HIP call: 64 queries at 128K need about
+    # 196 MiB of workspace, more than the 64 MiB static scratch
+    big = _problem(num_q=64)
+    _, need = _ws(lib, big, _ffi.SGA_OP_LAYER)
+    assert need > _ffi.SGA_NOALLOC_SCRATCH_BYTES
+    st = lib.sga_layer_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                   None, None, None)
+    assert st == 3 and b"static scratch" in lib.sga_last_error()
+    # the headline batch (16 x 128K) fits
+    _, need16 = _ws(lib, _problem(), _ffi.SGA_OP_LAYER)
+    assert need16 <= _ffi.SGA_NOALLOC_SCRATCH_BYTES
+    # argument errors come first, as in sga_layer_fwd
+    bad = _problem(reserved0=1)
+    assert lib.sga_layer_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                     None, None, None) == 1
+    assert lib.sga_layer_fwd_noalloc(ctypes.byref(_problem()), None, None, None, FAKE, FAKE, None,
+                                     None, FAKE, None, None, None) == 1
