@@ -6,7 +6,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsga.so")
+# the in-tree build; SGA_LIBRARY names another build of the same library
+# (for side-by-side measurements of build variants)
+LIB_PATH = os.environ.get("SGA_LIBRARY") or os.path.join(HERE, "libsga.so")
 
 SGA_OK = 0
 SGA_ERR_INVALID_ARGUMENT = 1

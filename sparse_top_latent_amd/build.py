@@ -67,21 +67,24 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, defines=()) -> str:
+    """Compile and link the library to `out`; `defines` are extra -D options
+    (build variants for side-by-side measurements)."""
     cc = hipcc()
-    objdir = os.path.join(HERE, "_build")
+    objdir = os.path.join(HERE, "_build") if out == LIB else out + ".objs"
     os.makedirs(objdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, "-c", *COMMON, *PER_FILE.get(os.path.basename(s), []), "-o", o, s],
+        futs = [ex.submit(_run, [cc, "-c", *COMMON, *[f"-D{d}" for d in defines],
+                                 *PER_FILE.get(os.path.basename(s), []), "-o", o, s],
                           verbose) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -241,6 +241,17 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   const int r0 = split * R * kMlaRowsPerSplit;
   const int nrows = min(R * kMlaRowsPerSplit, a.k - r0);  // >= 1
   const int rounds = (nrows + kMlaRowsPerSplit - 1) / kMlaRowsPerSplit;
+  // the query slice of this wave's 16 heads (B operands of S^T = rows . Q^T);
+  // with the fused top-k finish it is requested first, since it does not
+  // depend on the selection (elsewhere after the row lookup, which keeps the
+  // many-round instances clear of register spills)
+  const int head = hg * 16 + c16;
+  const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
+  v8bf qreg[kKsteps];
+  if (kFuse) {
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
+  }
   int64_t start;
   if (!kFuse) {
     // the selected positions are requested first (clamped, unconditional) so
@@ -277,11 +288,10 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     }
   }
   __syncthreads();  // rows[] ready
-  const int head = hg * 16 + c16;
-  const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
-  v8bf qreg[kKsteps];
+  if (!kFuse) {
 #pragma unroll
-  for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
+    for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
+  }
 
   // MXFP8: raw tiles at smem, the set's expanded bf16 tile after them, then
   // the scales of the round's 128 rows
