@@ -84,18 +84,22 @@ def index_source_sha(srcs=None):
     return h.hexdigest()
 
 
-def stream_read_gbs(torch, x, reps=5):
-    """Read bandwidth of a plain streaming reduction (torch sum) over x."""
-    v = x.view(torch.float32) if x.element_size() * x.numel() % 4 == 0 else x
-    v.sum()
+def stream_read_gbs(torch, sga, bufs, reps=10):
+    """Read bandwidth of the library's streaming-read reference (the decode
+    indexer's LDS-DMA copy pattern without the scoring) over the rotated
+    buffers `bufs`, timed with HIP events on the launch stream."""
+    sink = torch.empty((sga.lib().sga_stream_read_sink_words(),), dtype=torch.int32, device=bufs[0].device)
+    for b in bufs:
+        sga.sga_stream_read(b, sink)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
-        v.sum()
+    for i in range(reps):
+        sga.sga_stream_read(bufs[i % len(bufs)], sink)
     e1.record()
     torch.cuda.synchronize()
-    return x.element_size() * x.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    nbytes = bufs[0].numel() * bufs[0].element_size() // 8192 * 8192
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def host_subcase(case, queries):
@@ -142,6 +146,101 @@ def blas_threads():
         return 1
 
 
+def time_decode(args, case, prob, sga, torch, steps, warmup):
+    """Time `steps` sga_layer_fwd calls over the batch, then the same steps
+    eagerly with the library's per-phase HIP events.
+
+    The timed steps are replayed from one HIP graph of up to MAX_GRAPH_STEPS
+    consecutive steps (rotating over `args.copies` independent cache copies,
+    which keeps each step's caches out of the 256 MB Infinity Cache, as a
+    decode loop would run them back to back) plus one graph for a remainder,
+    so the graph launch cost is paid once per graph. (Measured on MI355X:
+    graphs of 3 to 48 steps run at 85.4 to 83.6 us per step, 12 steps and
+    more within 0.3 us of each other.)"""
+    dev = case.q.device
+    T, H, Dc = case.num_q, case.heads, case.d_latent
+    out = torch.empty((T, H, Dc), dtype=sga.out_torch_dtype(prob.c.out_dtype), device=dev)
+    ws = sga.workspace(prob, sga.SGA_OP_LAYER, device=dev)
+    copies = args.copies
+    kvs = [case.kv] + [case.kv.clone() for _ in range(copies - 1)]
+    kis = [case.k_idx] + [case.k_idx.clone() for _ in range(copies - 1)]
+    scs = [case.kv_scale] + ([case.kv_scale.clone() for _ in range(copies - 1)]
+                             if case.kv_scale is not None else [None] * (copies - 1))
+
+    def step(i):
+        c = i % copies
+        sga.sga_layer_fwd(prob, case.q_idx, case.w, kis[c], case.q, kvs[c], scs[c], case.gate,
+                          out, None, None, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    chunk = min(steps, MAX_GRAPH_STEPS - MAX_GRAPH_STEPS % copies)
+    plan = [(chunk, steps // chunk)] + ([(steps % chunk, 1)] if steps % chunk else [])
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for n, reps in plan:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    step(i)
+            graphs.append((g, reps))
+        for i in range(max(1, warmup // chunk)):
+            graphs[0][0].replay()
+        torch.cuda.synchronize()
+
+    # timed regions: exactly `steps` steps each, replayed from the graphs and
+    # launched eagerly (no events); the faster launch mode gives the result
+    def timed(run):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    def replay():
+        for g, reps in graphs:
+            for _ in range(reps):
+                g.replay()
+
+    def eager():
+        for i in range(steps):
+            step(i)
+
+    ms_graph = timed(replay) if graphs else None
+    ms_plain = timed(eager)
+    use_graph = ms_graph is not None and ms_graph <= ms_plain
+    ms_step = ms_graph if use_graph else ms_plain
+    qps = T * 1e3 / ms_step
+    del graphs
+
+    # per-kernel durations: the same steps launched eagerly with HIP events
+    # recorded by the library around each phase on the launch stream
+    sga.sga_profile_enable(steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t1) * 1e3 / steps
+    phase_ms, calls = sga.sga_profile_collect(4)
+    sga.sga_profile_enable(0)
+    phases = {n: round(v / max(calls, 1) * 1e3, 2) for n, v in
+              zip(("index_us", "topk_us", "mla_us", "combine_us"), phase_ms)}
+    return {"ms_step": ms_step, "qps": qps, "eager_ms": eager_ms, "phases": phases,
+            "idx_ms": phase_ms[0] / max(calls, 1), "kis": kis, "graphs": use_graph,
+            "ms_graph": ms_graph, "ms_plain": ms_plain,
+            "launch": (f"hip-graph ({' + '.join(f'{r} x {n}' for n, r in plan)} steps)" if use_graph
+                       else "eager launches")}
+
+
 def cpu_baseline(case, budget_s=15.0):
     """The oracle, as it stands, on host-resident queries of the same workload.
 
@@ -170,11 +269,53 @@ def cpu_baseline(case, budget_s=15.0):
         "value": round(done / t_used, 3),
         "unit": "queries/s",
         "cores": blas_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{done} query evaluations over the {T} queries of {case.name} through the whole path "
                    f"(exact scores, full-sort top-k, two-pass softmax MLA, gate) in float64, "
                    f"host-resident inputs, {t_used:.1f} s of oracle time"),
     }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_rate(case, budget_s, threads=None):
+    """Oracle queries/s over whole queries of `case` (bounded by budget_s
+    seconds of oracle time; at least one query), with BLAS limited to
+    `threads` threads when given."""
+    from oracle import case as ocase
+
+    def run():
+        done, t_used = 0, 0.0
+        for t in range(case.num_q):
+            sub = host_subcase(case, [t])
+            t0 = time.perf_counter()
+            ocase.run_queries(sub, keep_scores=False)
+            t_used += time.perf_counter() - t0
+            done += 1
+            if t_used >= budget_s:
+                break
+        return done, t_used
+
+    if threads is None:
+        done, t_used = run()
+        cores = blas_threads()
+    else:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=threads):
+            done, t_used = run()
+        cores = threads
+    return {"value": round(done / t_used, 3), "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {done} queries of {case.name} (whole path, float64), {t_used:.1f} s"}
 
 
 def indexer_flops(case):
@@ -185,26 +326,32 @@ def indexer_flops(case):
     return 2.0 * case.idx_heads * case.idx_dim * pairs, pairs
 
 
-def indexer_only(args, case, prob, sga, torch):
-    """The indexer score pass alone (the unit of the prefill target)."""
-    scores = torch.empty((case.num_q, case.max_kv_len), dtype=torch.float32, device="cuda")
-    kis = [case.k_idx] + [case.k_idx.clone() for _ in range(args.copies - 1)]
+def time_indexer(case, prob, sga, torch, steps, warmup, copies):
+    """Average milliseconds of one sga_index_scores pass over the batch (HIP
+    events around `steps` passes, index caches rotated over `copies`), and the
+    wall time of the timed region."""
+    scores = torch.empty((case.num_q, case.max_kv_len), dtype=torch.float32, device=case.q.device)
+    kis = [case.k_idx] + [case.k_idx.clone() for _ in range(copies - 1)]
 
     def step(i):
-        sga.sga_index_scores(prob, case.q_idx, case.w, kis[i % args.copies], scores)
+        sga.sga_index_scores(prob, case.q_idx, case.w, kis[i % copies], scores)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     ev1.record()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+
+
+def indexer_only(args, case, prob, sga, torch):
+    """The indexer score pass alone (the unit of the prefill target)."""
+    ms, elapsed = time_indexer(case, prob, sga, torch, args.steps, args.warmup, args.copies)
     flops, pairs = indexer_flops(case)
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] indexer {case.name}: {ms * 1e3:.1f} us per pass, {tflops:.0f} TFLOP/s "
@@ -311,7 +458,19 @@ def cache_append_bench(args, torch, sga):
     }), flush=True)
 
 
-FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 (vector and MFMA), published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def indexer_kl_split(case, k):
+    """(bf16 MFMA FLOPs, fp32 FLOPs) of one sga_indexer_kl call on the MI355X
+    shapes: the attention logits (2 H D per selected row) and the index scores
+    z in the forward and again in the backward (2 x 2 HI DI) run on bf16 MFMA;
+    the three gradient products (d_q_idx and d_k_idx on fp32 MFMA, d_w on the
+    vector ALUs; 3 x 2 HI DI) in fp32."""
+    rows = case.num_q * k
+    D, H, HI, DI = case.d_qk, case.heads, case.idx_heads, case.idx_dim
+    return rows * (2.0 * H * D + 4.0 * HI * DI), rows * 6.0 * HI * DI
 
 
 def indexer_kl_flops(case, k):
@@ -356,8 +515,17 @@ def indexer_kl_bench(args, case, prob, sga, torch):
     ms = ev0.elapsed_time(ev1) / args.steps
     flops = indexer_kl_flops(case, case.topk)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] indexer KL {case.name}: {ms * 1e3:.1f} us per call, {tflops:.1f} TFLOP/s "
-        f"({tflops / FP32_PEAK_TFLOPS:.1%} of the fp32 vector peak)")
+    # mixed-rate compute bound: each part of the work at the peak of the unit
+    # it runs on (bf16 MFMA 2.5 PFLOP/s, fp32 157.3 TFLOP/s)
+    f_bf16, f_fp32 = indexer_kl_split(case, case.topk)
+    ideal_ms = (f_bf16 / (BF16_PEAK_TFLOPS * 1e12) + f_fp32 / (FP32_PEAK_TFLOPS * 1e12)) * 1e3
+    mixed_peak = flops / (ideal_ms * 1e-3) / 1e12
+    kl_roofline = {"bound": "mfma", "kernel": "indexer KL (5 kernels, per call)", "achieved": round(tflops, 2),
+                   "peak": round(mixed_peak, 1), "unit": "TFLOP/s", "frac": round(tflops / mixed_peak, 4),
+                   "flops_per_launch": flops, "bf16_mfma_flops": f_bf16, "fp32_flops": f_fp32,
+                   "ideal_us": round(ideal_ms * 1e3, 2), "traffic": None}
+    log(f"[bench] indexer KL {case.name}: {ms * 1e3:.1f} us per call, {tflops:.1f} TFLOP/s, "
+        f"{tflops / mixed_peak:.1%} of the mixed bf16/fp32 rate ({ideal_ms * 1e3:.1f} us ideal)")
     base = None
     if not args.no_cpu_baseline:
         from oracle import case as ocase
@@ -377,9 +545,7 @@ def indexer_kl_bench(args, case, prob, sga, torch):
         "data": "synthetic",
         "config": {"workload": case.name, "queries": T, "topk": case.topk, "heads": H, "idx_heads": HI,
                    "idx_dim": DI},
-        "roofline": {"bound": "alu", "kernel": "indexer KL (4 kernels, per call)", "achieved": round(tflops, 2),
-                     "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
-                     "flops_per_launch": flops, "traffic": None},
+        "roofline": kl_roofline,
         "cpu_baseline": base,
     }), flush=True)
 
@@ -416,6 +582,8 @@ def main():
     ap.add_argument("--workload", default="decode_b16_n128k")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other configurations measured after the headline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--indexer-only", action="store_true",
                     help="time only sga_index_scores (reported in TFLOP/s against the FP8 MFMA peak)")
@@ -458,88 +626,22 @@ def main():
         return indexer_only(args, case, prob, sga, torch)
     if args.indexer_kl:
         return indexer_kl_bench(args, case, prob, sga, torch)
-    out = torch.empty((T, H, Dc), dtype=sga.out_torch_dtype(prob.c.out_dtype), device=dev)
-    ws = sga.workspace(prob, sga.SGA_OP_LAYER, device=dev)
-    # independent cache copies, rotated per step (defeats the 256 MB MALL)
-    kvs = [case.kv] + [case.kv.clone() for _ in range(args.copies - 1)]
-    kis = [case.k_idx] + [case.k_idx.clone() for _ in range(args.copies - 1)]
-    scs = [case.kv_scale] + ([case.kv_scale.clone() for _ in range(args.copies - 1)]
-                             if case.kv_scale is not None else [None] * (args.copies - 1))
-
-    def step(i):
-        c = i % args.copies
-        sga.sga_layer_fwd(prob, case.q_idx, case.w, kis[c], case.q, kvs[c], scs[c], case.gate,
-                          out, None, None, ws)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # HIP graphs: a decode step is a fixed chain of four launches. The timed
-    # steps are replayed from one graph of up to MAX_GRAPH_STEPS consecutive
-    # steps (rotating over the cache copies, as a decode loop would run them
-    # back to back) plus one graph for a remainder, so the graph launch cost is
-    # paid once per graph. (Measured on MI355X: graphs of 3 to 48 steps run at
-    # 85.4 to 83.6 us per step, 12 steps and more within 0.3 us of each other.)
-    graphs = []
-    chunk = min(args.steps, MAX_GRAPH_STEPS - MAX_GRAPH_STEPS % args.copies)
-    plan = [(chunk, args.steps // chunk)] + ([(args.steps % chunk, 1)] if args.steps % chunk else [])
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for c in range(args.copies):
-                step(c)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        for n, reps in plan:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(n):
-                    step(i)
-            graphs.append((g, reps))
-        for i in range(max(1, args.warmup // chunk)):
-            graphs[0][0].replay()
-        torch.cuda.synchronize()
-
-    # timed region: exactly `steps` steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if graphs:
-        for g, reps in graphs:
-            for _ in range(reps):
-                g.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    qps = T * args.steps / elapsed
-
-    # per-kernel durations: the same steps launched eagerly with HIP events
-    # recorded by the library around each phase on the launch stream
-    sga.sga_profile_enable(args.steps)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t1) * 1e3 / args.steps
-    phase_ms, calls = sga.sga_profile_collect(4)
-    sga.sga_profile_enable(0)
+    r = time_decode(args, case, prob, sga, torch, args.steps, args.warmup)
+    ms_step, qps, eager_ms, phases, idx_ms, kis = (r[k] for k in ("ms_step", "qps", "eager_ms", "phases",
+                                                                 "idx_ms", "kis"))
+    graphs, launch, r_ms_graph, r_ms_plain = r["graphs"], r["launch"], r["ms_graph"], r["ms_plain"]
     total_bytes, index_bytes = algorithmic_bytes(case)
-    idx_ms = phase_ms[0] / max(calls, 1)
     achieved = index_bytes / (idx_ms * 1e-3) / 1e9
     step_gbs = total_bytes / (ms_step * 1e-3) / 1e9
-    phases = {n: round(v / max(calls, 1) * 1e3, 2) for n, v in
-              zip(("index_us", "topk_us", "mla_us", "combine_us"), phase_ms)}
-    log(f"[bench] {ms_step * 1e3:.1f} us/step ({'graph' if graphs else 'eager'}), eager {eager_ms * 1e3:.1f} us/step, "
+    log(f"[bench] {ms_step * 1e3:.1f} us/step ({launch}; graph "
+        f"{'-' if r_ms_graph is None else f'{r_ms_graph * 1e3:.1f}'}, eager {r_ms_plain * 1e3:.1f}, "
+        f"eager with phase events {eager_ms * 1e3:.1f} us/step), "
         f"{qps:,.0f} queries/s, step {step_gbs:,.0f} GB/s of per-query bytes ({step_gbs / HBM_PEAK_GBS:.1%} of HBM), "
         f"phases {phases}")
-    stream_gbs = stream_read_gbs(torch, kvs[1 % args.copies])
-    log(f"[bench] index kernel {achieved:,.0f} GB/s; plain streaming read (torch sum over "
-        f"{kvs[0].numel() * kvs[0].element_size() / 1e9:.2f} GB) {stream_gbs:,.0f} GB/s")
+    stream_gbs = stream_read_gbs(torch, sga, kis)
+    log(f"[bench] index kernel {achieved:,.0f} GB/s; the library's streaming-read reference over "
+        f"{kis[0].numel() / 1e6:.0f} MB index caches {stream_gbs:,.0f} GB/s")
+    del r, kis
     rec = traffic_record(args.workload) if not args.page_size else None
     # Several queries per sequence share the scan of its index keys. With few
     # of them (multi-query decode) the index pass stays HBM-bound; with many
@@ -584,8 +686,10 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8+bf16",
         "data": "synthetic",
-        "launch": (f"hip-graph ({' + '.join(f'{r} x {n}' for n, r in plan)} steps)" if graphs else "eager"),
-        "eager_ms_per_step": round(eager_ms, 5),
+        "launch": launch,
+        "ms_per_step_by_launch": {"hip_graph": None if r_ms_graph is None else round(r_ms_graph, 5),
+                                  "eager": round(r_ms_plain, 5),
+                                  "eager_with_phase_events": round(eager_ms, 5)},
         "config": {"workload": case.name, "seqs": case.num_seqs, "queries": T,
                    "ctx": case.max_kv_len, "topk": case.topk, "heads": H, "d_latent": Dc,
                    "d_rope": case.d_rope, "idx_heads": case.idx_heads, "idx_dim": case.idx_dim,
@@ -603,7 +707,60 @@ def main():
     if not args.no_cpu_baseline and not args.page_size:  # (the paged run adds no new oracle work)
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(case)
+        result["cpu_baseline"]["single_thread"] = cpu_oracle_rate(case, 5.0, threads=1)
+    if case.name == "decode_b16_n128k" and not args.page_size and not args.no_secondary:
+        del case, prob
+        torch.cuda.empty_cache()
+        result["secondary"] = secondary_lines(args, sga, torch, not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
+
+
+def secondary_lines(args, sga, torch, cpu):
+    """The other configurations measured in the same run as the headline:
+    the prefill indexer pass (FP8 MFMA target), the 32 x 32K decode batch and
+    the mixed-length MXFP8 batch (each with a bounded oracle figure)."""
+    from sga_inputs import make_case
+
+    dev = torch.device("cuda", 0)
+    out = {}
+    case = make_case("prefill_q4096_n128k", device=dev)
+    prob = sga.Problem.from_case(case)
+    ms, _ = time_indexer(case, prob, sga, torch, max(5, args.steps // 4), max(2, args.warmup // 4), args.copies)
+    flops, pairs = indexer_flops(case)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] secondary prefill_q4096_n128k indexer: {ms * 1e3:.1f} us per pass, {tflops:.0f} TFLOP/s "
+        f"({tflops / FP8_PEAK_TFLOPS:.1%} of FP8 MFMA peak)")
+    out["prefill_q4096_n128k_indexer"] = {
+        "metric": "indexer score pass TFLOP/s (4,096 queries x up to 131,072 keys)", "value": round(tflops, 1),
+        "unit": "TFLOP/s", "ms_per_pass": round(ms, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_index_fp8_pf", "achieved": round(tflops, 1),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+                     "flops_per_launch": flops}}
+    del case, prob
+    torch.cuda.empty_cache()
+    for name in ("decode_b32_n32k", "varlen_mxfp8_b64"):
+        case = make_case(name, device=dev)
+        prob = sga.Problem.from_case(case)
+        r = time_decode(args, case, prob, sga, torch, args.steps, args.warmup)
+        total_bytes, index_bytes = algorithmic_bytes(case)
+        gbs = total_bytes / (r["ms_step"] * 1e-3) / 1e9
+        idx_gbs = index_bytes / (r["idx_ms"] * 1e-3) / 1e9
+        log(f"[bench] secondary {name}: {r['ms_step'] * 1e3:.1f} us/step, {r['qps']:,.0f} queries/s, "
+            f"{gbs / HBM_PEAK_GBS:.1%} of HBM, phases {r['phases']}")
+        out[name] = {
+            "metric": f"SGA decode queries/s ({name}, k={case.topk})", "value": round(r["qps"], 1),
+            "unit": "queries/s", "ms_per_step": round(r["ms_step"], 5), "launch": r["launch"],
+            "ms_per_step_by_launch": {"hip_graph": None if r["ms_graph"] is None else round(r["ms_graph"], 5),
+                                      "eager": round(r["ms_plain"], 5)},
+            "step_hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": total_bytes},
+            "index_hbm": {"achieved": round(idx_gbs, 1), "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_launch": index_bytes},
+            "phases_us": r["phases"],
+            "cpu_baseline": cpu_oracle_rate(case, 5.0) if cpu else None}
+        del case, prob, r
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

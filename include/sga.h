@@ -318,6 +318,18 @@ sga_status sga_indexer_kl(const sga_problem *p, const void *q_idx, const float *
 sga_status sga_profile_enable(int max_calls);
 sga_status sga_profile_collect(double *ms, int nphase, int *calls);
 
+/*
+ * Streaming-read reference, for measurement: reads `bytes` (a multiple of
+ * 8192) from the device buffer `src` (16-byte aligned) with the decode
+ * indexer's copy pattern (8 KiB tiles through an LDS ring by LDS-DMA, two
+ * 256-thread workgroups per CU, each a contiguous share) and no arithmetic
+ * beyond folding the bytes into one word per workgroup, written to `sink`
+ * (device, sga_stream_read_sink_words() words). Its bandwidth is what the
+ * indexer's copies alone reach on this device.
+ */
+sga_status sga_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int sga_stream_read_sink_words(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -230,6 +230,15 @@ def sga_layer_fwd_noalloc(prob: Problem, q_idx, w, k_idx, q, kv, kv_scale, gate,
         _stream(stream)))
 
 
+def sga_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """The library's streaming-read reference over a device tensor (see sga.h)."""
+    nbytes = src.numel() * src.element_size()
+    if sink.dtype != torch.int32 or sink.numel() < lib().sga_stream_read_sink_words():
+        raise ValueError("sink must be an int32 tensor of sga_stream_read_sink_words() words")
+    _ffi.check(lib().sga_stream_read(_ptr(src, "src"), nbytes - nbytes % 8192, _ptr(sink, "sink"),
+                                     _stream(stream)))
+
+
 def sga_cache_append(prob: Problem, kv_new, k_idx_new, slots, kv, kv_scale, k_idx,
                      stream=None) -> None:
     """Quantise new tokens into cache rows `slots` (see sga_cache_append in sga.h).

@@ -44,6 +44,8 @@ EXPORTS = (
     "sga_indexer_kl",
     "sga_profile_enable",
     "sga_profile_collect",
+    "sga_stream_read",
+    "sga_stream_read_sink_words",
 )
 
 
@@ -113,6 +115,8 @@ def load() -> ctypes.CDLL:
         "sga_profile_enable": ([ctypes.c_int], ctypes.c_int),
         "sga_profile_collect": ([ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+        "sga_stream_read": ([vp, sz, vp, vp], ctypes.c_int),
+        "sga_stream_read_sink_words": ([], ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)

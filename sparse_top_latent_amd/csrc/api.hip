@@ -580,6 +580,20 @@ sga_status sga_indexer_kl(const sga_problem *p, const void *q_idx, const float *
   }
 }
 
+sga_status sga_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  try {
+    if (!src || !sink) return fail(SGA_ERR_INVALID_ARGUMENT, "src / sink is NULL");
+    if (bytes % 8192 || ((uintptr_t)src & 15))
+      return fail(SGA_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 8192 and src 16-byte aligned");
+    return launched(launch_stream_read((const uint8_t *)src, (int64_t)bytes, sink, (hipStream_t)stream),
+                    "stream read");
+  } catch (...) {
+    return fail(SGA_ERR_DEVICE, "internal error");
+  }
+}
+
+int sga_stream_read_sink_words(void) { return kStreamReadBlocksPerCu * device_cu_count(); }
+
 sga_status sga_profile_enable(int max_calls) {
   try {
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);

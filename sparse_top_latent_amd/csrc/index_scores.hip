@@ -279,7 +279,69 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   if (kHist) write_hist0_list<false, kThreads>(hist, sel, t, blockIdx.x, scratch);
 }
 
+// --------------------------------------------------------------------------
+// Streaming-read reference: the index kernel's copy pattern with no scoring.
+// Each workgroup streams a contiguous share of 8 KiB tiles through the same
+// LDS ring (LDS-DMA, nontemporal, kIdxRing steps, one barrier per step), and
+// every thread reads back its 32 bytes of each tile and folds them into one
+// word, written to sink[blockIdx.x] so that no copy can be dropped.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(kIdxWaves * 64) void k_stream_read(const uint8_t *__restrict__ src, int64_t tiles,
+                                                                 uint32_t *__restrict__ sink) {
+  constexpr int kThreads = kIdxWaves * 64;
+  constexpr int kPer = kIdxTileBytes / (kThreads * 16);  // copies per thread and tile
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kIdxRing * kIdxTileBytes];
+  __shared__ uint32_t red[kIdxWaves];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t per = (tiles + gridDim.x - 1) / gridDim.x;
+  const int64_t t0 = min(tiles, (int64_t)blockIdx.x * per), t1 = min(tiles, t0 + per);
+  const int n = (int)(t1 - t0);
+  auto issue = [&](int i) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pc = u * kThreads + tid;
+      __builtin_amdgcn_global_load_lds(src + (t0 + i) * kIdxTileBytes + pc * 16,
+                                       (lds_void *)(ring + (i % kIdxRing) * kIdxTileBytes + (u * kThreads + wave * 64) * 16),
+                                       16, 0, kKeyLoadPolicy);
+    }
+  };
+  for (int i = 0; i < kIdxRing - 1 && i < n; ++i) issue(i);
+  uint32_t acc = 0;
+  for (int i = 0; i < n; ++i) {
+    const int after = min(n - 1, i + kIdxRing - 2) - i;  // tiles issued after tile i
+    wait_vmcnt_upto<kPer * (kIdxRing - 2)>(kPer * after);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (i + kIdxRing - 1 < n) issue(i + kIdxRing - 1);
+    const v4i *tb = (const v4i *)(ring + (i % kIdxRing) * kIdxTileBytes);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const v4i x = tb[u * kThreads + tid];
+      acc ^= (uint32_t)(x.x ^ x.y ^ x.z ^ x.w);
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0): reads done before the buffer is reused
+  }
+  for (int d = 32; d >= 1; d >>= 1) acc ^= __shfl_xor(acc, d, 64);
+  if ((tid & 63) == 0) red[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kIdxWaves; ++i) r ^= red[i];
+    sink[blockIdx.x] = r;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const uint8_t *src, int64_t bytes, uint32_t *sink, hipStream_t s) {
+  const int64_t tiles = bytes / kIdxTileBytes;
+  if (tiles <= 0) return hipSuccess;
+  const int64_t most = (int64_t)kStreamReadBlocksPerCu * device_cu_count();
+  const int grid = (int)(tiles < most ? tiles : most);
+  hipLaunchKernelGGL(k_stream_read, dim3(grid), dim3(kIdxWaves * 64), 0, s, src, tiles, sink);
+  return hipGetLastError();
+}
 
 int index_fp8_iters(int T, int max_kv_len) {
   // a workgroup scores 4 * iters tiles of 64 keys; aim for about two

@@ -43,6 +43,12 @@ hipError_t launch_index_fp8_prefill(const SeqMeta &m, int T, const uint8_t *q_id
                                     const uint8_t *k_idx, float *scores, int64_t stride,
                                     hipStream_t s);
 
+// Streaming-read reference (the index kernel's LDS-DMA copy pattern without
+// the scoring) over bytes / 8192 whole tiles of src; one word per workgroup
+// (at most kStreamReadBlocksPerCu per CU) goes to sink.
+constexpr int kStreamReadBlocksPerCu = 2;
+hipError_t launch_stream_read(const uint8_t *src, int64_t bytes, uint32_t *sink, hipStream_t s);
+
 // --- top-k select -----------------------------------------------------------
 // The level-0 histogram of a query (4096 bins of the top 12 key bits) arrives
 // as lists, one per producer workgroup ("slot") covering slot_keys positions.

@@ -247,3 +247,11 @@ def test_noalloc_layer_rejects_problems_beyond_its_scratch(lib):
                                      None, None, None) == 1
     assert lib.sga_layer_fwd_noalloc(ctypes.byref(_problem()), None, None, None, FAKE, FAKE, None,
                                      None, FAKE, None, None, None) == 1
+
+
+def test_stream_read_reference_argument_checks(lib):
+    # measurement utility: rejected before any HIP call
+    assert lib.sga_stream_read(None, 8192, FAKE, None) == 1
+    assert lib.sga_stream_read(FAKE, 8192, None, None) == 1
+    assert lib.sga_stream_read(FAKE, 8000, FAKE, None) == 1        # not whole 8 KiB tiles
+    assert lib.sga_stream_read(FAKE + 8, 8192, FAKE, None) == 1    # not 16-byte aligned
