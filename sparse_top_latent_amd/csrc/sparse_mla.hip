@@ -225,14 +225,31 @@ __device__ __forceinline__ int32_t split_row(const MlaArgs &a, int t, int64_t st
   return kPaged ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : (int32_t)(start + pos);
 }
 
+// Workgroup b of a 1-D grid of S x T split workgroups -> (split, query).
+// Workgroups are handed to the 8 XCDs round-robin (b mod 8); when the grid
+// divides evenly, the mapping gives every XCD a run of consecutive (query,
+// split) pairs, so that the splits of one query share an XCD and its L2:
+// the query's 73.7 KB slice and its top-k candidates, which every split
+// reads, are then fetched from memory once per query instead of once per
+// XCD. Any other grid keeps the plain order.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void split_of_block(int b, int S, int T, int *split, int *t) {
+  const int total = S * T;
+  int v = b;
+  if (total % kXcds == 0) v = (b % kXcds) * (total / kXcds) + b / kXcds;
+  *split = v % S;
+  *t = v / S;
+}
+
 template <bool kMx, int R, bool kFuse, bool kPaged>
 __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restrict__ opart,
-                                                    float2 *__restrict__ ml) {
+                                                    float2 *__restrict__ ml, int S) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // cache row of each selected row of the split (-1: none); int32 row ids
   // keep the gather's address batches small in registers
   __shared__ int32_t rows[R * kMlaRowsPerSplit];
-  const int split = blockIdx.x, t = blockIdx.y, S = gridDim.x;
+  int split, t;
+  split_of_block(blockIdx.x, S, a.T, &split, &t);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hg = wave & 3, set = wave >> 2, st = tid & 255;
@@ -677,7 +694,7 @@ static void launch_split8(const MlaArgs &a, uint16_t *opart, float2 *ml, int S, 
     return true;
   }();
   (void)attr;
-  hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse, kPaged>), dim3(S, a.T), dim3(512), smem, s, a, opart, ml);
+  hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse, kPaged>), dim3(S * a.T), dim3(512), smem, s, a, opart, ml, S);
 }
 
 template <bool kMx, bool kFuse, bool kPaged>
