@@ -638,10 +638,6 @@ def main():
         f"eager with phase events {eager_ms * 1e3:.1f} us/step), "
         f"{qps:,.0f} queries/s, step {step_gbs:,.0f} GB/s of per-query bytes ({step_gbs / HBM_PEAK_GBS:.1%} of HBM), "
         f"phases {phases}")
-    stream_gbs = stream_read_gbs(torch, sga, kis)
-    log(f"[bench] index kernel {achieved:,.0f} GB/s; the library's streaming-read reference over "
-        f"{kis[0].numel() / 1e6:.0f} MB index caches {stream_gbs:,.0f} GB/s")
-    del r, kis
     rec = traffic_record(args.workload) if not args.page_size else None
     # Several queries per sequence share the scan of its index keys. With few
     # of them (multi-query decode) the index pass stays HBM-bound; with many
@@ -650,6 +646,12 @@ def main():
     # neighbouring queries share, no longer bound the step.
     flops_all, _ = indexer_flops(case)
     mfma_bound = flops_all / index_bytes > FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+    stream_gbs = None
+    if not mfma_bound:
+        stream_gbs = stream_read_gbs(torch, sga, kis)
+        log(f"[bench] index kernel {achieved:,.0f} GB/s; the library's streaming-read reference over "
+            f"{kis[0].numel() / 1e6:.0f} MB index caches {stream_gbs:,.0f} GB/s")
+    del r, kis
     if mfma_bound:
         flops, _ = indexer_flops(case)
         tflops = flops / (idx_ms * 1e-3) / 1e12
