@@ -94,7 +94,7 @@ typedef struct sga_problem {
   int32_t num_q;         /* T: query rows                                                */
   int32_t max_kv_len;    /* host bound on every kv_len[b]; row stride of the score buffer */
   int32_t page_size;     /* 0: contiguous rows (kv_start); else rows in pages (see below) */
-  int64_t num_kv_rows;   /* rows in kv, kv_scale and k_idx                               */
+  int64_t num_kv_rows;   /* rows in kv, kv_scale and k_idx (at most 2^31 - 1)            */
   int32_t heads;         /* H: attention heads (64)                                      */
   int32_t d_latent;      /* Dc: latent width = value width (512)                          */
   int32_t d_rope;        /* Dr: rotary key width (64)                                     */

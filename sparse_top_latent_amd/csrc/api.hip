@@ -48,6 +48,9 @@ sga_status check_common(const sga_problem *p) {
                 p->num_q, p->num_seqs, p->max_kv_len);
   if (p->max_kv_len > kMaxKvLen)
     return fail(SGA_ERR_UNSUPPORTED, "max_kv_len %d exceeds %d", p->max_kv_len, kMaxKvLen);
+  // cache rows are addressed with 32-bit ids on the device
+  if (p->num_kv_rows > INT32_MAX)
+    return fail(SGA_ERR_UNSUPPORTED, "num_kv_rows %lld exceeds 2^31 - 1", (long long)p->num_kv_rows);
   if (p->topk < 1) return fail(SGA_ERR_INVALID_ARGUMENT, "topk must be >= 1 (got %d)", p->topk);
   if (p->num_q > 0 && (!p->q_seq || !p->q_pos))
     return fail(SGA_ERR_INVALID_ARGUMENT, "q_seq / q_pos is NULL");
@@ -164,7 +167,9 @@ sga_status plan_for(const sga_problem *p, int op, Plan *plan) {
 }
 
 size_t mla_ws(const sga_problem *p, const Plan &plan) {
-  return plan.mla == MlaPath::kF32 ? 0 : mla_split_ws_bytes(p->num_q, p->topk);
+  if (plan.mla == MlaPath::kF32) return 0;
+  const int shift = p->page_size ? __builtin_ctz((unsigned)p->page_size) : 0;
+  return mla_whole_query_path(p->num_q, p->kv_dtype, shift) ? 0 : mla_split_ws_bytes(p->num_q, p->topk);
 }
 
 size_t ws_bytes(const sga_problem *p, int op, const Plan &plan) {

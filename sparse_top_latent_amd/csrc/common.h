@@ -206,6 +206,19 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
 // 64, at most 1024); *total receives the block sum. `scratch` needs
 // blockDim / 64 words of LDS. Two barriers; the second lets the caller reuse
 // `scratch` right away.
+// Workgroup barrier for threads that communicate through LDS only: it waits
+// for this wave's LDS operations, not for its outstanding global loads (a
+// __syncthreads() drains those too, which stalls on loads whose results are
+// not needed yet).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0) only
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// kLdsOnly: the barriers wait for LDS operations only (lds_barrier).
+template <bool kLdsOnly = false>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch,
                                                          uint32_t *total) {
   const int lane = threadIdx.x & 63;
@@ -213,7 +226,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
   const int nw = blockDim.x >> 6;
   const uint32_t inc = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = inc;
-  __syncthreads();
+  if (kLdsOnly) lds_barrier(); else __syncthreads();
   uint32_t base = 0, tot = 0;
   for (int i = 0; i < nw; ++i) {
     const uint32_t x = scratch[i];
@@ -221,7 +234,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     tot += x;
   }
   *total = tot;
-  __syncthreads();
+  if (kLdsOnly) lds_barrier(); else __syncthreads();
   return base + inc - v;
 }
 

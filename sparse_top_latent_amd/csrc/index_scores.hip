@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kF32Block) void k_index_f32(SeqMeta m, int k, int H
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
-  if (want_hist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = n;
+  if (want_hist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = make_int2(n, (int32_t)start);
   const int base = blockIdx.x * kF32Block;
   if (base >= n) return;
   for (int i = threadIdx.x; i < HI * DI; i += kF32Block) qs[i] = q_idx[(size_t)t * HI * DI + i];
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
-  if (kHist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = n;
+  if (kHist && blockIdx.x == 0 && threadIdx.x == 0) sel.ncand[t] = make_int2(n, (int32_t)start);
   const int c0 = blockIdx.x * steps_per_wg * kIdxStepKeys;
   if (c0 >= n) return;
   // paged caches: the page ids under this workgroup's keys, one per lane

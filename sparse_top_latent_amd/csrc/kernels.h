@@ -55,8 +55,9 @@ hipError_t launch_stream_read(const uint8_t *src, int64_t bytes, uint32_t *sink,
 // Slot `slot` of query t starts at word t * list_q_stride + slot * slot_words
 // of `lists` (16-byte aligned): its entry count, then the entries
 // (bin << 20 | count) in descending bin order. No global atomics build them
-// and nothing is cleared beforehand. A producer also records n_t in ncand[t]
-// (from its workgroup 0 of query t).
+// and nothing is cleared beforehand. A producer also records, from its
+// workgroup 0 of query t, n_t and the cache row of position 0 of the query's
+// sequence in ncand[t] (the row is 0 in the paged layout; rows fit 32 bits).
 constexpr int kTopkMaxSlots = 4096;  // level-0 list slots one query may use
 struct TopkWs {
   uint32_t *lists;        // [T, list_q_stride]
@@ -64,7 +65,7 @@ struct TopkWs {
   int32_t slot_keys;      // positions one slot covers (set by the producer's launcher)
   int32_t slot_words;     // words per slot: 4 + at most 4096 entries (set by the producer's launcher)
   uint4 *thr;             // [T] (b0, keys above bin b0, candidates, 0)
-  int32_t *ncand;         // [T] candidate count n_t
+  int2 *ncand;            // [T] (candidate count n_t, row of position 0)
   uint2 *entries;         // [T, nchunk * kTopkChunk] candidates (position, key)
   int32_t nchunk;         // ceil(max_kv_len / kTopkChunk)
 };
@@ -107,6 +108,8 @@ hipError_t launch_mla_f32(const MlaArgs &a, hipStream_t s);
 // MI355X path: H=64, Dc=512, Dr=64, bf16 or MXFP8 rows
 constexpr int kMlaRowsPerSplit = 128;
 size_t mla_split_ws_bytes(int T, int k);
+// whether the MLA runs as whole queries (no partials, no combine pass)
+bool mla_whole_query_path(int T, int kv_dtype, int page_shift);
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s);
 // whether the split kernel should do the top-k's last step itself (fuse)
 bool mla_fuse_finish(int T, int k);

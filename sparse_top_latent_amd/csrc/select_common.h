@@ -178,45 +178,69 @@ __device__ __forceinline__ void write_hist0_list(const uint32_t *hist, const Top
   if (tid == 0) list[0] = total;
 }
 
+// Candidates of the top-k finish (below) for a workgroup of kBlock threads:
+// round r holds candidates [r * kRound, r * kRound + kRound) of the query,
+// thread tid the kPer consecutive ones from r * kRound + kPer tid. Reads past
+// the end are clamped into the array and not used.
+template <int kBlock>
+struct FinishInput {
+  static constexpr int kPer = 4096 / kBlock;  // candidates per thread and round
+  static constexpr int kRound = kBlock * kPer;
+  static_assert(kPer % 2 == 0, "candidate pairs");
+  uint2 c[kPer];  // round 0, kept in registers
+  uint4 th;       // the query's totals from k_topk_select
+};
+
+template <int kBlock>
+__device__ __forceinline__ void finish_load_round(const TopkWs &ws, int t, int r,
+                                                  uint2 (&pr)[FinishInput<kBlock>::kPer]) {
+  constexpr int kPer = FinishInput<kBlock>::kPer;
+  const uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
+  const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;
+  const uint32_t f0 = (uint32_t)r * FinishInput<kBlock>::kRound + threadIdx.x * kPer;
+#pragma unroll
+  for (int i = 0; i < kPer; i += 2) {
+    const uint32_t f = min(f0 + i, cap - 2);
+    const uint4 x = *(const uint4 *)(cand + f);
+    pr[i] = make_uint2(x.x, x.y);
+    pr[i + 1] = make_uint2(x.z, x.w);
+  }
+}
+
+// Requests the finish's first round of candidates and the query's totals. It
+// depends on nothing else, so a caller can issue it first and overlap its
+// latency with other lookups (the data is only used for queries with n_t > k).
+template <int kBlock>
+__device__ __forceinline__ void finish_request(const TopkWs &ws, int t, FinishInput<kBlock> &in) {
+  finish_load_round<kBlock>(ws, t, 0, in.c);
+  in.th = ws.thr[t];
+}
+
 // The last step of the top-k select for query t, done by one workgroup of
 // kBlock threads: from the candidates k_topk_select wrote (position order) and
 // its totals (b0, keys above bin b0, candidates), the level-1 and level-2
 // histograms give the exact k-th key K* and the number of ties at K* to take;
 // then, round by round in position order, one packed scan gives every
 // selected candidate its output index. `out(o, pos)` is called once for each
-// o in [0, k) (in no particular order across threads). LDS: `hist` holds
-// 2 * 1024 words, `scratch` kBlock / 64, `res` 2. Every thread of the
-// workgroup must call it (it has barriers). Only for queries with n_t > k.
+// o in [0, k) (in no particular order across threads). `in` comes from
+// finish_request. LDS: `hist` holds 2 * 1024 words, `scratch` kBlock / 64,
+// `res` 2. Every thread of the workgroup must call it (it has barriers, which
+// wait for LDS operations only, so loads the caller has in flight stay in
+// flight). Only for queries with n_t > k.
 template <int kBlock, class Out>
-__device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, uint32_t *hist,
-                                             uint32_t *scratch, int *res, Out out) {
-  constexpr int kPer = 4096 / kBlock;  // candidates per thread and round
-  constexpr int kRound = kBlock * kPer;
-  static_assert(kPer % 2 == 0, "candidate pairs");
+__device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, FinishInput<kBlock> &in,
+                                             uint32_t *hist, uint32_t *scratch, int *res, Out out) {
+  constexpr int kPer = FinishInput<kBlock>::kPer;
+  constexpr int kRound = FinishInput<kBlock>::kRound;
   const int tid = threadIdx.x;
-  const uint2 *cand = ws.entries + (size_t)t * ws.nchunk * kTopkChunk;
   const uint32_t cap = (uint32_t)ws.nchunk * kTopkChunk;
-  // Round r holds candidates [r * kRound, r * kRound + kRound), thread tid the
-  // kPer consecutive ones from r * kRound + kPer tid; round 0 stays in
-  // registers and is requested before the query's totals arrive (reads past
-  // the end are clamped into the array and not used)
-  auto load_round = [&](int r, uint2 (&pr)[kPer]) {
-    const uint32_t f0 = (uint32_t)r * kRound + tid * kPer;
-#pragma unroll
-    for (int i = 0; i < kPer; i += 2) {
-      const uint32_t f = min(f0 + i, cap - 2);
-      const uint4 x = *(const uint4 *)(cand + f);
-      pr[i] = make_uint2(x.x, x.y);
-      pr[i + 1] = make_uint2(x.z, x.w);
-    }
-  };
-  uint2 p0r[kPer];
-  load_round(0, p0r);
-  const uint4 th = ws.thr[t];
+  auto load_round = [&](int r, uint2 (&pr)[kPer]) { finish_load_round<kBlock>(ws, t, r, pr); };
+  uint2 (&p0r)[kPer] = in.c;
+  const uint4 th = in.th;
   const uint32_t ub0 = th.x, above0 = th.y;
   const uint32_t total = min(th.z, cap);
   for (int i = tid; i < 2 * kHist12Bins; i += kBlock) hist[i] = 0u;
-  __syncthreads();
+  lds_barrier();
   const int rounds = (int)((total + kRound - 1) / kRound);
   auto valid = [&](int r, int i) { return (uint32_t)r * kRound + tid * kPer + i < total; };
   uint32_t *hist1 = hist, *hist2 = hist + kHist12Bins;
@@ -237,7 +261,7 @@ __device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, uin
         res[1] = (int)a;
       }
     }
-    __syncthreads();
+    lds_barrier();
     *above = (uint32_t)res[1];
     return res[0];
   };
@@ -255,7 +279,7 @@ __device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, uin
     pin(pr);
     level1(r, pr);
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t want = (uint32_t)k - above0;
   uint32_t above1;
   const int b1 = find_bin(hist1, want, &above1);
@@ -274,7 +298,7 @@ __device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, uin
     pin(pr);
     level2(r, pr);
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t above2;
   const int b2 = find_bin(hist2, want, &above2);
   want -= above2;
@@ -294,7 +318,7 @@ __device__ __forceinline__ void finish_query(int k, const TopkWs &ws, int t, uin
       n_eq += ok && pr[i].y == kstar;
     }
     uint32_t tot;
-    const uint32_t pre = block_exclusive_scan((n_eq << 16) | n_gt, scratch, &tot);
+    const uint32_t pre = block_exclusive_scan<true>((n_eq << 16) | n_gt, scratch, &tot);
     uint32_t tr = tie_run + (pre >> 16);                      // ties in front of this run
     uint32_t o2 = gt_run + (pre & 0xFFFFu) + min(tr, take);   // outputs in front of it
 #pragma unroll

@@ -204,9 +204,10 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 // compiler waits for the wave's outstanding LDS-DMA copies before the first
 // such read; in practice the rest of the gather lands while the QK^T block in
 // front of it runs, so the wait costs little.
-template <int kM>
+template <int kM, int N>
 __device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int (&voff)[4], const v8bf &pb,
-                                           v4f (&acc)[kCt]) {
+                                           v4f (&acc)[N]) {
+  static_assert(4 * kM + 3 < N, "accumulator block");
   typedef __attribute__((address_space(3))) v4bf lds_v4bf;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -218,11 +219,46 @@ __device__ __forceinline__ void pv_block_b(const unsigned char *tile, const int 
   }
 }
 
+// The same block for a tile whose neighbours in the LDS ring are still being
+// copied: the compiler cannot tell the transposed read from those copies and
+// would wait for all of them before it, so the 8 reads are issued in one asm
+// statement that also waits for them (lgkmcnt) before it ends.
+template <int kM, int N>
+__device__ __forceinline__ void pv_block_ring(const unsigned char *tile, const int (&voff)[4], const v8bf &pb,
+                                              v4f (&acc)[N]) {
+  static_assert(4 * kM + 3 < N, "accumulator block");
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_u8 *)tile;
+  v2u lo[4], hi[4];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]),
+        "=&v"(hi[3])
+      : "v"(base + voff[0]), "v"(base + voff[1]), "v"(base + voff[2]), "v"(base + voff[3]), "n"(kM * 128),
+        "n"(kM * 128 + 16 * kRowChunks * 16)
+      : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4bf l4 = __builtin_bit_cast(v4bf, lo[i]);
+    const v4bf h4 = __builtin_bit_cast(v4bf, hi[i]);
+    const v8bf va = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+    acc[4 * kM + i] = mfma_bf16(va, pb, acc[4 * kM + i]);
+  }
+}
+
 // the cache row of position pos of the query's sequence (paged: through the
 // block table)
 template <bool kPaged>
-__device__ __forceinline__ int32_t split_row(const MlaArgs &a, int t, int64_t start, int32_t pos) {
-  return kPaged ? (int32_t)kv_row(a.meta, a.meta.q_seq[t], start, pos) : (int32_t)(start + pos);
+__device__ __forceinline__ int32_t split_row(const MlaArgs &a, int b, int64_t start, int32_t pos) {
+  return kPaged ? (int32_t)kv_row(a.meta, b, start, pos) : (int32_t)(start + pos);
 }
 
 // Workgroup b of a 1-D grid of S x T split workgroups -> (split, query).
@@ -259,56 +295,68 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   const int nrows = min(R * kMlaRowsPerSplit, a.k - r0);  // >= 1
   const int rounds = (nrows + kMlaRowsPerSplit - 1) / kMlaRowsPerSplit;
   // the query slice of this wave's 16 heads (B operands of S^T = rows . Q^T);
-  // with the fused top-k finish it is requested first, since it does not
-  // depend on the selection (elsewhere after the row lookup, which keeps the
-  // many-round instances clear of register spills)
+  // with the fused top-k finish it is requested right after the finish's
+  // first candidates, so that it lands while the finish runs; elsewhere after
+  // the row lookup, which keeps the many-round instances clear of register
+  // spills
   const int head = hg * 16 + c16;
   const uint8_t *qh = (const uint8_t *)a.q + ((size_t)t * kH + head) * kD * 2;
   v8bf qreg[kKsteps];
-  if (kFuse) {
+  auto load_q = [&] {
 #pragma unroll
     for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
-  }
+  };
   int64_t start;
   if (!kFuse) {
     // the selected positions are requested first (clamped, unconditional) so
     // that their latency overlaps the sequence lookup; thread i takes row i
     const int my_row = min(tid, R * kMlaRowsPerSplit - 1);
     int32_t pos = a.topk_idx[(size_t)t * a.k + r0 + min(my_row, nrows - 1)];
-    const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
+    const int b = a.meta.q_seq[t];
+    const int L = seq_len_clipped(a.meta, b, &start);
     if (tid < R * kMlaRowsPerSplit)
-      rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? split_row<kPaged>(a, t, start, pos) : -1;
+      rows[tid] = (tid < nrows && pos >= 0 && pos < L) ? split_row<kPaged>(a, b, start, pos) : -1;
   } else {
     // The top-k's last step, done here for the workgroup's own output slots
     // [r0, r0 + nrows) of the query (every split workgroup of the query
     // repeats it; that costs no time, since it replaces a kernel boundary and
     // the wait for the selected positions). n_t <= k: every candidate, in
-    // position order, then -1.
-    const int n = a.sel.ncand[t];
-    const int L = seq_len_clipped(a.meta, a.meta.q_seq[t], &start);
+    // position order, then -1. All the lookups are requested at once: the
+    // finish's first candidates and totals (the fused finish runs only when
+    // max_kv_len > k, so k_topk_select has written them), n_t with the row of
+    // position 0 (recorded by the index pass) and, paged, the sequence; then
+    // the query slice, so that waiting for any earlier load leaves it in
+    // flight. Every candidate position is below n_t, which the sequence's
+    // cached length bounds.
+    FinishInput<512> fin;
+    finish_request(a.sel, t, fin);
+    const int2 nc = a.sel.ncand[t];
+    const int b = kPaged ? a.meta.q_seq[t] : 0;
+    asm volatile("" ::: "memory");
+    load_q();
+    const int n = nc.x;
+    start = kPaged ? 0 : nc.y;
     if (tid < R * kMlaRowsPerSplit) {
       const int32_t pos = (n <= a.k && tid < nrows && r0 + tid < n) ? r0 + tid : -1;
-      rows[tid] = (pos >= 0 && pos < L) ? split_row<kPaged>(a, t, start, pos) : -1;
+      rows[tid] = pos >= 0 ? split_row<kPaged>(a, b, start, pos) : -1;
       if (n <= a.k && a.topk_out && tid < nrows) a.topk_out[(size_t)t * a.k + r0 + tid] = pos;
     }
     if (n > a.k) {  // uniform over the workgroup
       // (LDS for the histograms and scan at the start of the tile area; the
       // copies into it start after the barrier below)
       uint32_t *fh = (uint32_t *)smem;
-      finish_query<512>(a.k, a.sel, t, fh, fh + 2 * kHist12Bins, (int *)(fh + 2 * kHist12Bins + 8),
+      finish_query<512>(a.k, a.sel, t, fin, fh, fh + 2 * kHist12Bins, (int *)(fh + 2 * kHist12Bins + 8),
                         [&](uint32_t o, int32_t p) {
                           if (o >= (uint32_t)r0 && o < (uint32_t)(r0 + nrows)) {
-                            rows[o - r0] = (p >= 0 && p < L) ? split_row<kPaged>(a, t, start, p) : -1;
+                            rows[o - r0] = (p >= 0 && p < n) ? split_row<kPaged>(a, b, start, p) : -1;
                             if (a.topk_out) a.topk_out[(size_t)t * a.k + o] = p;
                           }
                         });
     }
   }
-  __syncthreads();  // rows[] ready
-  if (!kFuse) {
-#pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
-  }
+  // rows[] ready (written through LDS only: the query slice stays in flight)
+  if (kFuse) barrier_lds(); else __syncthreads();
+  if (!kFuse) load_q();
 
   // MXFP8: raw tiles at smem, the set's expanded bf16 tile after them, then
   // the scales of the round's 128 rows
@@ -537,6 +585,263 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
   if (set == 0 && g == 0) ml[((size_t)t * S + split) * kH + head] = make_float2(m, l);
 }
 
+// --------------------------------------------------------------------------
+// Whole-query kernel (bf16 rows, contiguous cache, many more queries than
+// CUs, e.g. a prefill chunk). One workgroup per CU takes a run of whole
+// queries and streams every 32-row tile of them through one ring of four LDS
+// slots, across query boundaries, so the gather never restarts. All 8 waves
+// work on the same tile: wave (hg, half) scores tile rows 16 half .. 16 half
+// + 15 for heads 16 hg .. 16 hg + 15 over the full 576 dims and swaps the
+// result with its partner wave through LDS, so both hold S for all 32 rows;
+// both then run the same online softmax and accumulate O for channels
+// 256 half .. 256 half + 255. A query's output is normalised, gated and
+// written at its last tile: no partials and no combine pass.
+//
+// The ring is refilled two tiles at a time: at every even tile j all 512
+// threads copy tiles j + 2 and j + 3 (9 16-byte copies per thread), so the
+// number of copies in flight behind any tile is fixed and the waits are
+// compile-time constants. The selected positions of each group of 128 rows
+// (a "chunk", 4 tiles) are brought into LDS by two waves with the same kind
+// of copy, two chunks ahead, and turned into cache rows one chunk ahead.
+// --------------------------------------------------------------------------
+constexpr int kWqSlots = 4;
+constexpr int kWqMaxQ = 64;  // queries one workgroup takes
+constexpr size_t kWqSmem = (size_t)kWqSlots * kTileBytes + 8 * 64 * 16;  // the ring, then the S exchange
+static_assert(kWqSmem + 2 * 128 * 4 * 2 + kWqMaxQ * 8 <= 160 * 1024, "LDS of k_mla_wq");
+
+template <bool kGateBf16>
+__global__ __launch_bounds__(512) void k_mla_wq(MlaArgs a, int qpw) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];  // the tile ring
+  __shared__ int32_t rowsbuf[2][128];                                   // cache rows of two chunks
+  __shared__ __attribute__((aligned(16))) int32_t posbuf[2][128];       // positions of two chunks
+  __shared__ int2 qmeta[kWqMaxQ];                                       // (row of position 0, length)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 3, half = wave >> 2;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int t0 = blockIdx.x * qpw;
+  const int nq = min(qpw, a.T - t0);
+  const int k = a.k;
+  const int C = (k + 127) / 128;  // chunks per query
+  const int NT = 4 * C;           // tiles per query (tiles past k hold no row)
+  const int N = nq * NT;          // tiles of the workgroup
+  const int NC = nq * C;          // chunks of the workgroup
+  const int head = hg * 16 + c16;
+  v4f *xs = (v4f *)(smem + kWqSlots * kTileBytes);  // S of each wave's 16 rows, after the ring
+
+  // chunk d -> query slot d / C, rows 128 (d % C) ..; the position of entry i
+  auto pos_src = [&](int d, int i) {
+    const int qi = d / C, c = d - qi * C;
+    const int e = min(128 * c + i, k - 1);  // entries past k: any valid address (masked below)
+    return a.topk_idx + (size_t)(t0 + qi) * k + e;
+  };
+  // positions -> cache rows for chunk d (threads 0..127), from posbuf[d & 1]
+  auto convert = [&](int d) {
+    if (tid < 128) {
+      const int qi = d / C, c = d - qi * C;
+      const int2 qm = qmeta[qi];
+      const int32_t pos = posbuf[d & 1][tid];
+      rowsbuf[d & 1][tid] = (128 * c + tid < k && pos >= 0 && pos < qm.y) ? qm.x + pos : -1;
+    }
+  };
+  // copies of tiles j and j + 1 (both in the ring): chunk index c = u * 512 +
+  // tid of the pair, c < 2304 in tile j; rows past the selection read zeros
+  // (a wave's 64 chunks never straddle the two tiles: 2304 = 36 x 64, so
+  // the tile and the LDS destination are uniform over the wave)
+  static_assert((kTile * kRowChunks) % 64 == 0, "a wave's copies stay in one tile");
+  auto issue_pair = [&](int j) {
+    // (the lane index is made opaque here so that the compiler recomputes the
+    // 9 addresses per call instead of keeping them in registers all along)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      const int cw = u * 512 + wave * 64;  // the wave's first chunk of the pair
+      const int second = cw >= kTile * kRowChunks ? 1 : 0;
+      const int tt = j + second;
+      const int cb = cw - second * kTile * kRowChunks;  // ... within tile tt
+      const int cc = cb + ln;
+      const int r = cc / kRowChunks;
+      const int col = (cc - r * kRowChunks) ^ row_swz(r);
+      const int32_t gr = rowsbuf[(tt >> 2) & 1][(tt & 3) * kTile + r];
+      const void *src = gr >= 0 ? (const void *)((const uint8_t *)a.kv + (int64_t)gr * (kD * 2) + col * 16)
+                                : (const void *)g_zero16;
+      dma16(src, smem + (tt & (kWqSlots - 1)) * kTileBytes + cb * 16);
+    }
+  };
+
+  // ---- prologue: query metadata, rows of chunks 0 and 1, query slice of the
+  // first query, copies of tiles 0 and 1
+  int2 qm0 = make_int2(0, 0);
+  if (tid < nq) {
+    int64_t start;
+    const int L = seq_len_clipped(a.meta, a.meta.q_seq[t0 + tid], &start);
+    qm0 = make_int2((int32_t)start, L);
+  }
+  int32_t p0 = -1;
+  if (tid < 256 && (tid >> 7) < NC) p0 = *pos_src(tid >> 7, tid & 127);
+  if (tid < nq) qmeta[tid] = qm0;
+  if (tid < 256) posbuf[tid >> 7][tid & 127] = p0;
+  __syncthreads();
+  convert(0);
+  if (NC > 1) convert(1);
+  v8bf qreg[kKsteps];
+  auto load_q = [&](int qi) {
+    const uint8_t *qh = (const uint8_t *)a.q + ((size_t)(t0 + qi) * kH + head) * kD * 2;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qh + (ks * 32 + 8 * g) * 2));
+  };
+  load_q(0);
+  __syncthreads();  // rowsbuf of chunks 0 and 1
+  // the slice is waited for here and after each reload below: a load still
+  // in flight at the loop's first score MFMA would make the compiler wait for
+  // every copy in flight there, in every iteration
+  wait_vmcnt<0>();
+  issue_pair(0);
+
+  v4f acc[kCt / 2];
+#pragma unroll
+  for (int ct = 0; ct < kCt / 2; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float scale2 = a.tau * kLog2e;
+  const int vr = 4 * g + (c16 >> 2);
+  const int qq = (c16 & 3) >> 1, vsub = (c16 & 1) * 8;
+  int voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (vr * kRowChunks + ((2 * i + qq) ^ row_swz(vr))) * 16 + vsub;
+  const bool out_bf16 = a.out_dtype == SGA_BF16;
+
+  for (int j = 0; j < N; ++j) {
+    // tile j has landed: at even j it is the older tile of the newest pair
+    // (5 or 4 of this thread's 9 copies of that pair belong to tile j + 1);
+    // at odd j the pair of tiles j + 1, j + 2 was issued after it
+    if (j & 1) {
+      wait_vmcnt<9>();
+    } else if (tid < 256) {
+      wait_vmcnt<4>();
+    } else {
+      wait_vmcnt<5>();
+    }
+    barrier_lds();  // tile j (and the positions copied with it) visible; tile j - 1 and xs done
+    if ((j & 1) == 0) {
+      const int e = j >> 2;
+      if ((j & 3) == 0 && j > 0 && e + 1 < NC) convert(e + 1);  // rows of chunk e + 1 (positions copied 2 tiles ago)
+      if ((j & 3) == 2 && wave < 2 && e + 2 < NC) {
+        // positions of chunk e + 2, two chunks ahead; older than the pair below
+        __builtin_amdgcn_global_load_lds(pos_src(e + 2, wave * 64 + lane), (lds_void *)&posbuf[e & 1][wave * 64], 4,
+                                         0, 0);
+      }
+      if (j + 2 < N) issue_pair(j + 2);
+    }
+    const int qi = j / NT, tt = j - qi * NT;
+    const unsigned char *tile = smem + (j & (kWqSlots - 1)) * kTileBytes;
+    const uint32_t tvalid = (uint32_t)__ballot(lane < kTile && rowsbuf[(j >> 2) & 1][(j & 3) * kTile + (lane & 31)] >= 0);
+    const bool last = tt == NT - 1;
+    if (tvalid != 0u) {  // uniform over the workgroup
+      v4f sv[2];
+      v4f own = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks)
+        own = mfma_bf16(as_v8bf(*(const v4i *)(tile + swz(16 * half + c16, 4 * ks + g) * 16)), qreg[ks], own);
+      xs[wave * 64 + lane] = own;
+      barrier_lds();
+      const v4f other = xs[(wave ^ 4) * 64 + lane];
+      sv[0] = half ? other : own;
+      sv[1] = half ? own : other;
+      float lg[8];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const bool ok = (tvalid >> ((jj >> 2) * 16 + 4 * g + (jj & 3))) & 1u;
+        lg[jj] = ok ? sv[jj >> 2][jj & 3] * scale2 : -INFINITY;
+        mt = fmaxf(mt, lg[jj]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < kCt / 2; ++ct) acc[ct] *= alpha;
+        m_run = m_new;
+      }
+      float p[8], ps = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        p[jj] = exp2f(lg[jj] - m_run);
+        ps += p[jj];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run += ps;
+      v8bf pb;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pb[jj] = (__bf16)p[jj];
+      const unsigned char *vt = tile + half * 512;  // this wave's 256 channels
+      pv_block_ring<0>(vt, voff, pb, acc);
+      pv_block_ring<1>(vt, voff, pb, acc);
+      pv_block_ring<2>(vt, voff, pb, acc);
+      pv_block_ring<3>(vt, voff, pb, acc);
+    }
+    if (last) {
+      // the query's output: O / l, gated, and its log-sum-exp (R11: none
+      // selected -> 0 and -inf)
+      const int t = t0 + qi;
+      const bool any = l_run > 0.0f;
+      const float inv = any ? 1.0f / l_run : 0.0f;
+      const size_t ob = ((size_t)t * kH + head) * kDc + (size_t)(256 * half + 4 * g);
+      uint2 graw[kCt / 2];
+      if (a.gate && kGateBf16) {
+#pragma unroll
+        for (int ct = 0; ct < kCt / 2; ++ct) graw[ct] = *(const uint2 *)((const uint16_t *)a.gate + ob + 16 * ct);
+      }
+      // (all outputs are formed in place first and stored afterwards)
+#pragma unroll
+      for (int ct = 0; ct < kCt / 2; ++ct) {
+        float y[4] = {acc[ct][0] * inv, acc[ct][1] * inv, acc[ct][2] * inv, acc[ct][3] * inv};
+        if (a.gate) {
+          float gv[4];
+          if (kGateBf16) {
+            gv[0] = bf16_bits_to_f32(graw[ct].x & 0xFFFFu);
+            gv[1] = bf16_bits_to_f32(graw[ct].x >> 16);
+            gv[2] = bf16_bits_to_f32(graw[ct].y & 0xFFFFu);
+            gv[3] = bf16_bits_to_f32(graw[ct].y >> 16);
+          } else {
+            const v4f gf = *(const v4f *)((const float *)a.gate + ob + 16 * ct);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gv[i] = gf[i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[i] *= sigmoidf_exact_ends(gv[i]);
+        }
+        acc[ct] = (v4f){y[0], y[1], y[2], y[3]};
+      }
+      if (out_bf16) {
+#pragma unroll
+        for (int ct = 0; ct < kCt / 2; ++ct) {
+          const uint32_t lo = f32_to_bf16_bits(acc[ct][0]) | (f32_to_bf16_bits(acc[ct][1]) << 16);
+          const uint32_t hi = f32_to_bf16_bits(acc[ct][2]) | (f32_to_bf16_bits(acc[ct][3]) << 16);
+          *(uint2 *)((uint16_t *)a.out + ob + 16 * ct) = make_uint2(lo, hi);
+        }
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < kCt / 2; ++ct) *(v4f *)((float *)a.out + ob + 16 * ct) = acc[ct];
+      }
+#pragma unroll
+      for (int ct = 0; ct < kCt / 2; ++ct) acc[ct] = (v4f){0.f, 0.f, 0.f, 0.f};
+      if (a.lse && half == 0 && g == 0) a.lse[(size_t)t * kH + head] = any ? m_run / kLog2e + __logf(l_run) : -INFINITY;
+      m_run = -INFINITY;
+      l_run = 0.0f;
+      // the slice of the next query (loaded unconditionally, the last query's
+      // again at the end, so that the old slice is dead during the output)
+      asm volatile("" ::: "memory");
+      load_q(min(qi + 1, nq - 1));
+      wait_vmcnt<0>();
+    }
+  }
+}
+
 constexpr int kMaxSplits = 2048 / kMlaRowsPerSplit;
 constexpr int kCombCt = 4;  // channel tiles per combine workgroup (256 threads)
 
@@ -697,6 +1002,30 @@ static void launch_split8(const MlaArgs &a, uint16_t *opart, float2 *ml, int S, 
   hipLaunchKernelGGL((k_mla_split8<kMx, R, kFuse, kPaged>), dim3(S * a.T), dim3(512), smem, s, a, opart, ml, S);
 }
 
+// The whole-query kernel takes bf16 rows in the contiguous layout when there
+// are at least two queries per CU (and so no fused top-k finish).
+bool mla_whole_query_path(int T, int kv_dtype, int page_shift) {
+  return kv_dtype == SGA_BF16 && page_shift == 0 && (int64_t)T >= 2LL * device_cu_count();
+}
+
+static hipError_t launch_wq(const MlaArgs &a, hipStream_t s) {
+  static const bool attr = [] {
+    (void)hipFuncSetAttribute((const void *)k_mla_wq<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWqSmem);
+    (void)hipFuncSetAttribute((const void *)k_mla_wq<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWqSmem);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)attr;
+  const int cus = device_cu_count();
+  const int qpw = std::min((a.T + cus - 1) / cus, kWqMaxQ);
+  const dim3 grid((a.T + qpw - 1) / qpw);
+  if (a.gate_dtype == SGA_BF16)
+    hipLaunchKernelGGL(k_mla_wq<true>, grid, dim3(512), kWqSmem, s, a, qpw);
+  else
+    hipLaunchKernelGGL(k_mla_wq<false>, grid, dim3(512), kWqSmem, s, a, qpw);
+  return hipGetLastError();
+}
+
 template <bool kMx, bool kFuse, bool kPaged>
 static void launch_split8_rp(const MlaArgs &a, uint16_t *opart, float2 *ml, int R, int S, hipStream_t s) {
   if (R == 4)
@@ -717,6 +1046,7 @@ static void launch_split8_r(const MlaArgs &a, uint16_t *opart, float2 *ml, int R
 
 hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (!a.fuse && mla_whole_query_path(a.T, a.kv_dtype, a.meta.page_shift)) return launch_wq(a, s);
   int R, S;
   mla_plan(a.T, a.k, &R, &S);
   uint16_t *opart = (uint16_t *)ws;
@@ -735,6 +1065,7 @@ hipError_t launch_mla_split(const MlaArgs &a, void *ws, hipStream_t s) {
 
 hipError_t launch_mla_combine(const MlaArgs &a, const void *ws, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (!a.fuse && mla_whole_query_path(a.T, a.kv_dtype, a.meta.page_shift)) return hipSuccess;  // written whole
   int R, S;
   mla_plan(a.T, a.k, &R, &S);
   const uint16_t *opart = (const uint16_t *)ws;

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void k_topk_hist0(SeqMeta m, const float *__re
   const int t = blockIdx.y;
   int64_t start;
   const int n = query_candidates(m, t, &start);
-  if (blockIdx.x == 0 && threadIdx.x == 0) ws.ncand[t] = n;
+  if (blockIdx.x == 0 && threadIdx.x == 0) ws.ncand[t] = make_int2(n, (int32_t)start);
   const int c0 = blockIdx.x * kTopkChunk;
   if (c0 >= n) return;
   // all of this thread's scores are requested before the histogram is
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_select(SeqMeta m, int k,
   float v[kSelPer];
   load_scores<kVec>(row, stride, c0 + tid * kSelPer, v);
 
-  const int n = ws.ncand[t];
+  const int n = ws.ncand[t].x;
   if (n <= k) {
     // every candidate is kept: positions 0..n-1, then -1 (no candidates for
     // k_topk_finish)
@@ -288,7 +288,9 @@ __global__ __launch_bounds__(kFinBlock) void k_topk_finish(int k, TopkWs ws, int
   __shared__ int res[2];
   const int t = blockIdx.x;
   int32_t *out = topk_idx + (size_t)t * k;
-  finish_query<kFinBlock>(k, ws, t, hist, scratch, res, [&](uint32_t o, int32_t pos) { out[o] = pos; });
+  FinishInput<kFinBlock> in;
+  finish_request(ws, t, in);
+  finish_query<kFinBlock>(k, ws, t, in, hist, scratch, res, [&](uint32_t o, int32_t pos) { out[o] = pos; });
 }
 
 }  // namespace
@@ -308,7 +310,7 @@ static size_t list_q_stride(int max_kv_len) {
 size_t topk_ws_bytes(int T, int max_kv_len) {
   size_t nch = ((size_t)max_kv_len + kTopkChunk - 1) / kTopkChunk;
   return align256((size_t)T * list_q_stride(max_kv_len) * 4) + align256((size_t)T * sizeof(uint4)) +
-         align256((size_t)T * sizeof(int32_t)) + align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
+         align256((size_t)T * sizeof(int2)) + align256((size_t)T * nch * kTopkChunk * sizeof(uint2));
 }
 
 TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
@@ -320,8 +322,8 @@ TopkWs topk_ws_carve(void *ws, int T, int max_kv_len) {
   p += align256((size_t)T * w.list_q_stride * 4);
   w.thr = (uint4 *)p;
   p += align256((size_t)T * sizeof(uint4));
-  w.ncand = (int32_t *)p;
-  p += align256((size_t)T * sizeof(int32_t));
+  w.ncand = (int2 *)p;
+  p += align256((size_t)T * sizeof(int2));
   w.entries = (uint2 *)p;
   return w;
 }

@@ -143,3 +143,48 @@ def test_mla_no_valid_rows():
     out, lse = _run_mla(case, idx)
     assert torch.count_nonzero(out.float()) == 0
     assert bool(torch.all(torch.isneginf(lse)))
+
+
+# More than twice as many queries as CUs: the whole-query kernel (bf16 rows,
+# contiguous cache) takes several queries per workgroup and writes outputs
+# directly. Short index lists keep the oracle cheap while every workgroup
+# crosses many query and 128-row chunk boundaries; k = 200 leaves a partial
+# chunk and a partial tile; some queries see fewer than k positions (padded
+# lists) and one has no valid entry at all.
+WQ_LENS = [700, 300, 1000, 450, 2500]
+
+
+def _wq_case(k, seed, gated=True, out_dtype=None):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    T = 2 * cus + 37
+    rng = np.random.default_rng(seed)
+    queries = []
+    for i in range(T):
+        b = i % len(WQ_LENS)
+        queries.append((b, int(rng.integers(0, WQ_LENS[b]))))
+    return make_custom(WQ_LENS, queries, dims=dict(FULL_DIMS, topk=k), precision="bf16", seed=seed,
+                       device="cuda", gated=gated, out_dtype=out_dtype, softmax_scale=1 / 24)
+
+
+@pytest.mark.parametrize("k,out_dtype", [(256, "bf16"), (200, "f32")])
+def test_mla_whole_queries(k, out_dtype):
+    case = _wq_case(k, 13 + k, out_dtype=out_dtype)
+    ref, idx = _oracle(case)
+    empty = 7
+    idx[empty] = -1
+    say(f"case mla whole queries k={k} out={out_dtype}, {case.num_q} queries")
+    out, lse = _run_mla(case, idx)
+    keep = np.array([t for t in range(case.num_q) if t != empty])
+    kt = torch.as_tensor(keep, device="cuda")
+    sub = {"y": ref["y"][keep], "lse": ref["lse"][keep]}
+    _compare(case, out[kt], lse[kt], sub, f"whole/{k}")
+    assert torch.count_nonzero(out[empty].float()) == 0
+    assert bool(torch.all(torch.isneginf(lse[empty])))
+
+
+def test_mla_whole_queries_ungated():
+    case = _wq_case(256, 21, gated=False)
+    ref, idx = _oracle(case)
+    say(f"case mla whole queries ungated, {case.num_q} queries")
+    out, lse = _run_mla(case, idx, gate=None)
+    _compare(case, out, lse, ref, "whole/ungated")
