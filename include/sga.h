@@ -9,10 +9,10 @@
  *     blocks), attention reads only those latent rows, and a per-head
  *     learned gate multiplies the attention result ahead of Wo;
  *   - "SK Telecom Opens A.X K2: 688B Parameters and One Telling Benchmark",
- *     section "Sparse Gated Attention" and its block-diagram caption (indexer
- *     and top-k selector feed MLA; a sigmoid output gate);
- *   - "A.X K2 Technical Report", section 2 (MLA backbone with a head-specific
- *     output gate) and section 3.4 (Stage 3C: the indexer's selection holds
+ *     section "Sparse Gated Attention" and its block-diagram caption (the
+ *     index scores pick the rows MLA reads; a sigmoid gate on the output);
+ *   - "A.X K2 Technical Report", section 2 (an MLA backbone whose heads each
+ *     gate their own output) and section 3.4 (Stage 3C: the indexer's selection holds
  *     2,048 positions for each query).
  * The pages print no formula. The operations below implement these readings:
  *   scores  I[t,s] = sum_h w[t,h] * max(0, qI[t,h,:] . kI[s,:])   for s <= p_t

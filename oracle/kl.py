@@ -7,7 +7,7 @@ learns from a KL objective that pulls its scores toward the attention
 weights, evaluated only on the sparse selection right from the beginning of
 that stage); "A.X-K2: a sparse-attention upgrade that
 costs nothing, trained natively in FP8", section "Sparse Gated Attention"
-(the indexer imitates the already gated attention distribution). The pages
+(the indexer learns to follow where the gated attention puts its weight). The pages
 give no formula. Readings, following the published form of the indexer
 design the report contrasts itself with:
   * for query t with selected set S_t, the target is the attention

@@ -49,8 +49,8 @@ import numpy as np
 
 
 # --------------------------------------------------------------------------
-# step 1: indexer scores  ([AK2-ART], [AK2-NEWS], [AK2-CARD]: a lightweight
-# indexer scores every cached key for each query; readings R1, R2, R5)
+# step 1: indexer scores  ([AK2-ART], [AK2-NEWS], [AK2-CARD]: a cheap indexer
+# rates each cached key for each query; readings R1, R2, R5)
 # --------------------------------------------------------------------------
 def visible_count(q_pos: int, kv_len: int) -> int:
     """Number of candidate positions of a query: positions 0..q_pos that are cached (R5)."""
@@ -156,7 +156,7 @@ def attend(q_t: np.ndarray, rows: np.ndarray, tau: float, d_latent: int):
 
 
 # --------------------------------------------------------------------------
-# step 4: head-specific sigmoid output gate  ([AK2-ART]: learned,
+# step 4: per-head sigmoid gate on the output  ([AK2-ART]: learned,
 # input-dependent gate on the attention output before Wo; [AK2-NEWS] caption:
 # sigmoid output gate; [AK2-CARD]: head-specific; reading R9)
 # --------------------------------------------------------------------------

@@ -1,8 +1,8 @@
 // Indexer score pass: I[t,s] = sum_h w[t,h] * max(0, qI[t,h,:] . kI[s,:]) for s < n_t.
 //
 // Source: "A.X-K2: a sparse-attention upgrade that costs nothing, trained
-// natively in FP8", section "Sparse Gated Attention" (a lightweight indexer
-// scores every cached key for each query); "A.X-K2" model card, section
+// natively in FP8", section "Sparse Gated Attention" (a cheap indexer rates
+// each cached key for each query); "A.X-K2" model card, section
 // "Sparse Gated Attention (SGA)" (the indexer rates and orders the cached
 // candidates). The weighted-ReLU form is the reading this library implements.
 //

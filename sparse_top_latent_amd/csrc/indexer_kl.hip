@@ -1,6 +1,6 @@
 // Indexer KL loss restricted to the sparse selection, and its gradients (the
 // training side of the indexer, "A.X K2 Technical Report" section 3.4: a KL
-// loss aligns the indexer's scores with the attention distribution, computed
+// loss pulls the indexer's ranking toward the attention weights, computed
 // over the sparse selection from the start).
 //
 // For query t with selected positions S_t (the forward's top-k list) and the
