@@ -48,6 +48,20 @@ def test_layer_full_dims_ragged_and_degenerate():
     compare_layer(case, label="ragged")
 
 
+def test_layer_workgroups_with_partial_load_batches():
+    # 10 queries over sequences up to 30,001 keys: the decode indexer then
+    # gives each workgroup 12 steps of 64 keys, not a multiple of the groups
+    # a wave keeps in flight, and every query but the short ones spans
+    # several workgroups (the keys past a workgroup's last step belong to the
+    # next one and must not enter its scores or level-0 counts)
+    lens = [20000, 4097, 64, 1, 9000, 12345, 2048, 30001]
+    qs = [(b, n - 1) for b, n in enumerate(lens)] + [(0, 777), (5, 4096)]
+    case = make_custom(lens, qs, dims=FULL_DIMS, precision="bf16", seed=51, device="cuda",
+                       softmax_scale=1 / 24)
+    say("case layer partial load batches")
+    compare_layer(case, label="partial batches")
+
+
 def test_layer_out_of_range_metadata_is_empty():
     # a query on an empty sequence, a bad sequence id, and a position past the cache
     case = make_custom([5000, 0], [(0, 4999), (1, 0), (0, 4999), (0, 4999)], dims=FULL_DIMS,
