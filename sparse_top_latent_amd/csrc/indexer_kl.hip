@@ -380,6 +380,116 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
   }
 }
 
+// The same for bf16 latent rows, with the workgroup's 64 rows copied once
+// into LDS (LDS-DMA, rows 0..31 and 32..63 as two batches) and every wave
+// reading its MFMA operands from there, instead of each of the 4 waves
+// loading every row from memory. Row r's 16-byte chunk c sits at chunk slot
+// r * 72 + (c ^ ((r >> 1) & 7)) (the swizzle spreads a 16-row operand read
+// over the LDS banks).
+constexpr int kKlRowChunks = 72;                         // 16-byte chunks per 576-wide bf16 row
+constexpr size_t kKlLdsRows = (size_t)kKlRows * kKlRowChunks * 16;  // 73,728 B
+__device__ __forceinline__ int kl_swz(int r, int c) { return r * kKlRowChunks + (c ^ ((r >> 1) & 7)); }
+
+template <bool kScores>
+__global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char tile[];  // [64 rows][72 chunks]
+  __shared__ float part[kKlThreads / 64][kKlRows];
+  __shared__ float spart[kKlThreads / 64][kKlRows];
+  __shared__ int64_t rows[kKlRows];
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t start;
+  const int n = query_candidates(a.meta, t, &start);
+  if (tid < kKlRows) {
+    const int r = r0 + tid;
+    rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
+  }
+  __syncthreads();  // rows[] ready
+  // the copies: chunk slot c = u * 256 + tid holds row c / 72, chunk
+  // (c % 72) ^ swizzle; unselected rows copy any 16 readable bytes (their
+  // logits are never used)
+#pragma unroll
+  for (int u = 0; u < 18; ++u) {
+    const int c = u * 256 + tid;
+    const int r = c / kKlRowChunks;
+    const int col = (c - r * kKlRowChunks) ^ ((r >> 1) & 7);
+    const int64_t row = rows[r];
+    const void *src = row >= 0 ? (const void *)((const uint16_t *)a.kv + row * a.D + col * 8)
+                               : (const void *)(a.q);  // any readable 16 bytes; masked below
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tile + (u * 256 + wave * 64) * 16), 16, 0, 0);
+  }
+  const int head = wave * 16 + c16;
+  const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
+  v4i qreg[kKlKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
+  const float lse_h = a.lse[(size_t)t * 64 + head];
+  v4i qireg[4];
+  float w_h = 0.0f;
+  if (kScores) {
+    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+    w_h = a.w[(size_t)t * 64 + head];
+  }
+  __syncthreads();  // every copy has landed (the barrier waits for this wave's loads first)
+#pragma unroll
+  for (int rt = 0; rt < kKlRows / 16; ++rt) {
+    const int rr = rt * 16 + c16;
+    const int64_t row = rows[rr];
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKlKsteps; ++ks) {
+      const v4i av = *(const v4i *)(tile + kl_swz(rr, 4 * ks + g) * 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, qreg[ks]),
+                                                     acc, 0, 0, 0);
+    }
+    v4f zc = {0.f, 0.f, 0.f, 0.f};
+    if (kScores) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0}
+                               : fp8x8_to_bf16(*(const uint2 *)((const uint8_t *)a.k_idx + row * 128 + ks * 32 + 8 * g));
+        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
+                                                    zc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = rt * 16 + 4 * g + i;
+      float e = rows[j] >= 0 ? __expf(a.tau * acc[i] - lse_h) : 0.0f;
+      e += __shfl_xor(e, 1);
+      e += __shfl_xor(e, 2);
+      e += __shfl_xor(e, 4);
+      e += __shfl_xor(e, 8);
+      if (c16 == 0) part[wave][j] = e;
+      if (kScores) {
+        float sc = fmaxf(zc[i], 0.0f) * w_h;
+        sc += __shfl_xor(sc, 1);
+        sc += __shfl_xor(sc, 2);
+        sc += __shfl_xor(sc, 4);
+        sc += __shfl_xor(sc, 8);
+        if (c16 == 0) spart[wave][j] = sc;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kKlRows && r0 + tid < a.k) {
+    float m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
+    a.mass[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? m : 0.0f;
+    if (kScores) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kKlThreads / 64; ++w) sc += spart[w][tid];
+      a.score[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? sc + 0.0f : -INFINITY;
+    }
+  }
+}
+
 __device__ __forceinline__ float block_sum(float v, float *red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   __syncthreads();
@@ -642,15 +752,26 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
                               160 * 1024);
     (void)hipFuncSetAttribute((const void *)k_kl_backward<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
+    (void)hipFuncSetAttribute((const void *)k_kl_mass_lds<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kKlLdsRows);
+    (void)hipFuncSetAttribute((const void *)k_kl_mass_lds<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kKlLdsRows);
     (void)hipGetLastError();
     return true;
   }();
   (void)attr;
   const dim3 grid(a.chunks, T);
+  const bool lds_rows = kv_dtype == SGA_BF16;  // bf16 rows are staged in LDS once per workgroup
   if (mfma && HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN) {
-    hipLaunchKernelGGL(k_kl_mass_mfma<true>, grid, dim3(kKlThreads), 0, s, a);
+    if (lds_rows)
+      hipLaunchKernelGGL(k_kl_mass_lds<true>, grid, dim3(kKlThreads), kKlLdsRows, s, a);
+    else
+      hipLaunchKernelGGL(k_kl_mass_mfma<true>, grid, dim3(kKlThreads), 0, s, a);
   } else if (mfma) {
-    hipLaunchKernelGGL(k_kl_mass_mfma<false>, grid, dim3(kKlThreads), 0, s, a);
+    if (lds_rows)
+      hipLaunchKernelGGL(k_kl_mass_lds<false>, grid, dim3(kKlThreads), kKlLdsRows, s, a);
+    else
+      hipLaunchKernelGGL(k_kl_mass_mfma<false>, grid, dim3(kKlThreads), 0, s, a);
     hipLaunchKernelGGL(k_kl_rows<false>, grid, dim3(kKlThreads), ((size_t)HI * kl_ld(DI) + 64) * 4, s, a);
   } else {
     hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
