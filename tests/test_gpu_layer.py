@@ -127,3 +127,44 @@ def test_layer_prefill_q4096_n128k_sampled():
     assert len(qs) >= 64 and qs[0] == 0 and qs[-1] == 4095
     say(f"case layer prefill_q4096_n128k ({len(qs)} sampled queries)")
     compare_layer(case, qs, label="prefill")
+
+
+def heavy_tail_index(case, seed):
+    """Index inputs whose top scores spread over many level-0 bins with ties.
+
+    One index head scores each key by its first channel alone (w one-hot, the
+    query's index matrix a unit vector), so a key's score is its first channel.
+    That channel takes exact E4M3FN integers: each of the 53 largest (18 ..
+    448) with probability 33/65536, the value 1 otherwise. Every score is then
+    an exact integer, each value in its own level-0 bin (3 mantissa bits), and
+    the 2,048 largest of a 128K-key query spread over about 30 bins with some
+    65 keys each: a slot's 15-entry list head no longer reaches the threshold
+    bin, and the k-th key has ties of which only the lowest positions are kept.
+    """
+    from sga_inputs.gen import uniform_int
+    vals = [v for v in range(1, 449) if float(torch.tensor(float(v)).to(torch.float8_e4m3fn).float()) == v]
+    top = torch.tensor(vals[::-1][:53], dtype=torch.float32, device="cuda")
+    codes = torch.cat([top, torch.ones(1, device="cuda")]).to(torch.float8_e4m3fn).view(torch.uint8)
+    rows = case.k_idx.shape[0]
+    r = uniform_int((rows,), seed, "heavy_hi", 0, 255, device="cuda").to(torch.int64) * 256 + \
+        uniform_int((rows,), seed, "heavy_lo", 0, 255, device="cuda").to(torch.int64)
+    j = torch.where(r < 53 * 33, r // 33, torch.full_like(r, 53))
+    case.k_idx[:, 0] = codes[j]
+    case.q_idx.zero_()
+    case.q_idx[:, 0, 0] = int(torch.tensor(1.0).to(torch.float8_e4m3fn).view(torch.uint8))
+    case.w.zero_()
+    case.w[:, 0] = 1.0
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_layer_heavy_tail_scores_whole_lists_and_partial_ties(precision):
+    # the top-k select takes its threshold from the whole level-0 lists (the
+    # list heads stop above it), and the k-th key has ties of which only the
+    # lowest positions are kept
+    lens = [131072, 50000, 262144, 3000]
+    qs = [(0, 131071), (1, 49999), (2, 262143), (2, 100000), (0, 4095), (3, 2999), (1, 2047)]
+    case = make_custom(lens, qs, dims=FULL_DIMS, precision=precision, seed=61, device="cuda",
+                       softmax_scale=1 / 24)
+    heavy_tail_index(case, 61)
+    say(f"case layer heavy-tail scores ({precision})")
+    compare_layer(case, label=f"heavy tail {precision}")
