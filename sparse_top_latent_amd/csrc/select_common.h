@@ -102,43 +102,54 @@ __device__ __forceinline__ int wave_find_threshold_bin(const uint32_t *hist, uin
 // Level-0 threshold search of one wave over list heads held in registers:
 // lane l < nl holds a head e[0..15] (entry count, then up to 15 entries
 // bin << 20 | count in descending bin order). Same result as adding the heads
-// into a 4096-bin histogram and calling wave_find_threshold_bin, in two
-// passes over 64 bins each: first the 64 buckets of 64 bins (bin >> 6), then
-// the 64 bins of the bucket that holds the `want`-th element. `h` is 128
-// words of LDS used by this wave alone (its LDS operations take effect in
-// order). Returns the same result for every lane.
-__device__ __forceinline__ int wave_heads_threshold_bin(uint32_t *h, const uint32_t (&e)[16], int nl,
-                                                        uint32_t want, uint32_t *above) {
+// into a 4096-bin histogram and calling wave_find_threshold_bin: the bin b
+// such that the heads hold fewer than `want` keys above b and at least `want`
+// at or above it (*above: the keys above b), or -1 with *above the heads'
+// total when they hold fewer than `want`. The count of keys at or above a bin
+// never increases with the bin, so a binary search over the range of bins the
+// heads hold finds b; each probe is a per-lane sum over its entries and one
+// wave sum, all in registers (no LDS, so no same-address conflicts, which the
+// top bins shared by all slots would cause). Returns the same result for
+// every lane.
+__device__ __forceinline__ int wave_heads_threshold_bin(const uint32_t (&e)[16], int nl, uint32_t want,
+                                                        uint32_t *above) {
   const int lane = threadIdx.x & 63;
-  h[lane] = 0u;
-  h[64 + lane] = 0u;
-  if (lane < nl) {
+  uint32_t bins[15], cnts[15];
+  const uint32_t ne = lane < nl ? min(e[0], 15u) : 0u;
 #pragma unroll
-    for (int i = 1; i < 16; ++i)
-      if ((uint32_t)i <= e[0]) atomicAdd(&h[e[i] >> 26], e[i] & 0xFFFFFu);
+  for (int i = 0; i < 15; ++i) {
+    const bool ok = (uint32_t)i < ne;
+    bins[i] = e[i + 1] >> 20;
+    cnts[i] = ok ? (e[i + 1] & 0xFFFFFu) : 0u;
   }
-  // lane l takes bucket 63 - l: an inclusive scan over lanes is a suffix
-  // scan over buckets
-  const uint32_t cc = h[63 - lane];
-  const uint32_t inc = wave_inclusive_scan(cc);
-  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  // keys of the heads at or above bin x (the same value in every lane)
+  auto count_ge = [&](int x) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) c += bins[i] >= (uint32_t)x ? cnts[i] : 0u;
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(c), 63);
+  };
+  // the range of bins held: [lo, hi]
+  int hi = ne ? (int)bins[0] : -1, lo = ne ? (int)bins[ne - 1] : 4096;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    hi = max(hi, __shfl_xor(hi, d, 64));
+    lo = min(lo, __shfl_xor(lo, d, 64));
+  }
+  const uint32_t total = count_ge(0);
   if (total < want) {
     *above = total;
     return -1;
   }
-  const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(inc >= want)) - 1);
-  const uint32_t above_c = (uint32_t)__builtin_amdgcn_readlane((int)(inc - cc), L);
-  const uint32_t bucket = 63u - (uint32_t)L;
-  if (lane < nl) {
-#pragma unroll
-    for (int i = 1; i < 16; ++i)
-      if ((uint32_t)i <= e[0] && (e[i] >> 26) == bucket) atomicAdd(&h[64 + ((e[i] >> 20) & 63u)], e[i] & 0xFFFFFu);
+  // the largest x in [lo, hi] with count_ge(x) >= want (count_ge(lo) = total)
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_ge(mid) >= want) lo = mid; else hi = mid - 1;
   }
-  const uint32_t fc = h[64 + 63 - lane];
-  const uint32_t finc = above_c + wave_inclusive_scan(fc);
-  const int J = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(finc >= want)) - 1);
-  *above = (uint32_t)__builtin_amdgcn_readlane((int)(finc - fc), J);
-  return (int)(bucket << 6) + 63 - J;
+  *above = count_ge(lo + 1);
+  return lo;
 }
 
 // Writes the nonzero bins of a 4096-bin LDS level-0 histogram as the list of

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_select(SeqMeta m, int k,
   if (nslots <= 64) {
     if (wave == 0) {
       uint32_t ab;
-      const int b = wave_heads_threshold_bin(hist, wd, nslots, (uint32_t)k, &ab);
+      const int b = wave_heads_threshold_bin(wd, nslots, (uint32_t)k, &ab);
       // the heads are exact down to the lowest bin read from every cut list
       const bool cut = __ballot(lane < nslots && wd[0] > 15u && (int)(wd[15] >> 20) > b) != 0;
       const uint32_t cnt = lane < nslots ? head_count_ge(wd, (uint32_t)b) : 0u;
