@@ -14,9 +14,11 @@
 //   d_kI[s] += sum_h g_s w_h [z_hs > 0] qI_h  (added into the caller's buffer)
 //
 // Kernels per call:
-//   k_kl_mass_mfma  one workgroup per (64 selected rows, query), MI355X shapes:
-//                   the head-summed attention mass of each row, logits by bf16
-//                   MFMA with the query slice in VGPRs, and (FP8 index
+//   k_kl_mass_lds   one workgroup per (64 selected rows, query), MI355X shapes
+//   k_kl_mass_mfma  with bf16 rows (_lds) or MXFP8 rows (_mfma): the
+//                   head-summed attention mass of each row, logits by bf16
+//                   MFMA with the query slice in VGPRs (bf16 rows read from
+//                   one LDS copy of the workgroup's 64 rows), and (FP8 index
 //                   tensors) each row's indexer score;
 //   k_kl_rows       one workgroup per (64 rows, query): each row's indexer score
 //                   (and, for the other shapes, its attention mass, fp32 dot
