@@ -520,7 +520,7 @@ def indexer_kl_bench(args, case, prob, sga, torch):
     f_bf16, f_fp32 = indexer_kl_split(case, case.topk)
     ideal_ms = (f_bf16 / (BF16_PEAK_TFLOPS * 1e12) + f_fp32 / (FP32_PEAK_TFLOPS * 1e12)) * 1e3
     mixed_peak = flops / (ideal_ms * 1e-3) / 1e12
-    kl_roofline = {"bound": "mfma", "kernel": "indexer KL (5 kernels, per call)", "achieved": round(tflops, 2),
+    kl_roofline = {"bound": "mfma", "kernel": "indexer KL (k_kl_mass_lds, k_kl_grad, k_kl_reduce; per call)", "achieved": round(tflops, 2),
                    "peak": round(mixed_peak, 1), "unit": "TFLOP/s", "frac": round(tflops / mixed_peak, 4),
                    "flops_per_launch": flops, "bf16_mfma_flops": f_bf16, "fp32_flops": f_fp32,
                    "ideal_us": round(ideal_ms * 1e3, 2), "traffic": None}

@@ -297,9 +297,11 @@ sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dt
  * with bf16 q and 576-wide bf16 or MXFP8 rows, the attention logits q . kv
  * run on bf16 MFMA (MXFP8 rows expanded exactly to bf16); with 64 x 128 FP8
  * index tensors, z = q_idx . k_idx runs on bf16 MFMA too (E4M3FN values are
- * exact in bf16) and the gradient products d_q_idx and d_k_idx on fp32 MFMA
- * 16x16x4. Every other shape, and the softmax, loss and reductions, use the
- * fp32 vector ALUs. Workspace: sga_workspace_size(p, SGA_OP_INDEXER_KL).
+ * exact in bf16), and so do the gradient products d_q_idx and d_k_idx: their
+ * fp32 factor g w [z > 0] enters as three bf16 parts whose sum carries its
+ * 24 significant bits, so every product is exact and accumulates in fp32.
+ * Every other shape, and the softmax, loss and reductions, use the fp32
+ * vector ALUs. Workspace: sga_workspace_size(p, SGA_OP_INDEXER_KL).
  */
 sga_status sga_indexer_kl(const sga_problem *p, const void *q_idx, const float *w,
                           const void *k_idx, const void *q, const void *kv,

@@ -23,12 +23,14 @@
 //   k_kl_rows       one workgroup per (64 rows, query): each row's indexer score
 //                   (and, for the other shapes, its attention mass, fp32 dot
 //                   products from q in LDS);
-//   k_kl_loss       one workgroup per query: the two normalisations, the loss
-//                   and g;
-//   k_kl_backward   one workgroup per (64 rows, query): z again and the
-//                   gradient products (bf16 and fp32 MFMA for 64 x 128 FP8
-//                   index tensors), d_kI by fp32 atomics, per-chunk partials
-//                   of d_w and d_qI;
+//   k_kl_grad       one workgroup per (64 rows, query), 64 FP8 index heads x
+//                   128 dims: the query's normalisers and loss, g, z again
+//                   (bf16 MFMA) and both gradient products (bf16 MFMA on an
+//                   exact three-part bf16 split of g w [z > 0]), d_kI by fp32
+//                   atomics, per-chunk partials of d_w and d_qI;
+//   k_kl_loss,      the other shapes: one workgroup per query for the two
+//   k_kl_backward   normalisations, the loss and g, then one per (64 rows,
+//                   query) for z and the gradient products on the vector ALUs;
 //   k_kl_reduce     sums the partials over the chunks (fixed order).
 // The softmax, loss and reductions are fp32 on the vector ALUs.
 
@@ -430,11 +432,21 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
   const float lse_h = a.lse[(size_t)t * 64 + head];
   v4i qireg[4];
   float w_h = 0.0f;
+  // the index keys of the lane's rows, requested together with the row
+  // copies (unselected rows read row 0; their z is masked below)
+  uint2 kraw[kScores ? kKlRows / 16 : 1][4];
   if (kScores) {
     const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
     w_h = a.w[(size_t)t * 64 + head];
+#pragma unroll
+    for (int rt = 0; rt < kKlRows / 16; ++rt) {
+      const int64_t row = rows[rt * 16 + c16];
+      const uint8_t *kr = (const uint8_t *)a.k_idx + (row < 0 ? 0 : row) * 128 + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = *(const uint2 *)(kr + ks * 32);
+    }
   }
   __syncthreads();  // every copy has landed (the barrier waits for this wave's loads first)
 #pragma unroll
@@ -452,8 +464,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
     if (kScores) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0}
-                               : fp8x8_to_bf16(*(const uint2 *)((const uint8_t *)a.k_idx + row * 128 + ks * 32 + 8 * g));
+        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[rt][ks]);
         zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
                                                     zc, 0, 0, 0);
       }
@@ -492,21 +503,25 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
   }
 }
 
+// kLdsOnly: the barriers wait for LDS operations only (lds_barrier), so
+// global loads the caller has in flight stay in flight
+template <bool kLdsOnly = false>
 __device__ __forceinline__ float block_sum(float v, float *red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  __syncthreads();
+  if (kLdsOnly) lds_barrier(); else __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  if (kLdsOnly) lds_barrier(); else __syncthreads();
   float s = 0.0f;
   for (int i = 0; i < kKlThreads / 64; ++i) s += red[i];
   return s;
 }
 
+template <bool kLdsOnly = false>
 __device__ __forceinline__ float block_max(float v, float *red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  __syncthreads();
+  if (kLdsOnly) lds_barrier(); else __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  if (kLdsOnly) lds_barrier(); else __syncthreads();
   float s = -INFINITY;
   for (int i = 0; i < kKlThreads / 64; ++i) s = fmaxf(s, red[i]);
   return s;
@@ -543,9 +558,8 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_loss(KlArgs a) {
   if (threadIdx.x == 0) a.loss[t] = mx > -INFINITY ? loss : 0.0f;
 }
 
-// kMfmaZ (64 FP8 index heads x 128 dims): z by bf16 MFMA as in
-// k_kl_mass_mfma, wave w taking index heads 16 w .. 16 w + 15
-template <bool kMfmaZ>
+// The backward for the shapes k_kl_grad does not take (fp32 tensors, other
+// head counts): z, then both gradient products on the fp32 vector ALUs.
 __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // rows of qi and kr are padded by four words: 16-byte aligned, and the z
@@ -582,43 +596,16 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     for (int e = 0; e < 8; ++e) kr[j * ld + d + e] = v[e];
   }
   __syncthreads();
-  if (kMfmaZ) {
-    const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-    const int h = wave * 16 + c16;
-    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + h) * 128;
-    v4i qireg[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
-#pragma unroll
-    for (int rt = 0; rt < kKlRows / 16; ++rt) {
-      const int64_t row = rows[rt * 16 + c16];
-      v4f zc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0}
-                               : fp8x8_to_bf16(*(const uint2 *)((const uint8_t *)a.k_idx + row * 128 + ks * 32 + 8 * g));
-        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
-                                                    zc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = rt * 16 + 4 * g + i;
-        gz[j * kGzLd + h] = zc[i] > 0.0f ? gr[j] * wsh[h] : 0.0f;
-        rz[j * kGzLd + h] = gr[j] * fmaxf(zc[i], 0.0f);
-      }
+  // z of (row j, index head h) for 4 threads per row
+  const int j = tid >> 2, hg = tid & 3;
+  for (int h = hg; h < a.HI; h += 4) {
+    float z = 0.0f;
+    for (int d = 0; d < a.DI; d += 4) {
+      const float4 x = *(const float4 *)(qi + h * ld + d), y = *(const float4 *)(kr + j * ld + d);
+      z = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, z))));
     }
-  } else {
-    // z of (row j, index head h) for 4 threads per row
-    const int j = tid >> 2, hg = tid & 3;
-    for (int h = hg; h < a.HI; h += 4) {
-      float z = 0.0f;
-      for (int d = 0; d < a.DI; d += 4) {
-        const float4 x = *(const float4 *)(qi + h * ld + d), y = *(const float4 *)(kr + j * ld + d);
-        z = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, z))));
-      }
-      gz[j * kGzLd + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
-      rz[j * kGzLd + h] = gr[j] * fmaxf(z, 0.0f);
-    }
+    gz[j * kGzLd + h] = z > 0.0f ? gr[j] * wsh[h] : 0.0f;
+    rz[j * kGzLd + h] = gr[j] * fmaxf(z, 0.0f);
   }
   __syncthreads();
   const size_t chunk = (size_t)t * a.chunks + blockIdx.x;
@@ -626,38 +613,6 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
     float s = 0.0f;
     for (int j = 0; j < kKlRows; ++j) s += rz[j * kGzLd + h];
     a.part_w[chunk * a.HI + h] = s;
-  }
-  if (kMfmaZ) {
-    // 64 x 128 shapes: both gradient products by fp32 MFMA 16x16x4 (fp32
-    // operands, as g is too small for bf16 at this precision). Wave w takes
-    // index-head tile w of d_qI = gz^T kr and row tile w of d_kI = gz qi,
-    // each over the 8 tiles of 16 d.
-    const int lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, c16 = lane & 15;
-    v4f accq[8], acck[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) accq[dt] = acck[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int ks = 0; ks < 16; ++ks) {
-      const int kk = ks * 4 + g4;  // row (d_qI) or index head (d_kI) of this lane's k
-      const float aq = gz[kk * kGzLd + wave * 16 + c16];          // A[i = head][k = row]
-      const float ak = gz[(wave * 16 + c16) * kGzLd + kk];        // A[i = row][k = head]
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        accq[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, kr[kk * ld + dt * 16 + c16], accq[dt], 0, 0, 0);
-        acck[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, qi[kk * ld + dt * 16 + c16], acck[dt], 0, 0, 0);
-      }
-    }
-    // C[i = 4 g4 + r][j = c16] of each tile
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g4 + r, d = dt * 16 + c16;
-        a.part_q[chunk * 64 * 128 + (size_t)(wave * 16 + i) * 128 + d] = accq[dt][r];
-        const int j = wave * 16 + i;
-        if (rows[j] >= 0 && gr[j] != 0.0f) atomicAdd(a.d_k_idx + rows[j] * 128 + d, acck[dt][r]);
-      }
-    return;
   }
   // four consecutive outputs per thread (16-byte LDS reads)
   for (int i = 4 * tid; i < a.HI * a.DI; i += 4 * kKlThreads) {
@@ -687,19 +642,317 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_backward(KlArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_kl_grad: the loss and the whole backward of one (64 selected rows, query)
+// workgroup for 64 FP8 index heads x 128 dims, in one kernel.
+//
+// Every workgroup of a query first reduces the query's scores and masses
+// (2 x k floats, held in L2 after the mass kernel) to the two normalisers:
+// log Z of the score softmax and the total mass; the first workgroup also
+// adds up the loss. Each thread then has g for its own rows.
+//
+// The gradient products are bf16 MFMA 16x16x32 with an exact three-way split
+// of the fp32 factor G[j,h] = g_j w_h [z_jh > 0] = G1 + G2 + G3 (each part the
+// bf16 rounding of what the previous parts leave; the three carry 24
+// significant bits, fp32's precision), while the other operand, the E4M3FN
+// index keys or query, is exact in bf16. Every product is then exact and the
+// MFMA accumulates in fp32, as an fp32 product would:
+//   d_qI[h,d] = sum_j G[j,h] kI[j,d]   (A = G^T [h][j], B = kI^T [d][j])
+//   d_kI[j,d] = sum_h G[j,h] qI[h,d]   (A = G   [j][h], B = qI^T [d][h])
+// The two products run one after the other through the same two LDS arrays
+// (the operand of each lane is 8 consecutive k values: one 16-byte read).
+// ---------------------------------------------------------------------------
+constexpr int kGradLd = 72;  // bf16 row stride of the operand arrays (36 dwords: 16 rows' 16-byte reads hit distinct banks)
+constexpr int kGradMaxPer = 16;  // scores per thread for k <= 4096
+
+__device__ __forceinline__ uint16_t bf16_bits_rn(float x) {
+  // round to nearest even (the parts are finite; NaN never reaches here)
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// x = p[0] + p[1] + p[2] + (a remainder below 2^-24 |x|), each part a bf16
+__device__ __forceinline__ void split3_bf16(float x, uint16_t (&p)[3]) {
+  p[0] = bf16_bits_rn(x);
+  const float r1 = x - bf16_bits_to_f32(p[0]);
+  p[1] = bf16_bits_rn(r1);
+  const float r2 = r1 - bf16_bits_to_f32(p[1]);
+  p[2] = bf16_bits_rn(r2);
+}
+
+__global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t opA[3][64 * kGradLd];  // G^T, then G (three parts)
+  __shared__ __attribute__((aligned(16))) uint16_t opB[128 * kGradLd];    // kI^T, then qI^T
+  __shared__ float red[kKlThreads / 64];
+  __shared__ float gsh[kKlRows];
+  __shared__ int64_t rows[kKlRows];
+  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int head = wave * 16 + c16;
+  // everything that depends on nothing else is requested first: the index
+  // query of this wave's 16 heads (bf16 B operands, exact) and their weights,
+  // the query's scores and masses, and the selected positions
+  const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
+  v4i qireg[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+  const float w_h = a.w[(size_t)t * 64 + head];
+  const float *sc = a.score + (size_t)t * a.k, *ms = a.mass + (size_t)t * a.k;
+  float scv[kGradMaxPer], msv[kGradMaxPer];
+#pragma unroll
+  for (int i = 0; i < kGradMaxPer; ++i) {
+    const int r = tid + i * kKlThreads;
+    scv[i] = r < a.k ? sc[r] : -INFINITY;
+    msv[i] = r < a.k ? ms[r] : 0.0f;
+  }
+  int64_t start;
+  const int n = query_candidates(a.meta, t, &start);
+  if (tid < kKlRows) {
+    const int r = r0 + tid;
+    rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
+  }
+  __syncthreads();  // rows[] ready
+  // the index keys of the lane's z rows; they stay in flight through the
+  // normalisers below (whose barriers wait for LDS operations only)
+  uint2 kraw[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t row = rows[rt * 16 + c16];
+    const uint8_t *kr = (const uint8_t *)a.k_idx + (row < 0 ? 0 : row) * 128 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = *(const uint2 *)(kr + ks * 32);
+  }
+
+  // the query's normalisers (as k_kl_loss computes them)
+  float mx = -INFINITY, tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kGradMaxPer; ++i) {
+    mx = fmaxf(mx, scv[i]);
+    tot += msv[i];
+  }
+  mx = block_max<true>(mx, red);
+  tot = block_sum<true>(tot, red);
+  float zs = 0.0f;
+  if (mx > -INFINITY)
+#pragma unroll
+    for (int i = 0; i < kGradMaxPer; ++i)
+      if (tid + i * kKlThreads < a.k) zs += __expf(scv[i] - mx);
+  zs = block_sum<true>(zs, red);
+  const float lz = mx + __logf(zs);
+  if (blockIdx.x == 0) {  // uniform over the workgroup
+    float loss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGradMaxPer; ++i) {
+      if (tid + i * kKlThreads < a.k && scv[i] > -INFINITY) {
+        const float tg = tot > 0.0f ? msv[i] / tot : 0.0f;
+        if (tg > 0.0f) loss += tg * (__logf(tg) - (scv[i] - lz));
+      }
+    }
+    loss = block_sum<true>(loss, red);
+    if (tid == 0) a.loss[t] = mx > -INFINITY ? loss : 0.0f;
+  }
+  // g of the workgroup's rows: row j's score and mass sit in thread
+  // (r0 + j) % 256, entry (r0 + j) / 256
+  {
+    const int owner = r0 % kKlThreads;  // r0 is a multiple of 64: rows j < 64 stay within one entry
+    const int i0 = r0 / kKlThreads;
+    if (tid >= owner && tid < owner + kKlRows) {
+      const int j = tid - owner;
+      float gv = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kGradMaxPer; ++i)
+        if (i == i0 && r0 + j < a.k && rows[j] >= 0 && scv[i] > -INFINITY)
+          gv = __expf(scv[i] - lz) - (tot > 0.0f ? msv[i] / tot : 0.0f);
+      gsh[j] = gv;
+    }
+  }
+  lds_barrier();  // gsh[] ready
+
+  // z = kI . qI^T per 16-row tile (this wave's 16 heads); wave w also stores
+  // k-step w of the keys transposed (kI^T [d][j]) for d_qI
+  v4f zc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t row = rows[rt * 16 + c16];
+    zc[rt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v4i kb = row < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[rt][ks]);
+      zc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
+                                                       __builtin_bit_cast(v8bf, qireg[ks]), zc[rt], 0, 0, 0);
+      if (ks == wave) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          opB[(ks * 32 + 8 * g + e) * kGradLd + rt * 16 + c16] =
+              (uint16_t)((uint32_t)kb[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+  // G for rows rt * 16 + 4 g + i and this lane's head, its parts into G^T
+  // [h][j] (four consecutive j per 8-byte store), and d_w's partial sum
+  float gval[4][4];
+  float rzs = 0.0f;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    uint16_t pp[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = rt * 16 + 4 * g + i;
+      const float gj = gsh[j];
+      gval[rt][i] = zc[rt][i] > 0.0f ? gj * w_h : 0.0f;
+      rzs += gj * fmaxf(zc[rt][i], 0.0f);
+      split3_bf16(gval[rt][i], pp[i]);
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const uint2 v = make_uint2((uint32_t)pp[0][p] | ((uint32_t)pp[1][p] << 16),
+                                 (uint32_t)pp[2][p] | ((uint32_t)pp[3][p] << 16));
+      *(uint2 *)&opA[p][head * kGradLd + rt * 16 + 4 * g] = v;
+    }
+  }
+  rzs += __shfl_xor(rzs, 16);
+  rzs += __shfl_xor(rzs, 32);
+  const size_t chunk = (size_t)t * a.chunks + blockIdx.x;
+  if (g == 0) a.part_w[chunk * 64 + head] = rzs;
+  __syncthreads();  // G^T and kI^T complete
+
+  // d_qI: wave w takes heads 16 w .. 16 w + 15, all 128 d
+  {
+    v4f acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i av[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) av[p] = *(const v4i *)&opA[p][head * kGradLd + ks * 32 + 8 * g];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4i bv = *(const v4i *)&opB[(dt * 16 + c16) * kGradLd + ks * 32 + 8 * g];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[p]),
+                                                            __builtin_bit_cast(v8bf, bv), acc[dt], 0, 0, 0);
+      }
+    }
+    // C[i = head 16 w + 4 g + r][j = d]
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        a.part_q[chunk * 64 * 128 + (size_t)(wave * 16 + 4 * g + r) * 128 + dt * 16 + c16] = acc[dt][r];
+  }
+  __syncthreads();  // every wave is done with G^T and kI^T
+
+  // G [j][h] parts and qI^T [d][h] for d_kI
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t pp[3];
+      split3_bf16(gval[rt][i], pp);
+      const int j = rt * 16 + 4 * g + i;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) opA[p][j * kGradLd + head] = pp[p];
+    }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      opB[(ks * 32 + 8 * g + e) * kGradLd + head] = (uint16_t)((uint32_t)qireg[ks][e >> 1] >> (16 * (e & 1)));
+  __syncthreads();
+
+  // d_kI: wave w takes rows 16 w .. 16 w + 15, all 128 d; added into the
+  // caller's buffer
+  {
+    v4f acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i av[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) av[p] = *(const v4i *)&opA[p][(wave * 16 + c16) * kGradLd + ks * 32 + 8 * g];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4i bv = *(const v4i *)&opB[(dt * 16 + c16) * kGradLd + ks * 32 + 8 * g];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[p]),
+                                                            __builtin_bit_cast(v8bf, bv), acc[dt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = wave * 16 + 4 * g + r;
+      const int64_t row = rows[j];
+      if (row >= 0 && gsh[j] != 0.0f)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) atomicAdd(a.d_k_idx + row * 128 + dt * 16 + c16, acc[dt][r]);
+    }
+  }
+}
+
+// d_q_idx and d_w: the partials summed over the chunks in a fixed order. A
+// workgroup takes 64 float4 outputs of d_q_idx; its four thread groups each
+// add a quarter of the chunks (eight loads in flight per thread), and the
+// four sums are added in group order. The first workgroup of a query also
+// sums d_w.
+constexpr int kRedOut = 64;
+constexpr int kRedGroups = kKlThreads / kRedOut;
+
 __global__ __launch_bounds__(kKlThreads) void k_kl_reduce(KlArgs a) {
-  const int t = blockIdx.y;
-  const int i = blockIdx.x * kKlThreads + threadIdx.x;  // over HI * DI + HI outputs
-  const int nq = a.HI * a.DI;
-  if (i >= nq + a.HI) return;
-  float s = 0.0f;
-  if (i < nq) {
-    for (int c = 0; c < a.chunks; ++c) s += a.part_q[((size_t)t * a.chunks + c) * nq + i];
-    a.d_q_idx[(size_t)t * nq + i] = s;
-  } else {
-    const int h = i - nq;
-    for (int c = 0; c < a.chunks; ++c) s += a.part_w[((size_t)t * a.chunks + c) * a.HI + h];
-    a.d_w[(size_t)t * a.HI + h] = s;
+  __shared__ float4 part[kRedGroups][kRedOut];
+  const int t = blockIdx.y, tid = threadIdx.x;
+  const int nq4 = a.HI * a.DI / 4;  // HI * DI is a multiple of 8
+  const int oo = tid % kRedOut, grp = tid / kRedOut;
+  const int o = blockIdx.x * kRedOut + oo;
+  const int per = (a.chunks + kRedGroups - 1) / kRedGroups;
+  const int c0 = min(a.chunks, grp * per), c1 = min(a.chunks, c0 + per);
+  float4 s = {0.f, 0.f, 0.f, 0.f};
+  if (o < nq4) {
+    const float4 *src = (const float4 *)a.part_q + (size_t)t * a.chunks * nq4 + o;
+    int c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * nq4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
+    }
+    for (; c < c1; ++c) {
+      const float4 v = src[(size_t)c * nq4];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+  }
+  part[grp][oo] = s;
+  __syncthreads();
+  if (grp == 0 && o < nq4) {
+#pragma unroll
+    for (int q = 1; q < kRedGroups; ++q) {
+      const float4 v = part[q][oo];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    ((float4 *)a.d_q_idx)[(size_t)t * nq4 + o] = s;
+  }
+  if (blockIdx.x == 0 && tid < a.HI) {
+    const float *src = a.part_w + (size_t)t * a.chunks * a.HI + tid;
+    float w = 0.0f;
+    int c = 0;
+    for (; c + 8 <= a.chunks; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * a.HI];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w += v[u];
+    }
+    for (; c < a.chunks; ++c) w += src[(size_t)c * a.HI];
+    a.d_w[(size_t)t * a.HI + tid] = w;
   }
 }
 
@@ -750,9 +1003,7 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
                               160 * 1024);
     (void)hipFuncSetAttribute((const void *)k_kl_rows<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    (void)hipFuncSetAttribute((const void *)k_kl_backward<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    (void)hipFuncSetAttribute((const void *)k_kl_backward<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void *)k_kl_backward, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipFuncSetAttribute((const void *)k_kl_mass_lds<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)kKlLdsRows);
@@ -778,13 +1029,13 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
   } else {
     hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
   }
-  hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
-  if (HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN)
-    hipLaunchKernelGGL(k_kl_backward<true>, grid, dim3(kKlThreads), smem, s, a);
-  else
-    hipLaunchKernelGGL(k_kl_backward<false>, grid, dim3(kKlThreads), smem, s, a);
-  hipLaunchKernelGGL(k_kl_reduce, dim3((HI * DI + HI + kKlThreads - 1) / kKlThreads, T), dim3(kKlThreads), 0, s,
-                     a);
+  if (HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN && k <= kGradMaxPer * kKlThreads) {
+    hipLaunchKernelGGL(k_kl_grad, grid, dim3(kKlThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
+    hipLaunchKernelGGL(k_kl_backward, grid, dim3(kKlThreads), smem, s, a);
+  }
+  hipLaunchKernelGGL(k_kl_reduce, dim3((HI * DI / 4 + kRedOut - 1) / kRedOut, T), dim3(kKlThreads), 0, s, a);
   return hipGetLastError();
 }
 
