@@ -30,11 +30,16 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i &a, const v8i &b, const v4f &c
 }
 
 // Piece swizzle of key row r in LDS: the 16-byte piece q of the row is
-// stored at piece q ^ key_swz(r). A ds_read_b128 of the B operand serves 16
-// lanes at a time, 16 consecutive rows with one piece each; rows r and r + 1
-// sit half the banks apart, and (r >> 1) & 7 spreads each row pair over all
-// eight piece positions, so every 16-lane group hits 64 distinct banks.
-__device__ __forceinline__ int key_swz(int r) { return (r >> 1) & 7; }
+// stored at piece q ^ key_swz(r). A ds_read_b128 of the B operand reads 16
+// consecutive rows with one piece each. The counters of gfx950
+// (SQ_LDS_BANK_CONFLICT) fit a read served 8 lanes at a time over 128 bytes
+// of banks: a 128-byte row starts on the same bank as every other row, so
+// the 8 rows of each 8-lane group need 8 distinct piece positions, which any
+// bijection of r & 7 gives. With (r >> 1) & 7 (distinct only over 16-lane
+// groups against 256 bytes of banks) half of the LDS-active cycles of the
+// prefill indexer were bank conflicts; with this swizzle there are none
+// (the kernel time did not change: the pass is bound by its MFMA work).
+__device__ __forceinline__ int key_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 // B operand of key tile kt (keys 16 kt .. 16 kt + 15 of a 64-key LDS tile):
 // key 16 kt + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row.
