@@ -160,10 +160,15 @@ __device__ __forceinline__ v8bf as_v8bf(const v4i &x) { return __builtin_bit_cas
 // 16-byte chunk `chunk` of tile row `row` lives at chunk slot
 // row*72 + (chunk ^ row_swz(row)): an XOR swizzle inside aligned groups of 8
 // chunks that spreads same-column reads of consecutive rows over the LDS
-// banks. Chosen by measurement on gfx950 (two waves per SIMD): the S-operand
-// reads (ds_read_b128, 16 consecutive rows, one chunk) run at about 226 B per
-// clock and CU, the V^T reads (ds_read_b64_tr_b16) at about 126.
-__device__ __forceinline__ int row_swz(int row) { return (row >> 1) & 7; }
+// banks (a row is 288 dwords, so every row starts on the same bank of a
+// 128-byte bank window). Chosen by the bank-conflict counter of gfx950
+// (SQ_LDS_BANK_CONFLICT) among XOR swizzles of period 16 in the row: with
+// row & 7 the whole-query kernel has no conflict cycles and the split
+// kernel 91 K per launch (16 x 128K), against 134 M and 615 K with
+// (row >> 1) & 7; swizzles that separate rows 4 apart instead (bits 1..0 of
+// the row moved up) doubled them. Kernel times did not change with any of
+// them (the MLA passes are not bound by LDS bandwidth).
+__device__ __forceinline__ int row_swz(int row) { return row & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowChunks + (chunk ^ row_swz(row)); }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
