@@ -82,3 +82,14 @@ def test_indexer_kl_mxfp8_paged():
     case = make_custom(lens, [(b, n - 1) for b, n in enumerate(lens)] + [(1, 9000)], dims=FULL_DIMS,
                        precision="mxfp8", seed=62, device="cuda")
     _check(paged_copy(case, 256, seed=5), "mxfp8 paged")
+
+
+def test_indexer_kl_topk_1000_shared_sequence():
+    # k = 1000 (not a multiple of the 64-row workgroups): the last workgroup of
+    # a query holds 40 rows; two queries of sequence 0 select overlapping rows,
+    # whose d_k_idx contributions add through the atomics; sequence 2 is
+    # shorter than k (every position selected)
+    lens = [5000, 1500, 999]
+    qs = [(0, 4999), (0, 3000), (1, 1499), (2, 998)]
+    case = make_custom(lens, qs, dims=dict(FULL_DIMS, topk=1000), precision="bf16", seed=63, device="cuda")
+    _check(case, "topk 1000")
