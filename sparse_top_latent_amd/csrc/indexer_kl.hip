@@ -388,11 +388,15 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
 // into LDS (LDS-DMA, rows 0..31 and 32..63 as two batches) and every wave
 // reading its MFMA operands from there, instead of each of the 4 waves
 // loading every row from memory. Row r's 16-byte chunk c sits at chunk slot
-// r * 72 + (c ^ ((r >> 1) & 7)) (the swizzle spreads a 16-row operand read
-// over the LDS banks).
+// r * 72 + (c ^ kl_row_swz(r)): a row is 288 dwords, so every row starts on
+// the same bank of a 128-byte bank window, and a 16-byte operand read of 16
+// rows (one chunk each) is served 8 lanes at a time; r & 7 gives those 8
+// rows 8 different chunk positions (by gfx950's bank-conflict counter, as
+// for the MLA tiles).
 constexpr int kKlRowChunks = 72;                         // 16-byte chunks per 576-wide bf16 row
 constexpr size_t kKlLdsRows = (size_t)kKlRows * kKlRowChunks * 16;  // 73,728 B
-__device__ __forceinline__ int kl_swz(int r, int c) { return r * kKlRowChunks + (c ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int kl_row_swz(int r) { return r & 7; }
+__device__ __forceinline__ int kl_swz(int r, int c) { return r * kKlRowChunks + (c ^ kl_row_swz(r)); }
 
 template <bool kScores>
 __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
   for (int u = 0; u < 18; ++u) {
     const int c = u * 256 + tid;
     const int r = c / kKlRowChunks;
-    const int col = (c - r * kKlRowChunks) ^ ((r >> 1) & 7);
+    const int col = (c - r * kKlRowChunks) ^ kl_row_swz(r);
     const int64_t row = rows[r];
     const void *src = row >= 0 ? (const void *)((const uint16_t *)a.kv + row * a.D + col * 8)
                                : (const void *)(a.q);  // any readable 16 bytes; masked below
@@ -449,26 +453,33 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
     }
   }
   __syncthreads();  // every copy has landed (the barrier waits for this wave's loads first)
+  // the four 16-row tiles as four independent accumulation chains, k-step
+  // by k-step (one chain per tile in turn left each MFMA waiting on the one
+  // before it)
+  v4f accs[kKlRows / 16], zcs[kKlRows / 16];
+#pragma unroll
+  for (int rt = 0; rt < kKlRows / 16; ++rt) accs[rt] = zcs[rt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kKlKsteps; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < kKlRows / 16; ++rt) {
+      const v4i av = *(const v4i *)(tile + kl_swz(rt * 16 + c16, 4 * ks + g) * 16);
+      accs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                         __builtin_bit_cast(v8bf, qreg[ks]), accs[rt], 0, 0, 0);
+    }
+  if (kScores) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int rt = 0; rt < kKlRows / 16; ++rt) {
+        const v4i kb = rows[rt * 16 + c16] < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[rt][ks]);
+        zcs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
+                                                          __builtin_bit_cast(v8bf, qireg[ks]), zcs[rt], 0, 0, 0);
+      }
+  }
 #pragma unroll
   for (int rt = 0; rt < kKlRows / 16; ++rt) {
-    const int rr = rt * 16 + c16;
-    const int64_t row = rows[rr];
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kKlKsteps; ++ks) {
-      const v4i av = *(const v4i *)(tile + kl_swz(rr, 4 * ks + g) * 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, qreg[ks]),
-                                                     acc, 0, 0, 0);
-    }
-    v4f zc = {0.f, 0.f, 0.f, 0.f};
-    if (kScores) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[rt][ks]);
-        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
-                                                    zc, 0, 0, 0);
-      }
-    }
+    const v4f acc = accs[rt], zc = zcs[rt];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = rt * 16 + 4 * g + i;
