@@ -338,7 +338,7 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     const int2 nc = a.sel.ncand[t];
     const int b = kPaged ? a.meta.q_seq[t] : 0;
     asm volatile("" ::: "memory");
-    load_q();
+    if (set == 0) load_q();  // set 1 takes its copy from set 0 through LDS (below)
     const int n = nc.x;
     start = kPaged ? 0 : nc.y;
     if (tid < R * kMlaRowsPerSplit) {
@@ -359,7 +359,20 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
                         });
     }
   }
-  // rows[] ready (written through LDS only: the query slice stays in flight)
+  // Fused: the two wave sets need the same query slice (waves w and w + 4
+  // serve the same 16 heads). Set 0 loaded it; it writes it to 73,728 bytes
+  // of LDS that no copy fills before the first tiles are under way (bf16:
+  // the ring's tiles 2 and 3; MXFP8: the expanded tiles), and set 1 reads it
+  // after the barrier below. One load of the slice per workgroup instead of
+  // two: the finish's first loads share the memory system with half as many
+  // bytes (split kernel 24.8-25.0 -> 24.3-24.5 us on 16 x 128K).
+  unsigned char *qx = smem + (kMx ? kMaxTiles * kMxRawBytes : 2 * kTileBytes) + hg * (kKsteps * 1024) + lane * 16;
+  static_assert(4 * kKsteps * 1024 == 2 * kTileBytes, "the query slice fills two tiles");
+  if (kFuse && set == 0) {
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) *(v4i *)(qx + ks * 1024) = __builtin_bit_cast(v4i, qreg[ks]);
+  }
+  // rows[] ready, and (fused) set 0's slice in LDS (written through LDS only)
   if (kFuse) barrier_lds(); else __syncthreads();
   if (!kFuse) load_q();
 
@@ -445,6 +458,13 @@ __global__ __launch_bounds__(512) void k_mla_split8(MlaArgs a, uint16_t *__restr
     // the random-row rate of the memory system. From the second round on, tile
     // `set` was requested during the previous round (see below).
     if (rd == 0) issue_tile(rrows, ntiles, set);
+    if (kFuse && rd == 0) {
+      if (set == 1) {
+#pragma unroll
+        for (int ks = 0; ks < kKsteps; ++ks) qreg[ks] = as_v8bf(*(const v4i *)(qx + ks * 1024));
+      }
+      barrier_lds();  // every wave is past the exchange area before tiles 2 and 3 (or their expansion) fill it
+    }
     issue_tile(rrows, ntiles, set + 2);
     if (kMx) {
   #pragma unroll
