@@ -183,29 +183,47 @@ __global__ __launch_bounds__(kIdxWaves * 64) void k_index_fp8(SeqMeta m, int T, 
           kKeyLoadPolicy);
     }
   };
-  // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row;
+  // The query's 64 x 128 index matrix has the shape of a key step (64 rows of
+  // 128 bytes). Every wave needs all of it (four 16 x 128 A tiles), so it is
+  // copied once per workgroup into the ring's last buffer, which no key step
+  // fills before the loop's first iteration, in the key steps' swizzled
+  // layout, and each wave reads its A tiles from there: a quarter of the L2
+  // traffic of four copies while the first steps are being fetched.
+  static_assert(kIdxStepBytes == 64 * 128, "the index matrix fills one ring buffer");
+  unsigned char *qbuf = ring + (kR - 1) * kIdxStepBytes;
+#pragma unroll
+  for (int u = 0; u < kIdxPieces; ++u) {
+    const int p = u * kThreads + tid;
+    const int r = p >> 3;
+    const uint8_t *src = q_idx + ((size_t)t * 64 + r) * 128 + (((p & 7) ^ key_swz(r)) << 4);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(qbuf + (u * kThreads + wave * 64) * 16), 16, 0, 0);
+  }
   // accumulator row r of this lane is head ht*16 + 4 kg + r
-  v8i a[4];
   float wv[16];
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const v4i *src = (const v4i *)(q_idx + ((size_t)t * 64 + ht * 16 + c16) * 128 + kg * 32);
-    const v4i lo = src[0], hi = src[1];
-    a[ht] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[ht * 4 + r] = w[(size_t)t * 64 + ht * 16 + 4 * kg + r];
-  }
   // The first steps are requested after the query's index matrix and weights,
   // so that only those loads are waited for before the loop (step 0 then
-  // lands while the waves finish setting up). The requests are unconditional,
-  // so that the compiler can count them in its own wait for the query
-  // registers; steps past nsteps read the clamped last key into ring buffers
-  // that are never read, and the loop's last wait covers them.
+  // lands while the waves finish setting up). The requests are unconditional;
+  // steps past nsteps read the clamped last key into ring buffers that are
+  // never read, and the loop's last wait covers them.
   for (int i = 0; i < kR - 1; ++i) issue(i);
   // (cleared before the first barrier of the loop; no wave adds to it earlier)
   if (kHist)
     for (int i = tid; i < kHist0Bins; i += kThreads) hist[i] = 0u;
   wait_vmcnt<kIdxPieces * (kR - 1)>();  // the query loads have landed; from here vmcnt counts copies and stores
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave's part of the index matrix is in LDS
+  asm volatile("" ::: "memory");
+  // A tiles: head ht*16 + c16, bytes [32 kg, 32 kg + 32) of its 128-byte row
+  v8i a[4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) a[ht] = load_key_operand(qbuf, ht, kg, c16);
+  // the reads are done before the loop's first barrier, after which step
+  // kR - 1 overwrites this buffer
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
   float *srow = scores + t * stride;
   for (int i = 0; i < nsteps; ++i) {
     // step i has landed once at most the copies of the steps issued after it
