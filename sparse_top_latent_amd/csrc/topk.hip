@@ -142,9 +142,16 @@ __global__ __launch_bounds__(kSelBlock) void k_topk_select(SeqMeta m, int k,
 
   // Requested first, before anything waits on the sequence lookup: the head
   // (count and 15 highest bins) of list `tid` and this thread's first scores.
-  const int hs = tid < max_slots ? tid : max_slots - 1;
-  const uint4 *hp = (const uint4 *)(lbase + (size_t)hs * ws.slot_words);
-  const uint4 h0 = hp[0], h1 = hp[1], h2 = hp[2], h3 = hp[3];
+  // Only threads below the slot count read a head (the others' values are
+  // never used; they would re-read the last list, 64 bytes a thread).
+  uint4 h0 = make_uint4(0u, 0u, 0u, 0u), h1 = h0, h2 = h0, h3 = h0;
+  if (tid < max_slots) {
+    const uint4 *hp = (const uint4 *)(lbase + (size_t)tid * ws.slot_words);
+    h0 = hp[0];
+    h1 = hp[1];
+    h2 = hp[2];
+    h3 = hp[3];
+  }
   float v[kSelPer];
   load_scores<kVec>(row, stride, c0 + tid * kSelPer, v);
 
