@@ -288,7 +288,8 @@ sga_status sga_cache_append(const sga_problem *p, int64_t num_tokens, int src_dt
  * [T, topk] and lse [T, H] are that forward's outputs (topk_idx_out, lse);
  * outputs loss [T], d_w [T, HI], d_q_idx [T, HI, DI] (fp32, written) and
  * d_k_idx [num_kv_rows, DI] (fp32, ADDED to: the caller clears it; the
- * order of the additions is not fixed). Queries without candidates give
+ * order of the additions is not fixed; no other work may touch d_k_idx
+ * while the call runs). Queries without candidates give
  * loss 0 and zero gradients.
  * Shapes: H, HI <= 64, HI * DI <= 8192, Dc + Dr and DI multiples of 8, topk
  * <= 4096, q in LDS (H * (Dc + Dr) bf16 or fp32) within 96 KiB; q SGA_F32 or

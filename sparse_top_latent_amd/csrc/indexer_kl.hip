@@ -26,8 +26,9 @@
 //   k_kl_grad       one workgroup per (64 rows, query), 64 FP8 index heads x
 //                   128 dims: the query's normalisers and loss, g, z again
 //                   (bf16 MFMA) and both gradient products (bf16 MFMA on an
-//                   exact three-part bf16 split of g w [z > 0]), d_kI by fp32
-//                   atomics, per-chunk partials of d_w and d_qI;
+//                   exact three-part bf16 split of g w [z > 0]), d_kI added
+//                   by fp32 atomics (plain stores for queries that own their
+//                   rows), per-chunk partials of d_w and d_qI;
 //   k_kl_loss,      the other shapes: one workgroup per query for the two
 //   k_kl_backward   normalisations, the loss and g, then one per (64 rows,
 //                   query) for z and the gradient products on the vector ALUs;
@@ -699,10 +700,34 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   __shared__ float red[kKlThreads / 64];
   __shared__ float gsh[kKlRows];
   __shared__ int64_t rows[kKlRows];
+  __shared__ int s_shared_rows;
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int head = wave * 16 + c16;
+  // May another query add into the cache rows this query selects? Not when
+  // the caches are contiguous, no other query names this query's sequence,
+  // and no other sequence's rows overlap its rows: then this query's
+  // additions into d_k_idx need no atomics (its positions are distinct, so
+  // each (row, d) is this workgroup's alone). Decided from the query and
+  // sequence tables (up to 1,024 entries each; past that, and for paged
+  // caches, whose pages sequences may share, the atomics stay). Every
+  // workgroup of the query reaches the same decision.
+  bool shared_rows = a.meta.page_shift != 0 || a.T > 1024 || a.meta.num_seqs > 1024;
+  if (!shared_rows) {
+    const int sb = a.meta.q_seq[t];
+    int64_t s0;
+    const int64_t l0 = seq_len_clipped(a.meta, sb, &s0);
+    for (int u = tid; u < a.T; u += kKlThreads)
+      if (u != t && a.meta.q_seq[u] == sb) shared_rows = true;
+    for (int u = tid; u < a.meta.num_seqs; u += kKlThreads) {
+      if (u == sb) continue;
+      int64_t s1;
+      const int64_t l1 = seq_len_clipped(a.meta, u, &s1);
+      if (l0 > 0 && l1 > 0 && s1 < s0 + l0 && s0 < s1 + l1) shared_rows = true;
+    }
+  }
+  if (tid == 0) s_shared_rows = 0;
   // everything that depends on nothing else is requested first: the index
   // query of this wave's 16 heads (bf16 B operands, exact) and their weights,
   // the query's scores and masses, and the selected positions
@@ -725,7 +750,8 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
     const int r = r0 + tid;
     rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
   }
-  __syncthreads();  // rows[] ready
+  __syncthreads();  // rows[] ready (and s_shared_rows cleared)
+  if (shared_rows) s_shared_rows = 1;  // read after later barriers
   // the index keys of the lane's z rows; they stay in flight through the
   // normalisers below (whose barriers wait for LDS operations only)
   uint2 kraw[4][4];
@@ -896,13 +922,24 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
                                                             __builtin_bit_cast(v8bf, bv), acc[dt], 0, 0, 0);
       }
     }
+    const bool atomic = s_shared_rows != 0;  // uniform over the workgroup
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = wave * 16 + 4 * g + r;
       const int64_t row = rows[j];
-      if (row >= 0 && gsh[j] != 0.0f)
+      if (row >= 0 && gsh[j] != 0.0f) {
+        float *dk = a.d_k_idx + row * 128 + c16;
+        if (atomic) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) atomicAdd(a.d_k_idx + row * 128 + dt * 16 + c16, acc[dt][r]);
+          for (int dt = 0; dt < 8; ++dt) atomicAdd(dk + dt * 16, acc[dt][r]);
+        } else {
+          float old[8];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) old[dt] = dk[dt * 16];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) dk[dt * 16] = old[dt] + acc[dt][r];
+        }
+      }
     }
   }
 }
