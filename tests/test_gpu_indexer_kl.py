@@ -93,3 +93,19 @@ def test_indexer_kl_topk_1000_shared_sequence():
     qs = [(0, 4999), (0, 3000), (1, 1499), (2, 998)]
     case = make_custom(lens, qs, dims=dict(FULL_DIMS, topk=1000), precision="bf16", seed=63, device="cuda")
     _check(case, "topk 1000")
+
+
+def test_indexer_kl_overlapping_sequences():
+    # sequence 1's rows start inside sequence 0's rows (a layout the contiguous
+    # ABI allows), so the two queries' selections can name the same cache
+    # rows: their d_k_idx additions must go through the atomics, while the
+    # query of the disjoint sequence 2 adds without them
+    import dataclasses
+
+    lens = [6000, 5000, 3000]
+    qs = [(0, 5999), (1, 4999), (2, 2999)]
+    base = make_custom(lens, qs, dims=FULL_DIMS, precision="bf16", seed=64, device="cuda")
+    starts = base.kv_start.clone()
+    starts[1] = 3000
+    case = dataclasses.replace(base, kv_start=starts)
+    _check(case, "overlapping sequences")
