@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
   v4i qireg[4];
   float w_h = 0.0f;
   // the index keys of the lane's rows, requested together with the row
-  // copies (unselected rows read row 0; their z is masked below)
+  // copies (unselected rows load nothing and give zeros)
   uint2 kraw[kScores ? kKlRows / 16 : 1][4];
   if (kScores) {
     const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
@@ -448,9 +448,9 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
 #pragma unroll
     for (int rt = 0; rt < kKlRows / 16; ++rt) {
       const int64_t row = rows[rt * 16 + c16];
-      const uint8_t *kr = (const uint8_t *)a.k_idx + (row < 0 ? 0 : row) * 128 + 8 * g;
+      const uint8_t *kr = (const uint8_t *)a.k_idx + row * 128 + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = *(const uint2 *)(kr + ks * 32);
+      for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = row >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
     }
   }
   __syncthreads();  // every copy has landed (the barrier waits for this wave's loads first)
@@ -757,10 +757,10 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   uint2 kraw[4][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const int64_t row = rows[rt * 16 + c16];
-    const uint8_t *kr = (const uint8_t *)a.k_idx + (row < 0 ? 0 : row) * 128 + 8 * g;
+    const int64_t row = rows[rt * 16 + c16];  // -1: not selected (loads nothing)
+    const uint8_t *kr = (const uint8_t *)a.k_idx + row * 128 + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = *(const uint2 *)(kr + ks * 32);
+    for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = row >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
   }
 
   // the query's normalisers (as k_kl_loss computes them)
