@@ -401,26 +401,47 @@ __device__ __forceinline__ int kl_swz(int r, int c) { return r * kKlRowChunks + 
 
 template <bool kScores>
 __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
+  constexpr int kRt = kKlRows / 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char tile[];  // [64 rows][72 chunks]
   __shared__ float part[kKlThreads / 64][kKlRows];
-  __shared__ float spart[kKlThreads / 64][kKlRows];
+  __shared__ float spart[kKlRows];
   __shared__ int64_t rows[kKlRows];
   typedef __attribute__((address_space(3))) void lds_void_t;
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int head = wave * 16 + c16;
+  // the selected positions and the sequence first, then the query-side
+  // operands, which do not depend on the selection: their loads are in
+  // flight while the cache rows are worked out and copied
+  const int32_t pos = (tid < kKlRows && r0 + tid < a.k) ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
   int64_t start;
   const int n = query_candidates(a.meta, t, &start);
-  if (tid < kKlRows) {
-    const int r = r0 + tid;
-    rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
+  const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
+  v4i qreg[kKlKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
+  const float lse_h = a.lse[(size_t)t * 64 + head];
+  // index scores: wave w takes rows 16 w .. 16 w + 15 against all 64 index
+  // heads (B operands of the 4 head tiles), so each index key is loaded once
+  v4i qireg[kScores ? 4 : 1][4];
+  float w_hb[kScores ? 4 : 1];
+  if (kScores) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + hb * 16 + c16) * 128;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qireg[hb][ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+      w_hb[hb] = a.w[(size_t)t * 64 + hb * 16 + c16];
+    }
   }
-  __syncthreads();  // rows[] ready
+  if (tid < kKlRows) rows[tid] = (pos >= 0 && pos < n) ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
+  lds_barrier();  // rows[] ready; the query loads stay in flight
   // the copies: chunk slot c = u * 256 + tid holds row c / 72, chunk
   // (c % 72) ^ swizzle; unselected rows copy any 16 readable bytes (their
   // logits are never used)
 #pragma unroll
-  for (int u = 0; u < 18; ++u) {
+  for (int u = 0; u < kKlRows * kKlRowChunks / 256; ++u) {
     const int c = u * 256 + tid;
     const int r = c / kKlRowChunks;
     const int col = (c - r * kKlRowChunks) ^ kl_row_swz(r);
@@ -429,58 +450,46 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
                                : (const void *)(a.q);  // any readable 16 bytes; masked below
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tile + (u * 256 + wave * 64) * 16), 16, 0, 0);
   }
-  const int head = wave * 16 + c16;
-  const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
-  v4i qreg[kKlKsteps];
-#pragma unroll
-  for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
-  const float lse_h = a.lse[(size_t)t * 64 + head];
-  v4i qireg[4];
-  float w_h = 0.0f;
-  // the index keys of the lane's rows, requested together with the row
+  // the index key of the lane's own row, requested together with the row
   // copies (unselected rows load nothing and give zeros)
-  uint2 kraw[kScores ? kKlRows / 16 : 1][4];
+  const int64_t krow = rows[wave * 16 + c16];
+  uint2 kraw[4];
   if (kScores) {
-    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
+    const uint8_t *kr = (const uint8_t *)a.k_idx + krow * 128 + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
-    w_h = a.w[(size_t)t * 64 + head];
-#pragma unroll
-    for (int rt = 0; rt < kKlRows / 16; ++rt) {
-      const int64_t row = rows[rt * 16 + c16];
-      const uint8_t *kr = (const uint8_t *)a.k_idx + row * 128 + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = row >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
-    }
+    for (int ks = 0; ks < 4; ++ks) kraw[ks] = krow >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
   }
   __syncthreads();  // every copy has landed (the barrier waits for this wave's loads first)
   // the four 16-row tiles as four independent accumulation chains, k-step
   // by k-step (one chain per tile in turn left each MFMA waiting on the one
   // before it)
-  v4f accs[kKlRows / 16], zcs[kKlRows / 16];
+  v4f accs[kRt];
 #pragma unroll
-  for (int rt = 0; rt < kKlRows / 16; ++rt) accs[rt] = zcs[rt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < kRt; ++rt) accs[rt] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < kKlKsteps; ++ks)
 #pragma unroll
-    for (int rt = 0; rt < kKlRows / 16; ++rt) {
+    for (int rt = 0; rt < kRt; ++rt) {
       const v4i av = *(const v4i *)(tile + kl_swz(rt * 16 + c16, 4 * ks + g) * 16);
       accs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
                                                          __builtin_bit_cast(v8bf, qreg[ks]), accs[rt], 0, 0, 0);
     }
+  v4f zcs[4];
   if (kScores) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int hb = 0; hb < 4; ++hb) zcs[hb] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < kKlRows / 16; ++rt) {
-        const v4i kb = rows[rt * 16 + c16] < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[rt][ks]);
-        zcs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
-                                                          __builtin_bit_cast(v8bf, qireg[ks]), zcs[rt], 0, 0, 0);
-      }
+    for (int ks = 0; ks < 4; ++ks) {
+      const v4i kb = krow < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[ks]);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        zcs[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
+                                                          __builtin_bit_cast(v8bf, qireg[hb][ks]), zcs[hb], 0, 0, 0);
+    }
   }
 #pragma unroll
-  for (int rt = 0; rt < kKlRows / 16; ++rt) {
-    const v4f acc = accs[rt], zc = zcs[rt];
+  for (int rt = 0; rt < kRt; ++rt) {
+    const v4f acc = accs[rt];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = rt * 16 + 4 * g + i;
@@ -490,14 +499,20 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
       e += __shfl_xor(e, 4);
       e += __shfl_xor(e, 8);
       if (c16 == 0) part[wave][j] = e;
-      if (kScores) {
-        float sc = fmaxf(zc[i], 0.0f) * w_h;
-        sc += __shfl_xor(sc, 1);
-        sc += __shfl_xor(sc, 2);
-        sc += __shfl_xor(sc, 4);
-        sc += __shfl_xor(sc, 8);
-        if (c16 == 0) spart[wave][j] = sc;
-      }
+    }
+  }
+  if (kScores) {
+    // zcs[hb][i]: z of row 16 wave + 4 g + i for index head 16 hb + c16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) sc = fmaf(fmaxf(zcs[hb][i], 0.0f), w_hb[hb], sc);
+      sc += __shfl_xor(sc, 1);
+      sc += __shfl_xor(sc, 2);
+      sc += __shfl_xor(sc, 4);
+      sc += __shfl_xor(sc, 8);
+      if (c16 == 0) spart[wave * 16 + 4 * g + i] = sc;
     }
   }
   __syncthreads();
@@ -507,9 +522,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
     for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
     a.mass[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? m : 0.0f;
     if (kScores) {
-      float sc = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kKlThreads / 64; ++w) sc += spart[w][tid];
+      const float sc = spart[tid];
       a.score[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? sc + 0.0f : -INFINITY;
     }
   }
@@ -698,13 +711,13 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t opA[3][64 * kGradLd];  // G^T, then G (three parts)
   __shared__ __attribute__((aligned(16))) uint16_t opB[128 * kGradLd];    // kI^T, then qI^T
   __shared__ float red[kKlThreads / 64];
+  __shared__ float rzw[kKlThreads / 64][64];  // d_w partials of the 4 waves
   __shared__ float gsh[kKlRows];
   __shared__ int64_t rows[kKlRows];
   __shared__ int s_shared_rows;
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int head = wave * 16 + c16;
   // May another query add into the cache rows this query selects? Not when
   // the caches are contiguous, no other query names this query's sequence,
   // and no other sequence's rows overlap its rows: then this query's
@@ -729,13 +742,17 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   }
   if (tid == 0) s_shared_rows = 0;
   // everything that depends on nothing else is requested first: the index
-  // query of this wave's 16 heads (bf16 B operands, exact) and their weights,
-  // the query's scores and masses, and the selected positions
-  const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
-  v4i qireg[4];
+  // query of all 64 heads (bf16 B operands of the 4 head tiles, exact) and
+  // their weights, the query's scores and masses, and the selected positions
+  v4i qireg[4][4];
+  float w_hb[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
-  const float w_h = a.w[(size_t)t * 64 + head];
+  for (int hb = 0; hb < 4; ++hb) {
+    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + hb * 16 + c16) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qireg[hb][ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+    w_hb[hb] = a.w[(size_t)t * 64 + hb * 16 + c16];
+  }
   const float *sc = a.score + (size_t)t * a.k, *ms = a.mass + (size_t)t * a.k;
   float scv[kGradMaxPer], msv[kGradMaxPer];
 #pragma unroll
@@ -750,17 +767,17 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
     const int r = r0 + tid;
     rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
   }
-  __syncthreads();  // rows[] ready (and s_shared_rows cleared)
+  lds_barrier();  // rows[] ready (and s_shared_rows cleared); the loads above stay in flight
   if (shared_rows) s_shared_rows = 1;  // read after later barriers
-  // the index keys of the lane's z rows; they stay in flight through the
-  // normalisers below (whose barriers wait for LDS operations only)
-  uint2 kraw[4][4];
+  // the index key of the lane's z row (wave w takes rows 16 w .. 16 w + 15);
+  // it stays in flight through the normalisers below (whose barriers wait
+  // for LDS operations only)
+  const int64_t krow = rows[wave * 16 + c16];  // -1: not selected (loads nothing)
+  uint2 kraw[4];
+  {
+    const uint8_t *kr = (const uint8_t *)a.k_idx + krow * 128 + 8 * g;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int64_t row = rows[rt * 16 + c16];  // -1: not selected (loads nothing)
-    const uint8_t *kr = (const uint8_t *)a.k_idx + row * 128 + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kraw[rt][ks] = row >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
+    for (int ks = 0; ks < 4; ++ks) kraw[ks] = krow >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
   }
 
   // the query's normalisers (as k_kl_loss computes them)
@@ -808,56 +825,55 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   }
   lds_barrier();  // gsh[] ready
 
-  // z = kI . qI^T per 16-row tile (this wave's 16 heads); wave w also stores
-  // k-step w of the keys transposed (kI^T [d][j]) for d_qI
+  // z = kI . qI^T of the wave's 16 rows against the 4 head tiles; the wave
+  // also stores its rows' keys transposed (kI^T [d][j]) for d_qI
   v4f zc[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int64_t row = rows[rt * 16 + c16];
-    zc[rt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int hb = 0; hb < 4; ++hb) zc[hb] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const v4i kb = row < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[rt][ks]);
-      zc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
-                                                       __builtin_bit_cast(v8bf, qireg[ks]), zc[rt], 0, 0, 0);
-      if (ks == wave) {
+  for (int ks = 0; ks < 4; ++ks) {
+    const v4i kb = krow < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[ks]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          opB[(ks * 32 + 8 * g + e) * kGradLd + rt * 16 + c16] =
-              (uint16_t)((uint32_t)kb[e >> 1] >> (16 * (e & 1)));
-      }
-    }
+    for (int hb = 0; hb < 4; ++hb)
+      zc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
+                                                       __builtin_bit_cast(v8bf, qireg[hb][ks]), zc[hb], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      opB[(ks * 32 + 8 * g + e) * kGradLd + wave * 16 + c16] = (uint16_t)((uint32_t)kb[e >> 1] >> (16 * (e & 1)));
   }
-  // G for rows rt * 16 + 4 g + i and this lane's head, its parts into G^T
-  // [h][j] (four consecutive j per 8-byte store), and d_w's partial sum
+  // G for rows 16 wave + 4 g + i and head 16 hb + c16, its parts into G^T
+  // [h][j] (four consecutive j per 8-byte store), and d_w's partial sums
   float gval[4][4];
-  float rzs = 0.0f;
+  float gj[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int i = 0; i < 4; ++i) gj[i] = gsh[wave * 16 + 4 * g + i];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
     uint16_t pp[4][3];
+    float rzs = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = rt * 16 + 4 * g + i;
-      const float gj = gsh[j];
-      gval[rt][i] = zc[rt][i] > 0.0f ? gj * w_h : 0.0f;
-      rzs += gj * fmaxf(zc[rt][i], 0.0f);
-      split3_bf16(gval[rt][i], pp[i]);
+      gval[hb][i] = zc[hb][i] > 0.0f ? gj[i] * w_hb[hb] : 0.0f;
+      rzs += gj[i] * fmaxf(zc[hb][i], 0.0f);
+      split3_bf16(gval[hb][i], pp[i]);
     }
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       const uint2 v = make_uint2((uint32_t)pp[0][p] | ((uint32_t)pp[1][p] << 16),
                                  (uint32_t)pp[2][p] | ((uint32_t)pp[3][p] << 16));
-      *(uint2 *)&opA[p][head * kGradLd + rt * 16 + 4 * g] = v;
+      *(uint2 *)&opA[p][(hb * 16 + c16) * kGradLd + wave * 16 + 4 * g] = v;
     }
+    rzs += __shfl_xor(rzs, 16);
+    rzs += __shfl_xor(rzs, 32);
+    if (g == 0) rzw[wave][hb * 16 + c16] = rzs;
   }
-  rzs += __shfl_xor(rzs, 16);
-  rzs += __shfl_xor(rzs, 32);
   const size_t chunk = (size_t)t * a.chunks + blockIdx.x;
-  if (g == 0) a.part_w[chunk * 64 + head] = rzs;
-  __syncthreads();  // G^T and kI^T complete
+  __syncthreads();  // G^T, kI^T and the d_w partials complete
+  if (tid < 64) a.part_w[chunk * 64 + tid] = (rzw[0][tid] + rzw[1][tid]) + (rzw[2][tid] + rzw[3][tid]);
 
   // d_qI: wave w takes heads 16 w .. 16 w + 15, all 128 d
   {
+    const int head = wave * 16 + c16;
     v4f acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -884,22 +900,26 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   }
   __syncthreads();  // every wave is done with G^T and kI^T
 
-  // G [j][h] parts and qI^T [d][h] for d_kI
+  // G [j][h] parts and qI^T [d][h] for d_kI (wave w stores head tile w of qI^T)
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint16_t pp[3];
-      split3_bf16(gval[rt][i], pp);
-      const int j = rt * 16 + 4 * g + i;
+      split3_bf16(gval[hb][i], pp);
+      const int j = wave * 16 + 4 * g + i;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) opA[p][j * kGradLd + head] = pp[p];
+      for (int p = 0; p < 3; ++p) opA[p][j * kGradLd + hb * 16 + c16] = pp[p];
     }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int hb = 0; hb < 4; ++hb)
+    if (hb == wave)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      opB[(ks * 32 + 8 * g + e) * kGradLd + head] = (uint16_t)((uint32_t)qireg[ks][e >> 1] >> (16 * (e & 1)));
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          opB[(ks * 32 + 8 * g + e) * kGradLd + hb * 16 + c16] =
+              (uint16_t)((uint32_t)qireg[hb][ks][e >> 1] >> (16 * (e & 1)));
   __syncthreads();
 
   // d_kI: wave w takes rows 16 w .. 16 w + 15, all 128 d; added into the
