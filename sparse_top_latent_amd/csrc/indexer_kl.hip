@@ -89,6 +89,7 @@ struct KlArgs {
   float *loss, *d_w, *d_q_idx, *d_k_idx;
   float *mass, *score, *grad;  // [T, k] each
   float *part_w, *part_q;      // [T, chunks, HI], [T, chunks, HI, DI]
+  float4 *part_n;              // [T, chunks]: a mass workgroup's (max score, sum exp(score - max), sum mass); or null
   int chunks;
 };
 
@@ -286,6 +287,32 @@ __device__ __forceinline__ v4i fp8x8_to_bf16(uint2 w8) {
 // computes each row's indexer score: z = kI . qI^T per 16-row tile by bf16
 // MFMA (E4M3FN values are exact in bf16, so z is the fp32 sum of exact
 // products), then sum_h w_h ReLU(z) over the wave's 16 heads and the 4 waves.
+static_assert(kKlRows == 64, "the mass epilogue takes one row per lane of wave 0");
+// Called by wave 0 (threads 0..63, one per row of the workgroup) with row
+// tid's mass m and indexer score sc: stores both, and with scores the
+// workgroup's partials of the query's normalisers, (max score, sum of exp(score
+// - max), sum of mass) over its rows, which k_kl_grad combines.
+template <bool kScores>
+__device__ __forceinline__ void mass_epilogue(const KlArgs &a, int t, int r0, int tid, bool selected, float m, float sc) {
+  const bool live = r0 + tid < a.k;
+  const float mv = live && selected ? m : 0.0f;
+  const float sv = live && selected ? sc + 0.0f : -INFINITY;
+  if (live) {
+    a.mass[(size_t)t * a.k + r0 + tid] = mv;
+    if (kScores) a.score[(size_t)t * a.k + r0 + tid] = sv;
+  }
+  if (kScores && a.part_n) {
+    float mx = sv;
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float se = sv > -INFINITY ? __expf(sv - mx) : 0.0f, sm = mv;
+    for (int o = 1; o < 64; o <<= 1) {
+      se += __shfl_xor(se, o);
+      sm += __shfl_xor(sm, o);
+    }
+    if (tid == 0) a.part_n[(size_t)t * a.chunks + blockIdx.x] = make_float4(mx, se, sm, 0.0f);
+  }
+}
+
 template <bool kScores>
 __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
   __shared__ float part[kKlThreads / 64][kKlRows];
@@ -371,17 +398,14 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
     }
   }
   __syncthreads();
-  if (tid < kKlRows && r0 + tid < a.k) {
-    float m = 0.0f;
+  if (tid < kKlRows) {  // wave 0
+    float m = 0.0f, sc = 0.0f;
 #pragma unroll
     for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
-    a.mass[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? m : 0.0f;
-    if (kScores) {
-      float sc = 0.0f;
+    if (kScores)
 #pragma unroll
       for (int w = 0; w < kKlThreads / 64; ++w) sc += spart[w][tid];
-      a.score[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? sc + 0.0f : -INFINITY;
-    }
+    mass_epilogue<kScores>(a, t, r0, tid, rows[tid] >= 0, m, sc);
   }
 }
 
@@ -516,15 +540,11 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
     }
   }
   __syncthreads();
-  if (tid < kKlRows && r0 + tid < a.k) {
+  if (tid < kKlRows) {  // wave 0
     float m = 0.0f;
 #pragma unroll
     for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
-    a.mass[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? m : 0.0f;
-    if (kScores) {
-      const float sc = spart[tid];
-      a.score[(size_t)t * a.k + r0 + tid] = rows[tid] >= 0 ? sc + 0.0f : -INFINITY;
-    }
+    mass_epilogue<kScores>(a, t, r0, tid, rows[tid] >= 0, m, kScores ? spart[tid] : 0.0f);
   }
 }
 
@@ -707,6 +727,10 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t (&p)[3]) {
   p[2] = bf16_bits_rn(r2);
 }
 
+// kPartN: the normalisers come from the mass kernel's per-workgroup partials
+// (a.part_n), and only the first workgroup of a query, which writes its loss,
+// loads every score and mass; otherwise every workgroup reduces them all.
+template <bool kPartN>
 __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t opA[3][64 * kGradLd];  // G^T, then G (three parts)
   __shared__ __attribute__((aligned(16))) uint16_t opB[128 * kGradLd];    // kI^T, then qI^T
@@ -754,12 +778,24 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
     w_hb[hb] = a.w[(size_t)t * 64 + hb * 16 + c16];
   }
   const float *sc = a.score + (size_t)t * a.k, *ms = a.mass + (size_t)t * a.k;
+  const bool all_rows = !kPartN || blockIdx.x == 0;  // uniform over the workgroup
   float scv[kGradMaxPer], msv[kGradMaxPer];
 #pragma unroll
   for (int i = 0; i < kGradMaxPer; ++i) {
     const int r = tid + i * kKlThreads;
-    scv[i] = r < a.k ? sc[r] : -INFINITY;
-    msv[i] = r < a.k ? ms[r] : 0.0f;
+    scv[i] = all_rows && r < a.k ? sc[r] : -INFINITY;
+    msv[i] = all_rows && r < a.k ? ms[r] : 0.0f;
+  }
+  // kPartN: the chunks' partials (one per lane; a.chunks <= 64 here) and the
+  // score and mass of row r0 + tid
+  float4 pn = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+  float own_s = -INFINITY, own_m = 0.0f;
+  if (kPartN) {
+    if (lane < a.chunks) pn = a.part_n[(size_t)t * a.chunks + lane];
+    if (tid < kKlRows && r0 + tid < a.k) {
+      own_s = sc[r0 + tid];
+      own_m = ms[r0 + tid];
+    }
   }
   int64_t start;
   const int n = query_candidates(a.meta, t, &start);
@@ -780,21 +816,33 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
     for (int ks = 0; ks < 4; ++ks) kraw[ks] = krow >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
   }
 
-  // the query's normalisers (as k_kl_loss computes them)
-  float mx = -INFINITY, tot = 0.0f;
+  // the query's normalisers (as k_kl_loss computes them): with kPartN every
+  // wave combines the chunks' partials itself (butterfly sums, so every lane
+  // of every wave holds the same values), otherwise a block reduction
+  float mx = -INFINITY, tot = 0.0f, zs = 0.0f;
+  if (kPartN) {
+    mx = pn.x;
+    for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    zs = pn.x > -INFINITY ? pn.y * __expf(pn.x - mx) : 0.0f;
+    tot = pn.z;
+    for (int o = 1; o < 64; o <<= 1) {
+      zs += __shfl_xor(zs, o);
+      tot += __shfl_xor(tot, o);
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < kGradMaxPer; ++i) {
-    mx = fmaxf(mx, scv[i]);
-    tot += msv[i];
+    for (int i = 0; i < kGradMaxPer; ++i) {
+      mx = fmaxf(mx, scv[i]);
+      tot += msv[i];
+    }
+    mx = block_max<true>(mx, red);
+    tot = block_sum<true>(tot, red);
+    if (mx > -INFINITY)
+#pragma unroll
+      for (int i = 0; i < kGradMaxPer; ++i)
+        if (tid + i * kKlThreads < a.k) zs += __expf(scv[i] - mx);
+    zs = block_sum<true>(zs, red);
   }
-  mx = block_max<true>(mx, red);
-  tot = block_sum<true>(tot, red);
-  float zs = 0.0f;
-  if (mx > -INFINITY)
-#pragma unroll
-    for (int i = 0; i < kGradMaxPer; ++i)
-      if (tid + i * kKlThreads < a.k) zs += __expf(scv[i] - mx);
-  zs = block_sum<true>(zs, red);
   const float lz = mx + __logf(zs);
   if (blockIdx.x == 0) {  // uniform over the workgroup
     float loss = 0.0f;
@@ -809,8 +857,13 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
     if (tid == 0) a.loss[t] = mx > -INFINITY ? loss : 0.0f;
   }
   // g of the workgroup's rows: row j's score and mass sit in thread
-  // (r0 + j) % 256, entry (r0 + j) / 256
-  {
+  // (r0 + j) % 256, entry (r0 + j) / 256 (kPartN: in thread j)
+  if (kPartN) {
+    if (tid < kKlRows)
+      gsh[tid] = (r0 + tid < a.k && rows[tid] >= 0 && own_s > -INFINITY)
+                     ? __expf(own_s - lz) - (tot > 0.0f ? own_m / tot : 0.0f)
+                     : 0.0f;
+  } else {
     const int owner = r0 % kKlThreads;  // r0 is a multiple of 64: rows j < 64 stay within one entry
     const int i0 = r0 / kKlThreads;
     if (tid >= owner && tid < owner + kKlRows) {
@@ -1029,7 +1082,8 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_reduce(KlArgs a) {
 size_t indexer_kl_ws_bytes(int T, int k, int HI, int DI) {
   const size_t chunks = (k + kKlRows - 1) / kKlRows;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return 3 * al((size_t)T * k * 4) + al((size_t)T * chunks * HI * 4) + al((size_t)T * chunks * HI * DI * 4);
+  return 3 * al((size_t)T * k * 4) + al((size_t)T * chunks * HI * 4) + al((size_t)T * chunks * HI * DI * 4) +
+         al((size_t)T * chunks * 16);
 }
 
 size_t indexer_kl_smem(int H, int D, int HI, int DI, int q_dtype) {
@@ -1059,7 +1113,8 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
   a.score = (float *)c; c += al((size_t)T * k * 4);
   a.grad = (float *)c; c += al((size_t)T * k * 4);
   a.part_w = (float *)c; c += al((size_t)T * a.chunks * HI * 4);
-  a.part_q = (float *)c;
+  a.part_q = (float *)c; c += al((size_t)T * a.chunks * HI * DI * 4);
+  a.part_n = nullptr;
   size_t smem = indexer_kl_smem(H, D, HI, DI, q_dtype);
   // the MI355X shapes take the attention mass from the MFMA kernel
   const bool mfma = H == 64 && q_dtype == SGA_BF16 && D == 32 * kKlKsteps &&
@@ -1084,6 +1139,7 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
   const dim3 grid(a.chunks, T);
   const bool lds_rows = kv_dtype == SGA_BF16;  // bf16 rows are staged in LDS once per workgroup
   if (mfma && HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN) {
+    a.part_n = (float4 *)c;  // the mass kernel's normaliser partials
     if (lds_rows)
       hipLaunchKernelGGL(k_kl_mass_lds<true>, grid, dim3(kKlThreads), kKlLdsRows, s, a);
     else
@@ -1098,7 +1154,10 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
     hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
   }
   if (HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN && k <= kGradMaxPer * kKlThreads) {
-    hipLaunchKernelGGL(k_kl_grad, grid, dim3(kKlThreads), 0, s, a);
+    if (a.part_n && a.chunks <= 64)
+      hipLaunchKernelGGL(k_kl_grad<true>, grid, dim3(kKlThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_kl_grad<false>, grid, dim3(kKlThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
     hipLaunchKernelGGL(k_kl_backward, grid, dim3(kKlThreads), smem, s, a);

@@ -31,9 +31,13 @@ def _close(got, ref, what):
     assert err <= bound, f"{what}: max|diff| {err:.3e} > {bound:.3e}"
 
 
-def run_kl(case):
+def run_kl(case, sel=None):
+    """sel: (topk_idx, lse) to use instead of the forward pass's."""
     prob = sga.Problem.from_case(case)
-    _, idx, lse = run_layer(case, prob)
+    if sel is None:
+        _, idx, lse = run_layer(case, prob)
+    else:
+        idx, lse = sel
     T, HI, DI = case.num_q, case.idx_heads, case.idx_dim
     loss = torch.full((T,), float("nan"), device="cuda")
     d_w = torch.full((T, HI), float("nan"), device="cuda")
@@ -46,9 +50,9 @@ def run_kl(case):
     return loss.cpu().numpy(), d_w.cpu().numpy(), d_q.cpu().numpy(), d_k
 
 
-def _check(case, label):
+def _check(case, label, sel=None):
     say(f"case indexer KL {label}: T={case.num_q} rows={case.num_kv_rows}")
-    loss, d_w, d_q, d_k = run_kl(case)
+    loss, d_w, d_q, d_k = run_kl(case, sel)
     ref = ocase.kl_queries(case)
     _close(loss, ref["loss"], f"{label} loss")
     for i in range(case.num_q):
@@ -109,3 +113,19 @@ def test_indexer_kl_overlapping_sequences():
     starts[1] = 3000
     case = dataclasses.replace(base, kv_start=starts)
     _check(case, "overlapping sequences")
+
+
+def test_indexer_kl_16_heads_fp8_index():
+    # 16 attention heads: the attention mass comes from the generic row kernel
+    # (no per-chunk normaliser partials), while the 64 x 128 FP8 index tensors
+    # still take the MFMA backward, which then reduces the query's scores and
+    # masses itself
+    lens = [9000, 3000]
+    qs = [(0, 8999), (1, 2999), (0, 4000)]
+    case = make_custom(lens, qs, dims=dict(FULL_DIMS, heads=16), precision="bf16", seed=65, device="cuda")
+    # the bf16 forward is built for 64 heads only: the selection and the
+    # per-head log-sum-exp come from the oracle's forward instead
+    fwd = ocase.run_queries(case, keep_scores=False)
+    idx = torch.as_tensor(fwd["topk_idx"], dtype=torch.int32, device="cuda")
+    lse = torch.as_tensor(fwd["lse"], dtype=torch.float32, device="cuda")
+    _check(case, "16 heads", sel=(idx, lse))
