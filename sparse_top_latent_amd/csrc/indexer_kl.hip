@@ -19,12 +19,15 @@
 //                   head-summed attention mass of each row, logits by bf16
 //                   MFMA with the query slice in VGPRs (bf16 rows read from
 //                   one LDS copy of the workgroup's 64 rows), and (FP8 index
-//                   tensors) each row's indexer score;
+//                   tensors) each row's indexer score and the workgroup's
+//                   partials of the query's softmax normalisers;
 //   k_kl_rows       one workgroup per (64 rows, query): each row's indexer score
 //                   (and, for the other shapes, its attention mass, fp32 dot
 //                   products from q in LDS);
 //   k_kl_grad       one workgroup per (64 rows, query), 64 FP8 index heads x
-//                   128 dims: the query's normalisers and loss, g, z again
+//                   128 dims: the query's normalisers (from the mass
+//                   workgroups' partials where the MFMA mass kernels ran) and
+//                   loss, g, z again
 //                   (bf16 MFMA) and both gradient products (bf16 MFMA on an
 //                   exact three-part bf16 split of g w [z > 0]), d_kI added
 //                   by fp32 atomics (plain stores for queries that own their
