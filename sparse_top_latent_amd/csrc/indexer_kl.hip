@@ -287,9 +287,10 @@ __device__ __forceinline__ v4i fp8x8_to_bf16(uint2 w8) {
 }
 
 // With kScores (64 FP8 index heads x 128 dims) the same workgroup also
-// computes each row's indexer score: z = kI . qI^T per 16-row tile by bf16
-// MFMA (E4M3FN values are exact in bf16, so z is the fp32 sum of exact
-// products), then sum_h w_h ReLU(z) over the wave's 16 heads and the 4 waves.
+// computes each row's indexer score: wave w takes rows 16 w .. 16 w + 15,
+// z = kI . qI^T against the 4 tiles of 16 index heads by bf16 MFMA (E4M3FN
+// values are exact in bf16, so z is the fp32 sum of exact products), then
+// sum_h w_h ReLU(z) over the 64 heads.
 static_assert(kKlRows == 64, "the mass epilogue takes one row per lane of wave 0");
 // Called by wave 0 (threads 0..63, one per row of the workgroup) with row
 // tid's mass m and indexer score sc: stores both, and with scores the
@@ -319,33 +320,46 @@ __device__ __forceinline__ void mass_epilogue(const KlArgs &a, int t, int r0, in
 template <bool kScores>
 __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
   __shared__ float part[kKlThreads / 64][kKlRows];
-  __shared__ float spart[kKlThreads / 64][kKlRows];
+  __shared__ float spart[kKlRows];
   __shared__ int64_t rows[kKlRows];
   const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int head = wave * 16 + c16;
+  // the selected positions and the sequence first, then the query-side
+  // operands, which do not depend on the selection: their loads are in
+  // flight while the cache rows are worked out
+  const int32_t pos = (tid < kKlRows && r0 + tid < a.k) ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
   int64_t start;
   const int n = query_candidates(a.meta, t, &start);
-  if (tid < kKlRows) {
-    const int r = r0 + tid;
-    rows[tid] = r < a.k ? sel_row(a, t, r, n, start) : -1;
-  }
-  const int head = wave * 16 + c16;
   const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
   v4i qreg[kKlKsteps];
 #pragma unroll
   for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
   const float lse_h = a.lse[(size_t)t * 64 + head];
   const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
-  // index query of index head `head` (B operand) and its weight
-  v4i qireg[4];
-  float w_h = 0.0f;
+  // index scores: wave w takes rows 16 w .. 16 w + 15 against all 64 index
+  // heads (B operands of the 4 head tiles), so each index key is loaded once
+  v4i qireg[kScores ? 4 : 1][4];
+  float w_hb[kScores ? 4 : 1];
   if (kScores) {
-    const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + head) * 128;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qireg[ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
-    w_h = a.w[(size_t)t * 64 + head];
+    for (int hb = 0; hb < 4; ++hb) {
+      const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + hb * 16 + c16) * 128;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qireg[hb][ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+      w_hb[hb] = a.w[(size_t)t * 64 + hb * 16 + c16];
+    }
   }
-  __syncthreads();
+  if (tid < kKlRows) rows[tid] = (pos >= 0 && pos < n) ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
+  lds_barrier();  // rows[] ready; the query loads stay in flight
+  // the index key of the lane's own row (unselected rows load nothing)
+  const int64_t krow = rows[wave * 16 + c16];
+  uint2 kraw[4];
+  if (kScores) {
+    const uint8_t *kr = (const uint8_t *)a.k_idx + krow * 128 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kraw[ks] = krow >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
+  }
   for (int rt = 0; rt < kKlRows / 16; ++rt) {
     const int64_t row = rows[rt * 16 + c16];
     v4i av[kKlKsteps];
@@ -370,17 +384,7 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
     for (int ks = 0; ks < kKlKsteps; ++ks)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[ks]), __builtin_bit_cast(v8bf, qreg[ks]),
                                                      acc, 0, 0, 0);
-    v4f zc = {0.f, 0.f, 0.f, 0.f};
-    if (kScores) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const v4i kb = row < 0 ? (v4i){0, 0, 0, 0}
-                               : fp8x8_to_bf16(*(const uint2 *)((const uint8_t *)a.k_idx + row * 128 + ks * 32 + 8 * g));
-        zc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb), __builtin_bit_cast(v8bf, qireg[ks]),
-                                                    zc, 0, 0, 0);
-      }
-    }
-    // acc[i]: logit of row rt*16 + 4 g + i for this lane's head; zc[i]: its z
+    // acc[i]: logit of row rt*16 + 4 g + i for this lane's head
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = rt * 16 + 4 * g + i;
@@ -390,25 +394,39 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
       e += __shfl_xor(e, 4);
       e += __shfl_xor(e, 8);
       if (c16 == 0) part[wave][j] = e;
-      if (kScores) {
-        float sc = fmaxf(zc[i], 0.0f) * w_h;
-        sc += __shfl_xor(sc, 1);
-        sc += __shfl_xor(sc, 2);
-        sc += __shfl_xor(sc, 4);
-        sc += __shfl_xor(sc, 8);
-        if (c16 == 0) spart[wave][j] = sc;
-      }
+    }
+  }
+  if (kScores) {
+    v4f zcs[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) zcs[hb] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v4i kb = krow < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[ks]);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        zcs[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
+                                                          __builtin_bit_cast(v8bf, qireg[hb][ks]), zcs[hb], 0, 0, 0);
+    }
+    // zcs[hb][i]: z of row 16 wave + 4 g + i for index head 16 hb + c16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) sc = fmaf(fmaxf(zcs[hb][i], 0.0f), w_hb[hb], sc);
+      sc += __shfl_xor(sc, 1);
+      sc += __shfl_xor(sc, 2);
+      sc += __shfl_xor(sc, 4);
+      sc += __shfl_xor(sc, 8);
+      if (c16 == 0) spart[wave * 16 + 4 * g + i] = sc;
     }
   }
   __syncthreads();
   if (tid < kKlRows) {  // wave 0
-    float m = 0.0f, sc = 0.0f;
+    float m = 0.0f;
 #pragma unroll
     for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
-    if (kScores)
-#pragma unroll
-      for (int w = 0; w < kKlThreads / 64; ++w) sc += spart[w][tid];
-    mass_epilogue<kScores>(a, t, r0, tid, rows[tid] >= 0, m, sc);
+    mass_epilogue<kScores>(a, t, r0, tid, rows[tid] >= 0, m, kScores ? spart[tid] : 0.0f);
   }
 }
 
