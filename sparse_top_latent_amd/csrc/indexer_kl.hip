@@ -15,10 +15,10 @@
 //
 // Kernels per call:
 //   k_kl_mass_lds   one workgroup per (64 selected rows, query), MI355X shapes
-//   k_kl_mass_mfma  with bf16 rows (_lds) or MXFP8 rows (_mfma): the
+//   k_kl_mass_mx    with bf16 rows (_lds) or MXFP8 rows (_mx): the
 //                   head-summed attention mass of each row, logits by bf16
-//                   MFMA with the query slice in VGPRs (bf16 rows read from
-//                   one LDS copy of the workgroup's 64 rows), and (FP8 index
+//                   MFMA with the query slice in VGPRs (rows read from one
+//                   LDS copy of the workgroup's 64 rows), and (FP8 index
 //                   tensors) each row's indexer score and the workgroup's
 //                   partials of the query's softmax normalisers;
 //   k_kl_rows       one workgroup per (64 rows, query): each row's indexer score
@@ -272,10 +272,16 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_rows(KlArgs a) {
 }
 
 // Attention mass of 64 selected rows with bf16 MFMA (64 heads, bf16 q, bf16
-// or MXFP8 rows, Dc + Dr = 32 kKlKsteps): wave w takes heads 16 w .. 16 w + 15
-// and all 64 rows, S^T = rows . q^T per 16-row tile (16x16x32 bf16 MFMA; the
-// query slice stays in VGPRs as the B operand; MXFP8 rows are expanded
-// exactly to bf16 on the way in).
+// or MXFP8 rows, Dc + Dr = 32 kKlKsteps): the workgroup's rows are copied once
+// into LDS; wave w takes heads 16 w .. 16 w + 15 and all 64 rows, S^T = rows .
+// q^T per 16-row tile (16x16x32 bf16 MFMA; the query slice stays in VGPRs as
+// the B operand; MXFP8 rows are expanded exactly to bf16 as they are read).
+//
+// With kScores (64 FP8 index heads x 128 dims) the same workgroup also
+// computes each row's indexer score: wave w takes rows 16 w .. 16 w + 15,
+// z = kI . qI^T against the 4 tiles of 16 index heads by bf16 MFMA (E4M3FN
+// values are exact in bf16, so z is the fp32 sum of exact products), then
+// sum_h w_h ReLU(z) over the 64 heads.
 constexpr int kKlKsteps = 18;
 
 // 8 E4M3FN bytes -> 8 bf16 (exact), as a 16-byte MFMA operand
@@ -286,11 +292,6 @@ __device__ __forceinline__ v4i fp8x8_to_bf16(uint2 w8) {
                (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, 1.0f, true))};
 }
 
-// With kScores (64 FP8 index heads x 128 dims) the same workgroup also
-// computes each row's indexer score: wave w takes rows 16 w .. 16 w + 15,
-// z = kI . qI^T against the 4 tiles of 16 index heads by bf16 MFMA (E4M3FN
-// values are exact in bf16, so z is the fp32 sum of exact products), then
-// sum_h w_h ReLU(z) over the 64 heads.
 static_assert(kKlRows == 64, "the mass epilogue takes one row per lane of wave 0");
 // Called by wave 0 (threads 0..63, one per row of the workgroup) with row
 // tid's mass m and indexer score sc: stores both, and with scores the
@@ -317,123 +318,10 @@ __device__ __forceinline__ void mass_epilogue(const KlArgs &a, int t, int r0, in
   }
 }
 
-template <bool kScores>
-__global__ __launch_bounds__(kKlThreads) void k_kl_mass_mfma(KlArgs a) {
-  __shared__ float part[kKlThreads / 64][kKlRows];
-  __shared__ float spart[kKlRows];
-  __shared__ int64_t rows[kKlRows];
-  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int head = wave * 16 + c16;
-  // the selected positions and the sequence first, then the query-side
-  // operands, which do not depend on the selection: their loads are in
-  // flight while the cache rows are worked out
-  const int32_t pos = (tid < kKlRows && r0 + tid < a.k) ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
-  int64_t start;
-  const int n = query_candidates(a.meta, t, &start);
-  const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
-  v4i qreg[kKlKsteps];
-#pragma unroll
-  for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
-  const float lse_h = a.lse[(size_t)t * 64 + head];
-  const bool mx = a.kv_dtype == SGA_MXFP8_E4M3FN;
-  // index scores: wave w takes rows 16 w .. 16 w + 15 against all 64 index
-  // heads (B operands of the 4 head tiles), so each index key is loaded once
-  v4i qireg[kScores ? 4 : 1][4];
-  float w_hb[kScores ? 4 : 1];
-  if (kScores) {
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + hb * 16 + c16) * 128;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qireg[hb][ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
-      w_hb[hb] = a.w[(size_t)t * 64 + hb * 16 + c16];
-    }
-  }
-  if (tid < kKlRows) rows[tid] = (pos >= 0 && pos < n) ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
-  lds_barrier();  // rows[] ready; the query loads stay in flight
-  // the index key of the lane's own row (unselected rows load nothing)
-  const int64_t krow = rows[wave * 16 + c16];
-  uint2 kraw[4];
-  if (kScores) {
-    const uint8_t *kr = (const uint8_t *)a.k_idx + krow * 128 + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kraw[ks] = krow >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
-  }
-  for (int rt = 0; rt < kKlRows / 16; ++rt) {
-    const int64_t row = rows[rt * 16 + c16];
-    v4i av[kKlKsteps];
-#pragma unroll
-    for (int ks = 0; ks < kKlKsteps; ++ks) {
-      const int d = ks * 32 + 8 * g;
-      if (row < 0) {
-        av[ks] = (v4i){0, 0, 0, 0};
-      } else if (!mx) {
-        av[ks] = *(const v4i *)((const uint16_t *)a.kv + row * a.D + d);
-      } else {
-        const uint2 w8 = *(const uint2 *)((const uint8_t *)a.kv + row * a.D + d);
-        const float sc = e8m0_to_f32(a.kv_scale[row * (a.D / 32) + ks]);
-        av[ks] = (v4i){(int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, sc, false)),
-                       (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, sc, true)),
-                       (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, sc, false)),
-                       (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, sc, true))};
-      }
-    }
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kKlKsteps; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[ks]), __builtin_bit_cast(v8bf, qreg[ks]),
-                                                     acc, 0, 0, 0);
-    // acc[i]: logit of row rt*16 + 4 g + i for this lane's head
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = rt * 16 + 4 * g + i;
-      float e = rows[j] >= 0 ? __expf(a.tau * acc[i] - lse_h) : 0.0f;
-      e += __shfl_xor(e, 1);
-      e += __shfl_xor(e, 2);
-      e += __shfl_xor(e, 4);
-      e += __shfl_xor(e, 8);
-      if (c16 == 0) part[wave][j] = e;
-    }
-  }
-  if (kScores) {
-    v4f zcs[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) zcs[hb] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const v4i kb = krow < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[ks]);
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb)
-        zcs[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
-                                                          __builtin_bit_cast(v8bf, qireg[hb][ks]), zcs[hb], 0, 0, 0);
-    }
-    // zcs[hb][i]: z of row 16 wave + 4 g + i for index head 16 hb + c16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float sc = 0.0f;
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) sc = fmaf(fmaxf(zcs[hb][i], 0.0f), w_hb[hb], sc);
-      sc += __shfl_xor(sc, 1);
-      sc += __shfl_xor(sc, 2);
-      sc += __shfl_xor(sc, 4);
-      sc += __shfl_xor(sc, 8);
-      if (c16 == 0) spart[wave * 16 + 4 * g + i] = sc;
-    }
-  }
-  __syncthreads();
-  if (tid < kKlRows) {  // wave 0
-    float m = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
-    mass_epilogue<kScores>(a, t, r0, tid, rows[tid] >= 0, m, kScores ? spart[tid] : 0.0f);
-  }
-}
-
-// The same for bf16 latent rows, with the workgroup's 64 rows copied once
-// into LDS (LDS-DMA, rows 0..31 and 32..63 as two batches) and every wave
-// reading its MFMA operands from there, instead of each of the 4 waves
-// loading every row from memory. Row r's 16-byte chunk c sits at chunk slot
+// bf16 latent rows: the workgroup's 64 rows are copied once into LDS
+// (LDS-DMA) and every wave reads its MFMA operands from there, instead of
+// each of the 4 waves loading every row from memory. Row r's 16-byte chunk c
+// sits at chunk slot
 // r * 72 + (c ^ kl_row_swz(r)): a row is 288 dwords, so every row starts on
 // the same bank of a 128-byte bank window, and a 16-byte operand read of 16
 // rows (one chunk each) is served 8 lanes at a time; r & 7 gives those 8
@@ -548,6 +436,151 @@ __global__ __launch_bounds__(kKlThreads) void k_kl_mass_lds(KlArgs a) {
   }
   if (kScores) {
     // zcs[hb][i]: z of row 16 wave + 4 g + i for index head 16 hb + c16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) sc = fmaf(fmaxf(zcs[hb][i], 0.0f), w_hb[hb], sc);
+      sc += __shfl_xor(sc, 1);
+      sc += __shfl_xor(sc, 2);
+      sc += __shfl_xor(sc, 4);
+      sc += __shfl_xor(sc, 8);
+      if (c16 == 0) spart[wave * 16 + 4 * g + i] = sc;
+    }
+  }
+  __syncthreads();
+  if (tid < kKlRows) {  // wave 0
+    float m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kKlThreads / 64; ++w) m += part[w][tid];
+    mass_epilogue<kScores>(a, t, r0, tid, rows[tid] >= 0, m, kScores ? spart[tid] : 0.0f);
+  }
+}
+
+// MXFP8 rows: the workgroup's 64 raw rows (576 E4M3FN bytes
+// each, 36 chunks of 16 bytes) are copied once into LDS by LDS-DMA and their
+// E8M0 scales staged beside them; every wave expands its operands from there
+// (8 bytes and one scale per lane and k-step). Row r's chunk c sits at slot
+// r * 36 + (c ^ ((r >> 1) & 3)): a row is 576 bytes, so a 128-byte bank
+// window sees only two row phases; the XOR (which keeps c within its group of
+// four, 36 being a multiple of 4) gives 8 neighbouring rows 8 different 16-byte
+// positions.
+constexpr int kKlMxChunks = 36;                                    // 16-byte chunks per 576-byte row
+constexpr size_t kKlLdsMx = (size_t)kKlRows * kKlMxChunks * 16;    // 36,864 B
+__device__ __forceinline__ int kl_mx_slot(int r, int c) { return r * kKlMxChunks + (c ^ ((r >> 1) & 3)); }
+
+template <bool kScores>
+__global__ __launch_bounds__(kKlThreads) void k_kl_mass_mx(KlArgs a) {
+  constexpr int kRt = kKlRows / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char tile[];  // [64 rows][36 chunks]
+  __shared__ float part[kKlThreads / 64][kKlRows];
+  __shared__ float spart[kKlRows];
+  __shared__ int64_t rows[kKlRows];
+  __shared__ uint8_t scl[kKlRows * kKlKsteps];  // E8M0 scale of (row, k-step)
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const int t = blockIdx.y, r0 = blockIdx.x * kKlRows;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int head = wave * 16 + c16;
+  // the selected positions and the sequence first, then the query-side
+  // operands, which do not depend on the selection
+  const int32_t pos = (tid < kKlRows && r0 + tid < a.k) ? a.topk_idx[(size_t)t * a.k + r0 + tid] : -1;
+  int64_t start;
+  const int n = query_candidates(a.meta, t, &start);
+  const uint16_t *qh = (const uint16_t *)a.q + ((size_t)t * 64 + head) * a.D;
+  v4i qreg[kKlKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKlKsteps; ++ks) qreg[ks] = *(const v4i *)(qh + ks * 32 + 8 * g);
+  const float lse_h = a.lse[(size_t)t * 64 + head];
+  v4i qireg[kScores ? 4 : 1][4];
+  float w_hb[kScores ? 4 : 1];
+  if (kScores) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const uint8_t *qih = (const uint8_t *)a.q_idx + ((size_t)t * 64 + hb * 16 + c16) * 128;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qireg[hb][ks] = fp8x8_to_bf16(*(const uint2 *)(qih + ks * 32 + 8 * g));
+      w_hb[hb] = a.w[(size_t)t * 64 + hb * 16 + c16];
+    }
+  }
+  if (tid < kKlRows) rows[tid] = (pos >= 0 && pos < n) ? kv_row(a.meta, a.meta.q_seq[t], start, pos) : -1;
+  lds_barrier();  // rows[] ready; the query loads stay in flight
+  // the row copies: slot c = u * 256 + tid holds row c / 36, chunk
+  // (c % 36) ^ swizzle; unselected rows copy any 16 readable bytes (their
+  // logits are never used)
+#pragma unroll
+  for (int u = 0; u < kKlRows * kKlMxChunks / 256; ++u) {
+    const int c = u * 256 + tid;
+    const int r = c / kKlMxChunks;
+    const int col = (c - r * kKlMxChunks) ^ ((r >> 1) & 3);
+    const int64_t row = rows[r];
+    const void *src = row >= 0 ? (const void *)((const uint8_t *)a.kv + row * a.D + col * 16) : (const void *)(a.q);
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(tile + (u * 256 + wave * 64) * 16), 16, 0, 0);
+  }
+  // the scales (unselected rows: 2^0)
+  uint8_t sv[(kKlRows * kKlKsteps + kKlThreads - 1) / kKlThreads];
+#pragma unroll
+  for (int u = 0; u < (kKlRows * kKlKsteps + kKlThreads - 1) / kKlThreads; ++u) {
+    const int i = u * kKlThreads + tid;
+    const int64_t row = i < kKlRows * kKlKsteps ? rows[i / kKlKsteps] : -1;
+    sv[u] = row >= 0 ? a.kv_scale[row * kKlKsteps + i % kKlKsteps] : (uint8_t)127;
+  }
+  // the index key of the lane's own row (unselected rows load nothing)
+  const int64_t krow = rows[wave * 16 + c16];
+  uint2 kraw[4];
+  if (kScores) {
+    const uint8_t *kr = (const uint8_t *)a.k_idx + krow * 128 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kraw[ks] = krow >= 0 ? *(const uint2 *)(kr + ks * 32) : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < (kKlRows * kKlKsteps + kKlThreads - 1) / kKlThreads; ++u) {
+    const int i = u * kKlThreads + tid;
+    if (i < kKlRows * kKlKsteps) scl[i] = sv[u];
+  }
+  __syncthreads();  // every copy has landed and the scales are staged
+  v4f accs[kRt];
+#pragma unroll
+  for (int rt = 0; rt < kRt; ++rt) accs[rt] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kKlKsteps; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < kRt; ++rt) {
+      const int r = rt * 16 + c16;
+      const uint2 w8 = *(const uint2 *)(tile + kl_mx_slot(r, 2 * ks + (g >> 1)) * 16 + (g & 1) * 8);
+      const float sc = e8m0_to_f32(scl[r * kKlKsteps + ks]);
+      const v4i av = {(int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, sc, false)),
+                      (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.x, sc, true)),
+                      (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, sc, false)),
+                      (int)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w8.y, sc, true))};
+      accs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                         __builtin_bit_cast(v8bf, qreg[ks]), accs[rt], 0, 0, 0);
+    }
+#pragma unroll
+  for (int rt = 0; rt < kRt; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = rt * 16 + 4 * g + i;
+      float e = rows[j] >= 0 ? __expf(a.tau * accs[rt][i] - lse_h) : 0.0f;
+      e += __shfl_xor(e, 1);
+      e += __shfl_xor(e, 2);
+      e += __shfl_xor(e, 4);
+      e += __shfl_xor(e, 8);
+      if (c16 == 0) part[wave][j] = e;
+    }
+  }
+  if (kScores) {
+    v4f zcs[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) zcs[hb] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const v4i kb = krow < 0 ? (v4i){0, 0, 0, 0} : fp8x8_to_bf16(kraw[ks]);
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        zcs[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, kb),
+                                                          __builtin_bit_cast(v8bf, qireg[hb][ks]), zcs[hb], 0, 0, 0);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float sc = 0.0f;
@@ -1164,12 +1197,12 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
     if (lds_rows)
       hipLaunchKernelGGL(k_kl_mass_lds<true>, grid, dim3(kKlThreads), kKlLdsRows, s, a);
     else
-      hipLaunchKernelGGL(k_kl_mass_mfma<true>, grid, dim3(kKlThreads), 0, s, a);
+      hipLaunchKernelGGL(k_kl_mass_mx<true>, grid, dim3(kKlThreads), kKlLdsMx, s, a);
   } else if (mfma) {
     if (lds_rows)
       hipLaunchKernelGGL(k_kl_mass_lds<false>, grid, dim3(kKlThreads), kKlLdsRows, s, a);
     else
-      hipLaunchKernelGGL(k_kl_mass_mfma<false>, grid, dim3(kKlThreads), 0, s, a);
+      hipLaunchKernelGGL(k_kl_mass_mx<false>, grid, dim3(kKlThreads), kKlLdsMx, s, a);
     hipLaunchKernelGGL(k_kl_rows<false>, grid, dim3(kKlThreads), ((size_t)HI * kl_ld(DI) + 64) * 4, s, a);
   } else {
     hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
