@@ -784,8 +784,11 @@ __device__ __forceinline__ void split3_bf16(float x, uint16_t (&p)[3]) {
 // kPartN: the normalisers come from the mass kernel's per-workgroup partials
 // (a.part_n), and only the first workgroup of a query, which writes its loss,
 // loads every score and mass; otherwise every workgroup reduces them all.
-template <bool kPartN>
-__global__ __launch_bounds__(kKlThreads) void k_kl_grad(KlArgs a) {
+// kMinWg: workgroups per CU the registers must allow (3 for grids of more
+// than two workgroups per CU: 168 VGPRs instead of 184, one spilled; 1 keeps
+// every register for grids the CUs hold at once).
+template <bool kPartN, int kMinWg>
+__global__ __launch_bounds__(kKlThreads, kMinWg) void k_kl_grad(KlArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t opA[3][64 * kGradLd];  // G^T, then G (three parts)
   __shared__ __attribute__((aligned(16))) uint16_t opB[128 * kGradLd];    // kI^T, then qI^T
   __shared__ float red[kKlThreads / 64];
@@ -1208,10 +1211,18 @@ hipError_t launch_indexer_kl(const SeqMeta &m, int T, int H, int D, int HI, int 
     hipLaunchKernelGGL(k_kl_rows<true>, grid, dim3(kKlThreads), smem, s, a);
   }
   if (HI == 64 && DI == 128 && idx_dtype == SGA_FP8_E4M3FN && k <= kGradMaxPer * kKlThreads) {
-    if (a.part_n && a.chunks <= 64)
-      hipLaunchKernelGGL(k_kl_grad<true>, grid, dim3(kKlThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_kl_grad<false>, grid, dim3(kKlThreads), 0, s, a);
+    const bool many = (size_t)a.chunks * T > 2 * (size_t)device_cu_count();
+    if (a.part_n && a.chunks <= 64) {
+      if (many)
+        hipLaunchKernelGGL((k_kl_grad<true, 3>), grid, dim3(kKlThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_kl_grad<true, 1>), grid, dim3(kKlThreads), 0, s, a);
+    } else {
+      if (many)
+        hipLaunchKernelGGL((k_kl_grad<false, 3>), grid, dim3(kKlThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_kl_grad<false, 1>), grid, dim3(kKlThreads), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL(k_kl_loss, dim3(T), dim3(kKlThreads), 0, s, a);
     hipLaunchKernelGGL(k_kl_backward, grid, dim3(kKlThreads), smem, s, a);
